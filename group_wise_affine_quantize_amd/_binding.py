@@ -1,0 +1,262 @@
+"""ctypes binding of libnq.so: argument marshalling only.
+
+Every function here takes torch tensors on the GPU, checks that their dtypes
+and shapes describe the call, and passes raw device pointers and the current
+HIP stream to the C entry point of the same name (include/nq.h).  All
+arithmetic happens in libnq's HIP kernels; there is no fallback of any kind.
+If libnq.so was not built, the first call raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libnq.so"
+
+NQ_ROW_INDEPENDENT_ROWS = 8
+NQ_F32, NQ_BF16 = 0, 1
+NQ_ROUTE_GEMV, NQ_ROUTE_TILED = 1, 2
+
+_lib = None
+
+
+class NQError(RuntimeError):
+    """A libnq call returned a non-zero status."""
+
+    def __init__(self, status, message):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+        self.message = message
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("rows_per_wave", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+    def as_dict(self):
+        return {"route": {1: "gemv", 2: "tiled"}.get(self.route, self.route),
+                "ksplit": self.ksplit, "rows_per_wave": self.rows_per_wave,
+                "tile_m": self.tile_m, "tile_n": self.tile_n}
+
+
+def library_path():
+    return os.path.join(HERE, _LIB_NAME)
+
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGNATURES = {
+    "nq_quantize": [_P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P],
+    "nq_dequantize": [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _I32, _P],
+    "nq_qmm_plan": [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Plan)],
+    "nq_qmm_workspace_bytes": [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32],
+    "nq_qmm": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P],
+    "nq_qmm_row_exact": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ,
+                         _P],
+    "nq_qmm_with_plan": [ctypes.POINTER(Plan), _P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64,
+                         _I32, _I32, _P, _P, _SZ, _P],
+    "nq_gather_qmm_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+                                      _I32],
+    "nq_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P,
+                      _I32, _P, _P, _SZ, _P],
+    "nq_status_string": [_I32],
+    "nq_last_error": [],
+    "nq_version": [],
+}
+_RESTYPES = {"nq_qmm_workspace_bytes": _SZ, "nq_gather_qmm_workspace_bytes": _SZ,
+             "nq_status_string": ctypes.c_char_p, "nq_last_error": ctypes.c_char_p,
+             "nq_version": ctypes.c_char_p}
+
+
+def load_library(path=None):
+    """Loads libnq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m group_wise_affine_quantize_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, ctypes.c_int)
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        lib = load_library()
+        raise NQError(status, lib.nq_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return NQ_F32
+    if t.dtype == torch.bfloat16:
+        return NQ_BF16
+    raise TypeError(f"libnq takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _torch_dtype(dt):
+    torch = _torch()
+    return torch.float32 if dt == NQ_F32 else torch.bfloat16
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _contig(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def words_per_row(k, bits):
+    return k * bits // 32
+
+
+def nq_quantize(w, group_size, bits, codes=None, scales=None, biases=None, stream=None):
+    """w [..., k] (f32 or bf16) -> (codes uint32-as-int32 [..., k*bits/32],
+    scales [..., k/gs], biases [..., k/gs]) in w's dtype."""
+    torch = _torch()
+    lib = load_library()
+    _contig("w", w)
+    k = w.shape[-1]
+    n = w.numel() // k if k else 0
+    lead = tuple(w.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (words_per_row(k, bits),), dtype=torch.int32, device=w.device)
+    if scales is None:
+        scales = torch.empty(lead + (k // group_size if group_size else 0,), dtype=w.dtype,
+                             device=w.device)
+    if biases is None:
+        biases = torch.empty_like(scales)
+    _check(lib.nq_quantize(_ptr(w), _dt(w), n, k, group_size, bits, _ptr(codes), _ptr(scales),
+                           _ptr(biases), _stream(stream)))
+    return codes, scales, biases
+
+
+def nq_dequantize(codes, scales, biases, group_size, bits, out_dtype=None, out=None, stream=None):
+    """-> w_hat [..., k] in out_dtype (default: the scales' dtype)."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("codes", codes), ("scales", scales), ("biases", biases)):
+        _contig(name, t)
+    k = scales.shape[-1] * group_size
+    n = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
+    out_dtype = out_dtype or scales.dtype
+    if out is None:
+        out = torch.empty(tuple(scales.shape[:-1]) + (k,), dtype=out_dtype, device=scales.device)
+    _check(lib.nq_dequantize(_ptr(codes), _ptr(scales), _ptr(biases), _dt(scales), n, k,
+                             group_size, bits, _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def nq_qmm_plan(m, n, k, group_size, bits, x_dtype, sb_dtype, row_exact=False):
+    torch = _torch()
+    lib = load_library()
+    plan = Plan()
+    xd = NQ_F32 if x_dtype == torch.float32 else NQ_BF16
+    sd = NQ_F32 if sb_dtype == torch.float32 else NQ_BF16
+    _check(lib.nq_qmm_plan(m, n, k, group_size, bits, xd, sd, int(bool(row_exact)),
+                           ctypes.byref(plan)))
+    return plan
+
+
+def nq_qmm_workspace_bytes(m, n, k, group_size, bits, x_dtype, sb_dtype, row_exact=False):
+    torch = _torch()
+    xd = NQ_F32 if x_dtype == torch.float32 else NQ_BF16
+    sd = NQ_F32 if sb_dtype == torch.float32 else NQ_BF16
+    return load_library().nq_qmm_workspace_bytes(m, n, k, group_size, bits, xd, sd,
+                                                 int(bool(row_exact)))
+
+
+def _qmm_call(entry, x, codes, scales, biases, group_size, bits, y, workspace, stream, plan=None):
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases)):
+        _contig(name, t)
+    m, k = x.shape
+    n = scales.shape[0]
+    if scales.shape[1] * group_size != k or codes.shape != (n, words_per_row(k, bits)):
+        raise ValueError("codes/scales shapes do not match x and the quantization")
+    if y is None:
+        y = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = [_ptr(x), _dt(x), m, k, _ptr(codes), _ptr(scales), _ptr(biases), _dt(scales), n,
+            group_size, bits, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)]
+    if plan is not None:
+        _check(lib.nq_qmm_with_plan(ctypes.byref(plan), *args))
+    else:
+        _check(getattr(lib, entry)(*args))
+    return y
+
+
+def nq_qmm(x, codes, scales, biases, group_size, bits, y=None, workspace=None, stream=None):
+    """y [m, n] = x [m, k] times the transposed dequantized weights, in x's dtype."""
+    return _qmm_call("nq_qmm", x, codes, scales, biases, group_size, bits, y, workspace, stream)
+
+
+def nq_qmm_row_exact(x, codes, scales, biases, group_size, bits, y=None, workspace=None,
+                     stream=None):
+    """nq_qmm whose every row is bit-equal to the one-row product."""
+    return _qmm_call("nq_qmm_row_exact", x, codes, scales, biases, group_size, bits, y,
+                     workspace, stream)
+
+
+def nq_qmm_with_plan(plan, x, codes, scales, biases, group_size, bits, y=None, workspace=None,
+                     stream=None):
+    return _qmm_call(None, x, codes, scales, biases, group_size, bits, y, workspace, stream,
+                     plan=plan)
+
+
+def nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, x_dtype, sb_dtype,
+                                  sorted_hint=False):
+    torch = _torch()
+    xd = NQ_F32 if x_dtype == torch.float32 else NQ_BF16
+    sd = NQ_F32 if sb_dtype == torch.float32 else NQ_BF16
+    return load_library().nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, xd,
+                                                        sd, int(bool(sorted_hint)))
+
+
+def nq_gather_qmm(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint=False, y=None,
+                  workspace=None, stream=None):
+    """x [rows, l, k]; codes [e, n, k*bits/32]; scales/biases [e, n, k/gs];
+    rhs_idx [rows] (int32/uint32 bit patterns) -> y [rows, l, n] in x's dtype."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases),
+                    ("rhs_idx", rhs_idx)):
+        _contig(name, t)
+    if rhs_idx.element_size() != 4:
+        raise ValueError("rhs_idx must hold 32-bit ids")
+    rows, l, k = x.shape
+    e, n = scales.shape[0], scales.shape[1]
+    if rhs_idx.numel() != rows:
+        raise ValueError("rhs_idx must have one id per row")
+    if y is None:
+        y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.nq_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
+                             _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(rhs_idx),
+                             int(bool(sorted_hint)), _ptr(y), _ptr(workspace), ws_bytes,
+                             _stream(stream)))
+    return y
