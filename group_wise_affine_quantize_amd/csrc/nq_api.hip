@@ -1,0 +1,459 @@
+// C-ABI entry points of libnq: argument validation, the pure kernel planner
+// and dispatch to the kernel translation units.  See include/nq.h for the
+// contract of every call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "nq.h"
+#include "nq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nq_status fail(nq_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool dtype_ok(int dt) { return dt == NQ_F32 || dt == NQ_BF16; }
+int64_t dtype_bytes(int dt) { return dt == NQ_F32 ? 4 : 2; }
+const char *dtype_name(int dt) { return dt == NQ_F32 ? "f32" : dt == NQ_BF16 ? "bf16" : "?"; }
+
+// Bit widths of the stand-alone quantize/dequantize kernels and of the
+// product kernels ("an unsupported combination fails in the operation that
+// uses it").
+bool storage_bits_ok(int b) { return b == 1 || b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
+bool product_bits_ok(int b) { return b == 4 || b == 8; }
+bool group_ok(int gs) { return gs == 32 || gs == 64 || gs == 128; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned_to(const void *p, int64_t a) { return ((uintptr_t)p % (uintptr_t)a) == 0; }
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlap(Span a, Span b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + (uintptr_t)a.bytes;
+    const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + (uintptr_t)b.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+nq_status check_quant(const char *op, int gs, int bits, bool product)
+{
+    if (!group_ok(gs)) return fail(NQ_ERR_QUANT, "%s: group_size=%d is not 32, 64 or 128", op, gs);
+    if (product ? !product_bits_ok(bits) : !storage_bits_ok(bits))
+        return fail(NQ_ERR_QUANT, "%s: bits=%d is not supported (%s)", op, bits,
+                    product ? "products take 4 or 8" : "1, 2, 3, 4, 5, 6 or 8");
+    return NQ_OK;
+}
+
+nq_status check_dims(const char *op, int64_t n, int64_t k, int gs)
+{
+    if (n < 0 || k < 0) return fail(NQ_ERR_SHAPE, "%s: negative size (n=%lld, k=%lld)", op,
+                                    (long long)n, (long long)k);
+    if (n >= kMaxDim || k >= kMaxDim || (k > 0 && n > kMaxElems / k))
+        return fail(NQ_ERR_SHAPE, "%s: size too large (n=%lld, k=%lld)", op, (long long)n,
+                    (long long)k);
+    if (k % gs != 0)
+        return fail(NQ_ERR_SHAPE, "%s: k=%lld is not a multiple of group_size=%d", op,
+                    (long long)k, gs);
+    return NQ_OK;
+}
+
+nq_status check_launch(const char *op, hipError_t err)
+{
+    if (err != hipSuccess)
+        return fail(NQ_ERR_LAUNCH, "%s: kernel launch failed: %s", op, hipGetErrorString(err));
+    return NQ_OK;
+}
+
+// The K split of the matrix-vector family.  A function of (n, k) only --
+// never of the row count -- so that a row's arithmetic is the same however
+// many rows share the call.  Enough waves are formed to keep every compute
+// unit's memory pipeline busy: about 2048 waves (8 per CU on 256 CUs).
+int gemv_ksplit(int64_t n, int64_t k)
+{
+    const int64_t steps = (k + nqk::kStepElems - 1) / nqk::kStepElems;
+    if (steps <= 1) return 1;
+    const int64_t base_waves = (n + 3) / 4;
+    const int64_t want = (2048 + base_waves - 1) / std::max<int64_t>(base_waves, 1);
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, steps, 8}));
+}
+
+nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int bits,
+                    int x_dt, int sb_dt, int row_exact, nq_plan *plan)
+{
+    memset(plan, 0, sizeof *plan);
+    const bool tiled = !row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 &&
+                       nqk::tiled_supported(128, 128, bits);
+    (void)op;
+    (void)sb_dt;
+    (void)gs;
+    if (tiled) {
+        plan->route = NQ_ROUTE_TILED;
+        plan->tile_m = 128;
+        plan->tile_n = 128;
+    } else {
+        plan->route = NQ_ROUTE_GEMV;
+        plan->ksplit = gemv_ksplit(n, k);
+        plan->rows_per_wave = 4;
+    }
+    return NQ_OK;
+}
+
+nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits)
+{
+    if (!plan) return fail(NQ_ERR_NULL, "%s: plan is null", op);
+    if (plan->route == NQ_ROUTE_GEMV) {
+        if (plan->ksplit < 1 || plan->ksplit > 8)
+            return fail(NQ_ERR_PLAN, "%s: ksplit=%d is not in [1, 8]", op, plan->ksplit);
+        if (plan->rows_per_wave != 4)
+            return fail(NQ_ERR_PLAN, "%s: rows_per_wave=%d is not supported (4)", op,
+                        plan->rows_per_wave);
+        return NQ_OK;
+    }
+    if (plan->route == NQ_ROUTE_TILED) {
+        if (x_dt != NQ_BF16) return fail(NQ_ERR_PLAN, "%s: the tiled route takes bf16 x", op);
+        if (!nqk::tiled_supported(plan->tile_m, plan->tile_n, bits))
+            return fail(NQ_ERR_PLAN, "%s: tile %dx%d is not supported", op, plan->tile_m,
+                        plan->tile_n);
+        return NQ_OK;
+    }
+    return fail(NQ_ERR_PLAN, "%s: unknown route %d", op, plan->route);
+}
+
+struct QmmArgs {
+    const void *x;
+    int x_dt;
+    int64_t m, k;
+    const uint32_t *codes;
+    const void *scales, *biases;
+    int sb_dt;
+    int64_t n;
+    int gs, bits;
+    void *y;
+    void *ws;
+    size_t ws_bytes;
+};
+
+nq_status check_qmm(const char *op, const QmmArgs &a, bool *empty)
+{
+    *empty = false;
+    if (!dtype_ok(a.x_dt) || !dtype_ok(a.sb_dt))
+        return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, sb_dt=%d)", op, a.x_dt, a.sb_dt);
+    nq_status st = check_quant(op, a.gs, a.bits, true);
+    if (st) return st;
+    if (a.m < 0) return fail(NQ_ERR_SHAPE, "%s: negative m=%lld", op, (long long)a.m);
+    if ((st = check_dims(op, a.n, a.k, a.gs))) return st;
+    if (a.m >= kMaxDim || (a.k > 0 && a.m > kMaxElems / a.k) || (a.n > 0 && a.m > kMaxElems / a.n))
+        return fail(NQ_ERR_SHAPE, "%s: m=%lld is too large", op, (long long)a.m);
+    if (a.m == 0 || a.n == 0) {
+        *empty = true;
+        return NQ_OK;
+    }
+    if (!a.y) return fail(NQ_ERR_NULL, "%s: y is null", op);
+    if (a.k > 0 && (!a.x || !a.codes || !a.scales || !a.biases))
+        return fail(NQ_ERR_NULL, "%s: x, codes, scales and biases must be non-null", op);
+    if (!aligned16(a.x) || !aligned16(a.codes) || !aligned16(a.y))
+        return fail(NQ_ERR_ALIGN, "%s: x, codes and y must be 16-byte aligned", op);
+    if (!aligned_to(a.scales, dtype_bytes(a.sb_dt)) || !aligned_to(a.biases, dtype_bytes(a.sb_dt)))
+        return fail(NQ_ERR_ALIGN, "%s: scales and biases must be aligned to %lld bytes", op,
+                    (long long)dtype_bytes(a.sb_dt));
+    const Span y{a.y, a.m * a.n * dtype_bytes(a.x_dt)};
+    const Span ins[4] = {{a.x, a.m * a.k * dtype_bytes(a.x_dt)},
+                         {a.codes, a.n * (a.k * a.bits / 32) * 4},
+                         {a.scales, a.n * (a.k / a.gs) * dtype_bytes(a.sb_dt)},
+                         {a.biases, a.n * (a.k / a.gs) * dtype_bytes(a.sb_dt)}};
+    static const char *names[4] = {"x", "codes", "scales", "biases"};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(y, ins[i])) return fail(NQ_ERR_ALIAS, "%s: y overlaps %s", op, names[i]);
+    return NQ_OK;
+}
+
+nq_status run_qmm(const char *op, const nq_plan &plan, const QmmArgs &a, hipStream_t stream)
+{
+    if (plan.route == NQ_ROUTE_TILED) {
+        nqk::TiledLaunch t;
+        t.x = a.x;
+        t.y = a.y;
+        t.codes = a.codes;
+        t.scales = a.scales;
+        t.biases = a.biases;
+        t.sb_dt = a.sb_dt;
+        t.m = a.m;
+        t.n = a.n;
+        t.k = a.k;
+        t.gs = a.gs;
+        t.bits = a.bits;
+        t.tile_m = plan.tile_m;
+        t.tile_n = plan.tile_n;
+        return check_launch(op, nqk::launch_tiled(t, stream));
+    }
+    nqk::GemvLaunch g;
+    g.x = a.x;
+    g.y = a.y;
+    g.codes = a.codes;
+    g.scales = a.scales;
+    g.biases = a.biases;
+    g.idx = nullptr;
+    g.x_dt = a.x_dt;
+    g.sb_dt = a.sb_dt;
+    g.items = 1;
+    g.rows_per_item = a.m;
+    g.k = a.k;
+    g.n = a.n;
+    g.e = 1;
+    g.gs = a.gs;
+    g.bits = a.bits;
+    g.ksplit = plan.ksplit;
+    g.rows_per_wave = plan.rows_per_wave;
+    return check_launch(op, nqk::launch_gemv(g, stream));
+}
+
+nq_status qmm_common(const char *op, int row_exact, const nq_plan *forced, const QmmArgs &a,
+                     hipStream_t stream)
+{
+    g_last_error.clear();
+    bool empty = false;
+    nq_status st = check_qmm(op, a, &empty);
+    if (st || empty) return st;
+    nq_plan plan;
+    if (forced) {
+        if ((st = check_plan(op, forced, a.x_dt, a.bits))) return st;
+        plan = *forced;
+    } else {
+        make_plan(op, a.m, a.n, a.k, a.gs, a.bits, a.x_dt, a.sb_dt, row_exact, &plan);
+    }
+    return run_qmm(op, plan, a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+nq_status nq_quantize(const void *w, nq_dtype w_dt, int64_t n, int64_t k, int32_t group_size,
+                      int32_t bits, uint32_t *codes, void *scales, void *biases, hipStream_t stream)
+{
+    const char *op = "nq_quantize";
+    g_last_error.clear();
+    if (!dtype_ok(w_dt)) return fail(NQ_ERR_DTYPE, "%s: unknown dtype w_dt=%d", op, (int)w_dt);
+    nq_status st = check_quant(op, group_size, bits, false);
+    if (st) return st;
+    if ((st = check_dims(op, n, k, group_size))) return st;
+    if (n == 0 || k == 0) return NQ_OK;
+    if (!w || !codes || !scales || !biases)
+        return fail(NQ_ERR_NULL, "%s: w, codes, scales and biases must be non-null", op);
+    if (!aligned16(w) || !aligned16(codes))
+        return fail(NQ_ERR_ALIGN, "%s: w and codes must be 16-byte aligned", op);
+    const int64_t eb = dtype_bytes(w_dt);
+    if (!aligned_to(scales, eb) || !aligned_to(biases, eb))
+        return fail(NQ_ERR_ALIGN, "%s: scales and biases must be aligned to %lld bytes", op,
+                    (long long)eb);
+    const Span sw{w, n * k * eb}, sc{codes, n * (k * bits / 32) * 4},
+        ss{scales, n * (k / group_size) * eb}, sbi{biases, n * (k / group_size) * eb};
+    if (overlap(sc, sw) || overlap(ss, sw) || overlap(sbi, sw))
+        return fail(NQ_ERR_ALIAS, "%s: an output overlaps w", op);
+    if (overlap(sc, ss) || overlap(sc, sbi) || overlap(ss, sbi))
+        return fail(NQ_ERR_ALIAS, "%s: codes, scales and biases overlap", op);
+    return check_launch(op, nqk::launch_quantize(w, w_dt, n, k, group_size, bits, codes, scales,
+                                                 biases, stream));
+}
+
+nq_status nq_dequantize(const uint32_t *codes, const void *scales, const void *biases,
+                        nq_dtype sb_dt, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                        void *w_out, nq_dtype out_dt, hipStream_t stream)
+{
+    const char *op = "nq_dequantize";
+    g_last_error.clear();
+    if (!dtype_ok(sb_dt) || !dtype_ok(out_dt))
+        return fail(NQ_ERR_DTYPE, "%s: unknown dtype (sb_dt=%d, out_dt=%d)", op, (int)sb_dt,
+                    (int)out_dt);
+    nq_status st = check_quant(op, group_size, bits, false);
+    if (st) return st;
+    if ((st = check_dims(op, n, k, group_size))) return st;
+    if (n == 0 || k == 0) return NQ_OK;
+    if (!w_out || !codes || !scales || !biases)
+        return fail(NQ_ERR_NULL, "%s: codes, scales, biases and w_out must be non-null", op);
+    if (!aligned16(w_out) || !aligned16(codes))
+        return fail(NQ_ERR_ALIGN, "%s: codes and w_out must be 16-byte aligned", op);
+    const int64_t sbb = dtype_bytes(sb_dt);
+    if (!aligned_to(scales, sbb) || !aligned_to(biases, sbb))
+        return fail(NQ_ERR_ALIGN, "%s: scales and biases must be aligned to %lld bytes", op,
+                    (long long)sbb);
+    const Span so{w_out, n * k * dtype_bytes(out_dt)};
+    if (overlap(so, Span{codes, n * (k * bits / 32) * 4}) ||
+        overlap(so, Span{scales, n * (k / group_size) * sbb}) ||
+        overlap(so, Span{biases, n * (k / group_size) * sbb}))
+        return fail(NQ_ERR_ALIAS, "%s: w_out overlaps an input", op);
+    return check_launch(op, nqk::launch_dequantize(codes, scales, biases, sb_dt, n, k, group_size,
+                                                   bits, w_out, out_dt, stream));
+}
+
+nq_status nq_qmm_plan(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                      nq_dtype x_dt, nq_dtype sb_dt, int32_t row_exact, nq_plan *plan)
+{
+    const char *op = "nq_qmm_plan";
+    g_last_error.clear();
+    if (!plan) return fail(NQ_ERR_NULL, "%s: plan is null", op);
+    if (!dtype_ok(x_dt) || !dtype_ok(sb_dt))
+        return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, sb_dt=%d)", op, (int)x_dt, (int)sb_dt);
+    nq_status st = check_quant(op, group_size, bits, true);
+    if (st) return st;
+    if (m < 0) return fail(NQ_ERR_SHAPE, "%s: negative m=%lld", op, (long long)m);
+    if ((st = check_dims(op, n, k, group_size))) return st;
+    return make_plan(op, m, n, k, group_size, bits, x_dt, sb_dt, row_exact, plan);
+}
+
+size_t nq_qmm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                              nq_dtype x_dt, nq_dtype sb_dt, int32_t row_exact)
+{
+    (void)m, (void)n, (void)k, (void)group_size, (void)bits, (void)x_dt, (void)sb_dt, (void)row_exact;
+    return 0;
+}
+
+nq_status nq_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const uint32_t *codes,
+                 const void *scales, const void *biases, nq_dtype sb_dt, int64_t n,
+                 int32_t group_size, int32_t bits, void *y, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream)
+{
+    const QmmArgs a{x, x_dt, m, k, codes, scales, biases, sb_dt, n, group_size, bits, y,
+                    workspace, workspace_bytes};
+    return qmm_common("nq_qmm", 0, nullptr, a, stream);
+}
+
+nq_status nq_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t m, int64_t k,
+                           const uint32_t *codes, const void *scales, const void *biases,
+                           nq_dtype sb_dt, int64_t n, int32_t group_size, int32_t bits, void *y,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const QmmArgs a{x, x_dt, m, k, codes, scales, biases, sb_dt, n, group_size, bits, y,
+                    workspace, workspace_bytes};
+    return qmm_common("nq_qmm_row_exact", 1, nullptr, a, stream);
+}
+
+nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, int64_t m,
+                           int64_t k, const uint32_t *codes, const void *scales,
+                           const void *biases, nq_dtype sb_dt, int64_t n, int32_t group_size,
+                           int32_t bits, void *y, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream)
+{
+    if (!plan) {
+        g_last_error.clear();
+        return fail(NQ_ERR_NULL, "nq_qmm_with_plan: plan is null");
+    }
+    const QmmArgs a{x, x_dt, m, k, codes, scales, biases, sb_dt, n, group_size, bits, y,
+                    workspace, workspace_bytes};
+    return qmm_common("nq_qmm_with_plan", 0, plan, a, stream);
+}
+
+size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n,
+                                     int32_t group_size, int32_t bits, nq_dtype x_dt,
+                                     nq_dtype sb_dt, int32_t sorted_hint)
+{
+    (void)rows, (void)l, (void)k, (void)e, (void)n, (void)group_size, (void)bits, (void)x_dt,
+        (void)sb_dt, (void)sorted_hint;
+    return 0;
+}
+
+nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                        const uint32_t *codes, const void *scales, const void *biases,
+                        nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                        const uint32_t *rhs_idx, int32_t sorted_hint, void *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    const char *op = "nq_gather_qmm";
+    g_last_error.clear();
+    (void)sorted_hint, (void)workspace, (void)workspace_bytes;
+    if (!dtype_ok(x_dt) || !dtype_ok(sb_dt))
+        return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, sb_dt=%d)", op, (int)x_dt, (int)sb_dt);
+    nq_status st = check_quant(op, group_size, bits, true);
+    if (st) return st;
+    if (rows < 0 || l < 0 || e < 0)
+        return fail(NQ_ERR_SHAPE, "%s: negative size (rows=%lld, l=%lld, e=%lld)", op,
+                    (long long)rows, (long long)l, (long long)e);
+    if ((st = check_dims(op, n, k, group_size))) return st;
+    if (e >= kMaxDim || (e > 0 && n > kMaxElems / std::max<int64_t>(e, 1) / std::max<int64_t>(k, 1)))
+        return fail(NQ_ERR_SHAPE, "%s: e=%lld is too large", op, (long long)e);
+    if (rows >= kMaxDim || l >= kMaxDim || (rows > 0 && l > kMaxElems / rows) ||
+        (rows * l > 0 && std::max<int64_t>(k, n) > kMaxElems / (rows * l)))
+        return fail(NQ_ERR_SHAPE, "%s: rows*l is too large", op);
+    if (rows == 0 || l == 0 || n == 0) return NQ_OK;
+    if (!y || !rhs_idx) return fail(NQ_ERR_NULL, "%s: y and rhs_idx must be non-null", op);
+    if (k > 0 && (!x || (e > 0 && (!codes || !scales || !biases))))
+        return fail(NQ_ERR_NULL, "%s: x, codes, scales and biases must be non-null", op);
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(y))
+        return fail(NQ_ERR_ALIGN, "%s: x, codes and y must be 16-byte aligned", op);
+    const int64_t sbb = dtype_bytes(sb_dt);
+    if (!aligned_to(scales, sbb) || !aligned_to(biases, sbb) || !aligned_to(rhs_idx, 4))
+        return fail(NQ_ERR_ALIGN, "%s: scales, biases or rhs_idx misaligned", op);
+    const Span sy{y, rows * l * n * dtype_bytes(x_dt)};
+    const Span ins[5] = {{x, rows * l * k * dtype_bytes(x_dt)},
+                         {codes, e * n * (k * bits / 32) * 4},
+                         {scales, e * n * (k / group_size) * sbb},
+                         {biases, e * n * (k / group_size) * sbb},
+                         {rhs_idx, rows * 4}};
+    static const char *names[5] = {"x", "codes", "scales", "biases", "rhs_idx"};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(sy, ins[i])) return fail(NQ_ERR_ALIAS, "%s: y overlaps %s", op, names[i]);
+
+    nqk::GemvLaunch g;
+    g.x = x;
+    g.y = y;
+    g.codes = codes;
+    g.scales = scales;
+    g.biases = biases;
+    g.idx = rhs_idx;
+    g.x_dt = x_dt;
+    g.sb_dt = sb_dt;
+    g.items = rows;
+    g.rows_per_item = l;
+    g.k = k;
+    g.n = n;
+    g.e = e;
+    g.gs = group_size;
+    g.bits = bits;
+    g.ksplit = gemv_ksplit(n, k);   // the plan nq_qmm_row_exact takes
+    g.rows_per_wave = 4;
+    return check_launch(op, nqk::launch_gemv(g, stream));
+}
+
+const char *nq_status_string(nq_status s)
+{
+    switch (s) {
+    case NQ_OK: return "ok";
+    case NQ_ERR_NULL: return "null pointer";
+    case NQ_ERR_DTYPE: return "unsupported dtype";
+    case NQ_ERR_QUANT: return "unsupported group size or bit width";
+    case NQ_ERR_SHAPE: return "invalid shape";
+    case NQ_ERR_ALIGN: return "misaligned pointer";
+    case NQ_ERR_ALIAS: return "output overlaps an input";
+    case NQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case NQ_ERR_LAUNCH: return "kernel launch failed";
+    case NQ_ERR_PLAN: return "plan does not fit";
+    }
+    return "unknown status";
+}
+
+const char *nq_last_error(void) { return g_last_error.c_str(); }
+
+const char *nq_version(void) { return "0.1.0"; }
+
+}  // extern "C"

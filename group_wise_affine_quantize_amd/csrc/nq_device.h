@@ -1,0 +1,91 @@
+// Device-side helpers shared by the gfx950 kernels of libnq.
+//
+// Storage types: fp32 is `float`; bf16 is carried as its 16-bit pattern
+// (`uint16_t`).  Every fp32 -> bf16 conversion rounds to nearest-even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nqk {
+
+typedef uint16_t bf16_bits;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// Round to nearest-even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <typename T> struct Elt;
+
+template <> struct Elt<float> {
+    static constexpr int bytes = 4;
+    __device__ __forceinline__ static float load(const float *p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float *p, int64_t i, float v) { p[i] = v; }
+    // Value that `store` would keep.
+    __device__ __forceinline__ static float stored(float v) { return v; }
+};
+
+template <> struct Elt<bf16_bits> {
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static float load(const bf16_bits *p, int64_t i)
+    {
+        return bf16_to_f32(p[i]);
+    }
+    __device__ __forceinline__ static void store(bf16_bits *p, int64_t i, float v)
+    {
+        p[i] = (bf16_bits)f32_to_bf16(v);
+    }
+    __device__ __forceinline__ static float stored(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// Loads 32 consecutive elements starting at p (16-byte aligned) as fp32.
+template <typename T> __device__ __forceinline__ void load32_f32(const T *p, float *v);
+
+template <> __device__ __forceinline__ void load32_f32<float>(const float *p, float *v)
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint4 d = q[i];
+        v[4 * i + 0] = __uint_as_float(d.x);
+        v[4 * i + 1] = __uint_as_float(d.y);
+        v[4 * i + 2] = __uint_as_float(d.z);
+        v[4 * i + 3] = __uint_as_float(d.w);
+    }
+}
+
+template <> __device__ __forceinline__ void load32_f32<bf16_bits>(const bf16_bits *p, float *v)
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 d = q[i];
+        uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+            v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+}
+
+// Code j (0..31) of a 32-element lane chunk held in BITS words (LSB-first
+// bit stream; codes of 3, 5 and 6 bits may straddle two words).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(const uint32_t *w, int j)
+{
+    const int bit = j * BITS;
+    const int wi = bit >> 5, sh = bit & 31;
+    uint32_t q = w[wi] >> sh;
+    if (sh + BITS > 32) q |= w[wi + 1] << (32 - sh);
+    return q & ((1u << BITS) - 1u);
+}
+
+}  // namespace nqk

@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI layer (nq_api.hip) and the kernel
+// translation units.  Launchers assume validated arguments and only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nqk {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// Elements handled by one lane per K step of the matrix-vector family: one
+// lane chunk is 32 codes = `bits` uint32 words, always inside one group.
+constexpr int kLaneChunk = 32;
+constexpr int kWave = 64;
+constexpr int kStepElems = kLaneChunk * kWave;   // 2048 elements of K per wave step
+
+hipError_t launch_quantize(const void *w, int w_dt, int64_t n, int64_t k, int gs, int bits,
+                           uint32_t *codes, void *scales, void *biases, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint32_t *codes, const void *scales, const void *biases,
+                             int sb_dt, int64_t n, int64_t k, int gs, int bits, void *out,
+                             int out_dt, hipStream_t stream);
+
+// One launch of the matrix-vector family over `items` independent products
+// that share n, k and the quantization: item i multiplies rows_per_item
+// consecutive rows of x (starting at row i * rows_per_item) with the weights
+// of expert idx[i] (or the only weight matrix when idx is null), writing the
+// same rows of y.  Items whose expert id is >= e produce zero rows.
+struct GemvLaunch {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const void *scales;
+    const void *biases;
+    const uint32_t *idx;     // null: plain product
+    int x_dt, sb_dt;
+    int64_t items, rows_per_item, k, n, e;
+    int gs, bits;
+    int ksplit, rows_per_wave;
+};
+hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
+
+// Tiled bf16-MFMA product: y[m, n] = x[m, k] . w_hat[n, k]^T, x and y bf16.
+struct TiledLaunch {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const void *scales;
+    const void *biases;
+    int sb_dt;
+    int64_t m, n, k;
+    int gs, bits;
+    int tile_m, tile_n;
+};
+hipError_t launch_tiled(const TiledLaunch &a, hipStream_t stream);
+bool tiled_supported(int tile_m, int tile_n, int bits);
+
+}  // namespace nqk

@@ -1,0 +1,237 @@
+// Group-wise affine quantize and dequantize kernels for gfx950.
+//
+// Method: "Quantization" page of the nuvec documentation, section "Affine":
+// rows are cut into groups of group_size values, each group keeps one scale
+// and one bias, values become `bits`-bit codes packed into uint32 words and
+// w ~ scale * code + bias.  Scale/bias selection (min/max), rounding and bit
+// order follow the contract stated in include/nq.h.
+//
+// Both kernels are bandwidth-bound streams: one lane owns 32 consecutive
+// elements of a row (one lane chunk, always inside one group), reads them with
+// 16-byte loads and writes `bits` words of codes.  A group of 32/64/128
+// values spans 1/2/4 adjacent lanes, which exchange min/max with xor
+// shuffles.  The file is built with -ffp-contract=off: every fp32 step below
+// rounds once, as written, which is what makes quantize bit-exact.
+#include <math.h>
+
+#include "nq_device.h"
+#include "nq_internal.h"
+
+namespace nqk {
+
+template <int BITS>
+__device__ __forceinline__ void store_words(uint32_t *dst, const uint32_t *wd)
+{
+    if constexpr (BITS % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i)
+            reinterpret_cast<uint4 *>(dst)[i] =
+                make_uint4(wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]);
+    } else if constexpr (BITS % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < BITS / 2; ++i)
+            reinterpret_cast<uint2 *>(dst)[i] = make_uint2(wd[2 * i], wd[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) dst[i] = wd[i];
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_words(const uint32_t *src, uint32_t *wd)
+{
+    if constexpr (BITS % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i) {
+            uint4 d = reinterpret_cast<const uint4 *>(src)[i];
+            wd[4 * i] = d.x, wd[4 * i + 1] = d.y, wd[4 * i + 2] = d.z, wd[4 * i + 3] = d.w;
+        }
+    } else if constexpr (BITS % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < BITS / 2; ++i) {
+            uint2 d = reinterpret_cast<const uint2 *>(src)[i];
+            wd[2 * i] = d.x, wd[2 * i + 1] = d.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) wd[i] = src[i];
+    }
+}
+
+// One lane per 32-element chunk; chunks are numbered row-major over [n, k/32].
+template <int BITS, typename WT>
+__global__ void __launch_bounds__(256)
+quantize_kernel(const WT *__restrict__ w, int64_t chunks, int64_t k, int gs,
+                uint32_t *__restrict__ codes, WT *__restrict__ scales, WT *__restrict__ biases)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool valid = c < chunks;
+    const int lanes_per_group = gs / kLaneChunk;   // 1, 2 or 4, adjacent lanes
+    const float top = (float)((1u << BITS) - 1u);
+
+    float v[kLaneChunk];
+    if (valid) {
+        load32_f32<WT>(w + c * kLaneChunk, v);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLaneChunk; ++j) v[j] = 0.0f;
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int j = 1; j < kLaneChunk; ++j) {
+        mn = v[j] < mn ? v[j] : mn;
+        mx = v[j] > mx ? v[j] : mx;
+    }
+    // A group's lanes are all valid or all invalid (k is a multiple of gs).
+    for (int off = 1; off < lanes_per_group; off <<= 1) {
+        const float omn = __shfl_xor(mn, off);
+        const float omx = __shfl_xor(mx, off);
+        mn = omn < mn ? omn : mn;
+        mx = omx > mx ? omx : mx;
+    }
+    if (!valid) return;
+
+    mn = mn + 0.0f;   // -0 -> +0, so the result does not depend on the order
+    mx = mx + 0.0f;
+    const float range = mx - mn;
+    float scale = range / top;   // IEEE division (correctly rounded)
+    scale = scale + 0.0f;
+    const float s = Elt<WT>::stored(scale);
+    const float b = Elt<WT>::stored(mn);
+
+    const int64_t chunks_per_row = k / kLaneChunk;
+    const int64_t row = c / chunks_per_row;
+    const int64_t cir = c - row * chunks_per_row;
+    if (cir % lanes_per_group == 0) {
+        const int64_t gi = row * (k / gs) + cir / lanes_per_group;
+        Elt<WT>::store(scales, gi, scale);
+        Elt<WT>::store(biases, gi, mn);
+    }
+
+    uint32_t wd[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) wd[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < kLaneChunk; ++j) {
+        uint32_t q = 0u;
+        if (s != 0.0f) {
+            float t = (v[j] - b) / s;
+            t = rintf(t);
+            t = fminf(fmaxf(t, 0.0f), top);
+            q = (uint32_t)t;
+        }
+        const int bit = j * BITS;
+        wd[bit >> 5] |= q << (bit & 31);
+        if ((bit & 31) + BITS > 32) wd[(bit >> 5) + 1] |= q >> (32 - (bit & 31));
+    }
+    store_words<BITS>(codes + c * BITS, wd);
+}
+
+template <int BITS, typename ST, typename OT>
+__global__ void __launch_bounds__(256)
+dequantize_kernel(const uint32_t *__restrict__ codes, const ST *__restrict__ scales,
+                  const ST *__restrict__ biases, int64_t chunks, int64_t k, int gs,
+                  OT *__restrict__ out)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= chunks) return;
+    const int64_t chunks_per_row = k / kLaneChunk;
+    const int64_t row = c / chunks_per_row;
+    const int64_t cir = c - row * chunks_per_row;
+    const int64_t gi = row * (k / gs) + cir * kLaneChunk / gs;
+    const float s = Elt<ST>::load(scales, gi);
+    const float b = Elt<ST>::load(biases, gi);
+    uint32_t wd[BITS];
+    load_words<BITS>(codes + c * BITS, wd);
+    float v[kLaneChunk];
+#pragma unroll
+    for (int j = 0; j < kLaneChunk; ++j) v[j] = fmaf(s, (float)code_at<BITS>(wd, j), b);
+    OT *dst = out + c * kLaneChunk;
+    if constexpr (sizeof(OT) == 4) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            reinterpret_cast<uint4 *>(dst)[i] =
+                make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                           __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p[j] = f32_to_bf16(v[8 * i + 2 * j]) | (f32_to_bf16(v[8 * i + 2 * j + 1]) << 16);
+            reinterpret_cast<uint4 *>(dst)[i] = make_uint4(p[0], p[1], p[2], p[3]);
+        }
+    }
+}
+
+namespace {
+
+template <typename WT>
+hipError_t quantize_bits(const void *w, int64_t n, int64_t k, int gs, int bits, uint32_t *codes,
+                         void *scales, void *biases, hipStream_t stream)
+{
+    const int64_t chunks = n * (k / kLaneChunk);
+    const dim3 block(256);
+    const dim3 grid((unsigned)((chunks + 255) / 256));
+    const WT *wp = static_cast<const WT *>(w);
+    WT *sp = static_cast<WT *>(scales), *bp = static_cast<WT *>(biases);
+    switch (bits) {
+#define NQ_Q(B)                                                                            \
+    case B:                                                                                \
+        quantize_kernel<B, WT><<<grid, block, 0, stream>>>(wp, chunks, k, gs, codes, sp, bp); \
+        break;
+        NQ_Q(1) NQ_Q(2) NQ_Q(3) NQ_Q(4) NQ_Q(5) NQ_Q(6) NQ_Q(8)
+#undef NQ_Q
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename ST, typename OT>
+hipError_t dequantize_bits(const uint32_t *codes, const void *scales, const void *biases,
+                           int64_t n, int64_t k, int gs, int bits, void *out, hipStream_t stream)
+{
+    const int64_t chunks = n * (k / kLaneChunk);
+    const dim3 block(256);
+    const dim3 grid((unsigned)((chunks + 255) / 256));
+    const ST *sp = static_cast<const ST *>(scales), *bp = static_cast<const ST *>(biases);
+    OT *op = static_cast<OT *>(out);
+    switch (bits) {
+#define NQ_D(B)                                                                                 \
+    case B:                                                                                     \
+        dequantize_kernel<B, ST, OT><<<grid, block, 0, stream>>>(codes, sp, bp, chunks, k, gs, op); \
+        break;
+        NQ_D(1) NQ_D(2) NQ_D(3) NQ_D(4) NQ_D(5) NQ_D(6) NQ_D(8)
+#undef NQ_D
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *w, int w_dt, int64_t n, int64_t k, int gs, int bits,
+                           uint32_t *codes, void *scales, void *biases, hipStream_t stream)
+{
+    if (w_dt == DT_F32) return quantize_bits<float>(w, n, k, gs, bits, codes, scales, biases, stream);
+    return quantize_bits<bf16_bits>(w, n, k, gs, bits, codes, scales, biases, stream);
+}
+
+hipError_t launch_dequantize(const uint32_t *codes, const void *scales, const void *biases,
+                             int sb_dt, int64_t n, int64_t k, int gs, int bits, void *out,
+                             int out_dt, hipStream_t stream)
+{
+    if (sb_dt == DT_F32) {
+        if (out_dt == DT_F32)
+            return dequantize_bits<float, float>(codes, scales, biases, n, k, gs, bits, out, stream);
+        return dequantize_bits<float, bf16_bits>(codes, scales, biases, n, k, gs, bits, out, stream);
+    }
+    if (out_dt == DT_F32)
+        return dequantize_bits<bf16_bits, float>(codes, scales, biases, n, k, gs, bits, out, stream);
+    return dequantize_bits<bf16_bits, bf16_bits>(codes, scales, biases, n, k, gs, bits, out, stream);
+}
+
+}  // namespace nqk

@@ -1,0 +1,209 @@
+/*
+ * nq.h -- group-wise affine quantization and quantized matrix products on
+ * AMD Instinct MI355X (gfx950).  C ABI of libnq.so.
+ *
+ * What the operations compute is defined by the "Quantization" page of the
+ * nuvec documentation (hupe1980.github.io/nuvec/docs/quantization/):
+ *   - section "Affine": each row of the weights w [n, k] is cut into groups of
+ *     group_size (32, 64 or 128) consecutive values; each group keeps one scale
+ *     and one bias, each value becomes a `bits`-bit code packed into uint32
+ *     words, and w ~ scale * code + bias;
+ *   - section "Affine", example: the product is x times the TRANSPOSED weights
+ *     (quantized_matmul with transpose = true), dequantize returns the
+ *     approximate weights;
+ *   - section "Floating-point formats", example: the product comes out in x's
+ *     dtype;
+ *   - section "Products on the GPU": few rows run as matrix-vector products,
+ *     many rows as tiled products, split-K serves a small output with a long
+ *     inner dimension; in row-exact mode every row of a product of up to 8
+ *     rows equals that row's one-row product bit for bit;
+ *   - section "Mixture of experts": gather_qmm multiplies each row by the
+ *     weights of the expert chosen for it, without gathering the weights.
+ * The nuvec API index (docs.rs/nuvec) adds: scales are stored in the weights'
+ * dtype (struct Quantized); the row-independence limit ROW_INDEPENDENT_ROWS
+ * (constant; 8 rows per the section above); the choice of kernel depends only
+ * on shapes, dtypes, options and the row-exact mode (section "Determinism",
+ * "Routing is pure"); and results are bit-identical run to run (section
+ * "Determinism").
+ *
+ * Conventions shared by every entry point:
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronises; a call only validates its
+ *     arguments and enqueues kernels on `stream` (0 = the null stream).
+ *   - Arrays are dense and row-major.  Base pointers of x, w, codes, the
+ *     output and the workspace must be 16-byte aligned; scales and biases
+ *     must be aligned to their element size.
+ *   - Layout of a quantized matrix of n rows and k columns (k a multiple of
+ *     group_size): codes [n, k*bits/32] uint32, scales [n, k/group_size] and
+ *     biases [n, k/group_size] in sb_dt.  Element j of a row occupies bits
+ *     [j*bits, (j+1)*bits) of the row's little-endian bit stream (bit i of the
+ *     stream is bit i%32 of word i/32): least significant bits first.
+ *   - Every argument is checked before anything is enqueued.  On an error the
+ *     call returns a non-zero nq_status, writes nothing, enqueues nothing, and
+ *     nq_last_error() names the entry point and the reason (a thread-local
+ *     string).  A launch failure reported by the HIP runtime is NQ_ERR_LAUNCH.
+ *   - A call with an empty output (m == 0 or n == 0, rows == 0) returns NQ_OK
+ *     and enqueues nothing.  k == 0 gives an all-zero product.
+ *   - Outputs must not overlap any input or each other (NQ_ERR_ALIAS).
+ *   - No float atomics are used: the same call on the same inputs gives the
+ *     same bits, whatever else runs on the device.
+ *   - Calls are reentrant across host threads and streams.
+ */
+#ifndef NQ_H
+#define NQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NQ_OK = 0,
+    NQ_ERR_NULL = 1,      /* a required pointer is null */
+    NQ_ERR_DTYPE = 2,     /* unknown dtype, or a dtype pair not supported */
+    NQ_ERR_QUANT = 3,     /* group_size not in {32, 64, 128}, or bits not supported by the
+                             operation: quantize/dequantize take 1-6 and 8, products 4 and 8 */
+    NQ_ERR_SHAPE = 4,     /* negative size, k % group_size != 0, bad expert count, size overflow */
+    NQ_ERR_ALIGN = 5,     /* a base pointer is not aligned as documented above */
+    NQ_ERR_ALIAS = 6,     /* an output overlaps an input or another output */
+    NQ_ERR_WORKSPACE = 7, /* workspace null or smaller than the *_workspace_bytes figure */
+    NQ_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch */
+    NQ_ERR_PLAN = 9       /* an explicit plan that does not fit the shapes */
+} nq_status;
+
+typedef enum { NQ_F32 = 0, NQ_BF16 = 1 } nq_dtype;
+
+/* Rows of a product that keep the bits of their one-row product in every
+ * mode (nuvec API index, constant ROW_INDEPENDENT_ROWS). */
+#define NQ_ROW_INDEPENDENT_ROWS 8
+
+/* ---------------------------------------------------------------- quantize */
+
+/* Quantize w [n, k] (w_dt) in groups of group_size along each row
+ * ("Affine" section).  For each group: bias = the group minimum and
+ * scale = (max - min) / (2^bits - 1), computed in fp32 and rounded to w_dt;
+ * code = clamp(round_half_even((w - bias) / scale), 0, 2^bits - 1) with the
+ * STORED scale and bias, or 0 when the stored scale is 0.
+ * Outputs: codes [n, k*bits/32] uint32, scales and biases [n, k/group_size]
+ * in w_dt.  Bit-exact with IEEE fp32 arithmetic (no contraction, correctly
+ * rounded division, denormals kept).  Non-finite weights are outside the
+ * contract. */
+nq_status nq_quantize(const void *w, nq_dtype w_dt, int64_t n, int64_t k, int32_t group_size,
+                      int32_t bits, uint32_t *codes, void *scales, void *biases,
+                      hipStream_t stream);
+
+/* Dequantize ("Affine" section, q.dequantize): w_out[r, j] =
+ * round_to_out_dt(fmaf(scale, code, bias)) -- one fp32 fused multiply-add,
+ * then round-to-nearest-even into out_dt.  w_out: [n, k] in out_dt (the
+ * documented default is the scales' dtype; the caller passes it). */
+nq_status nq_dequantize(const uint32_t *codes, const void *scales, const void *biases,
+                        nq_dtype sb_dt, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                        void *w_out, nq_dtype out_dt, hipStream_t stream);
+
+/* ---------------------------------------------------------------- products */
+
+/* Kernel families ("Products on the GPU" section).  NQ_ROUTE_GEMV is the
+ * matrix-vector family for up to 8 rows per launch chunk; its K loop may be
+ * cut into `ksplit` slices of whole 32-element lane chunks whose partial sums
+ * are combined in a fixed order (split-K).  NQ_ROUTE_TILED is the tiled
+ * matrix-core (bf16 MFMA) product for many rows. */
+typedef enum { NQ_ROUTE_GEMV = 1, NQ_ROUTE_TILED = 2 } nq_route;
+
+typedef struct {
+    int32_t route;          /* nq_route */
+    int32_t ksplit;         /* GEMV: K slices per output row, 1..8 (1 = no split) */
+    int32_t rows_per_wave;  /* GEMV: output rows per 64-lane wavefront */
+    int32_t tile_m;         /* TILED: rows of x per workgroup tile */
+    int32_t tile_n;         /* TILED: weight rows per workgroup tile */
+    int32_t reserved[3];    /* zero */
+} nq_plan;
+
+/* The kernel choice for a product y[m, n] = x[m, k] . w_hat[n, k]^T.  A pure
+ * function of its arguments and the device generation.  With row_exact = 0,
+ * m <= 8 takes the GEMV family and m > 8 the tiled family (x in bf16; fp32 x
+ * stays on the GEMV family, which keeps fp32 activations).  With
+ * row_exact = 1 every m takes the GEMV family in chunks of at most 8 rows.
+ * The GEMV family's ksplit and rows_per_wave depend only on (n, k,
+ * group_size, bits, dtypes), never on m, which is what makes its rows
+ * independent of how many rows share a call. */
+nq_status nq_qmm_plan(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                      nq_dtype x_dt, nq_dtype sb_dt, int32_t row_exact, nq_plan *plan);
+
+/* Workspace bytes a product needs (0 for every current plan; reserved for
+ * cross-workgroup split-K). */
+size_t nq_qmm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group_size,
+                              int32_t bits, nq_dtype x_dt, nq_dtype sb_dt, int32_t row_exact);
+
+/* y [m, n] (x_dt) = x [m, k] (x_dt) times the transposed dequantized
+ * weights (codes/scales/biases of n rows and k columns, see above), fp32
+ * accumulation ("Affine" example: x.quantized_matmul(&q, true)).  The kernel
+ * is chosen by nq_qmm_plan(..., row_exact = 0).  Rows m < 8 of a call are
+ * already bit-equal to their one-row calls, since the GEMV family keeps each
+ * row's arithmetic fixed. */
+nq_status nq_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const uint32_t *codes,
+                 const void *scales, const void *biases, nq_dtype sb_dt, int64_t n,
+                 int32_t group_size, int32_t bits, void *y, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* As nq_qmm in row-exact mode ("Products on the GPU" section; nuvec API index,
+ * with_row_exact): every row of y is bit-equal to nq_qmm on that row alone,
+ * for any m (chunks of at most NQ_ROW_INDEPENDENT_ROWS rows of the GEMV
+ * family). */
+nq_status nq_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t m, int64_t k,
+                           const uint32_t *codes, const void *scales, const void *biases,
+                           nq_dtype sb_dt, int64_t n, int32_t group_size, int32_t bits, void *y,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* As nq_qmm with an explicit plan (for tests and tuning).  NQ_ERR_PLAN if the
+ * plan does not fit.  Row independence is only promised for plans returned by
+ * nq_qmm_plan. */
+nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, int64_t m,
+                           int64_t k, const uint32_t *codes, const void *scales,
+                           const void *biases, nq_dtype sb_dt, int64_t n, int32_t group_size,
+                           int32_t bits, void *y, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------- mixture of experts */
+
+/* Workspace bytes nq_gather_qmm needs for these arguments. */
+size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n,
+                                     int32_t group_size, int32_t bits, nq_dtype x_dt,
+                                     nq_dtype sb_dt, int32_t sorted_hint);
+
+/* gather_qmm ("Mixture of experts" section): x [rows, l, k] (x_dt); stacked
+ * expert weights codes [e, n, k*bits/32], scales and biases [e, n, k/gs];
+ * rhs_idx [rows] uint32 (the expert of each row).  y [rows, l, n] (x_dt):
+ * y[r, j, :] = x[r, j, :] times the transposed weights of expert rhs_idx[r].
+ * Weights are indexed in place, never copied.  An id >= e gives an all-zero
+ * row of y (the id is never used to address memory).  sorted_hint = 1 says
+ * the ids are non-decreasing; it may change the kernel, never the result:
+ * every row is bit-equal to nq_qmm_row_exact of x[r] with expert
+ * rhs_idx[r]'s weights (and so to nq_qmm of it when l <= 8). */
+nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                        const uint32_t *codes, const void *scales, const void *biases,
+                        nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                        const uint32_t *rhs_idx, int32_t sorted_hint, void *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- errors */
+
+/* A static description of a status code. */
+const char *nq_status_string(nq_status s);
+
+/* The message of the calling thread's last call ("" if it succeeded): the
+ * entry point and the reason, e.g. "nq_qmm: k=500 is not a multiple of
+ * group_size=64".  Valid until the thread's next call into the library. */
+const char *nq_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *nq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NQ_H */

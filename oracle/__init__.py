@@ -43,7 +43,7 @@ def lib():
         L.oracle_bf16_round.argtypes = [_c_p, _c_p, _c_i64]
         for f in ("oracle_quantize", "oracle_dequantize", "oracle_dequantize_f64",
                   "oracle_qmm_f64", "oracle_qmm_sample_f64", "oracle_gather_qmm_f64",
-                  "oracle_bits_supported", "oracle_group_supported"):
+                  "oracle_bits_supported", "oracle_group_supported", "oracle_threads"):
             getattr(L, f).restype = _c_int
         L.oracle_bf16_round.restype = None
         _lib = L
@@ -64,6 +64,11 @@ def _ptr(a):
 
 def _c(a):
     return np.ascontiguousarray(a)
+
+
+def threads():
+    """OpenMP threads the oracle's loops use."""
+    return int(lib().oracle_threads())
 
 
 def bf16_round(a):

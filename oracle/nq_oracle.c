@@ -45,6 +45,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <omp.h>
+
 enum { OR_F32 = 0, OR_BF16 = 1 };
 
 /* ---- storage formats ---------------------------------------------------- */
@@ -131,6 +133,9 @@ int oracle_bits_supported(int bits)
 }
 
 int oracle_group_supported(int gs) { return gs == 32 || gs == 64 || gs == 128; }
+
+/* Threads the OpenMP loops below run on. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 void oracle_bf16_round(const float *in, uint16_t *out, int64_t count)
 {

@@ -1,0 +1,232 @@
+"""Host-side checks of libnq.so that need no GPU.
+
+- The library loads and exports every function include/nq.h declares.
+- The planner is pure and its split of K never depends on the row count
+  ("Determinism" section of the nuvec API index: routing is pure; rows of a
+  row-exact product equal their one-row products).
+- Every argument error is reported before anything is enqueued: each call
+  below is invalid and returns its status without touching the device (the
+  pointers are fake and never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from group_wise_affine_quantize_amd import _binding as B
+
+HEADER = os.path.join(ROOT, "include", "nq.h")
+
+NQ_OK, NQ_ERR_NULL, NQ_ERR_DTYPE, NQ_ERR_QUANT, NQ_ERR_SHAPE = 0, 1, 2, 3, 4
+NQ_ERR_ALIGN, NQ_ERR_ALIAS, NQ_ERR_WORKSPACE, NQ_ERR_LAUNCH, NQ_ERR_PLAN = 5, 6, 7, 8, 9
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.library_path()):
+        pytest.fail("libnq.so is not built (python -m group_wise_affine_quantize_amd.build)")
+    return B.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"nq_quantize", "nq_dequantize", "nq_qmm", "nq_qmm_row_exact", "nq_gather_qmm",
+            "nq_qmm_plan", "nq_last_error", "nq_status_string"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    # the binding wraps every declared entry point under the same name
+    for name in names:
+        assert name in B._SIGNATURES, name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert re.search(r"#define NQ_ROW_INDEPENDENT_ROWS 8\b", text)
+    assert B.NQ_ROW_INDEPENDENT_ROWS == 8
+    assert re.search(r"NQ_F32 = 0, NQ_BF16 = 1", text)
+    assert re.search(r"NQ_ROUTE_GEMV = 1, NQ_ROUTE_TILED = 2", text)
+    assert ctypes.sizeof(B.Plan) == 32
+
+
+def test_status_strings(lib):
+    for st in range(10):
+        assert lib.nq_status_string(st)
+    assert lib.nq_status_string(0) == b"ok"
+    assert lib.nq_version().count(b".") == 2
+
+
+def plan(lib, m, n, k, gs=64, bits=4, x=BF16, sb=BF16, row_exact=0):
+    p = B.Plan()
+    st = lib.nq_qmm_plan(m, n, k, gs, bits, x, sb, row_exact, ctypes.byref(p))
+    assert st == NQ_OK, lib.nq_last_error()
+    return p
+
+
+def test_plan_is_pure_and_row_independent(lib):
+    shapes = [(14336, 4096), (4096, 4096), (1024, 14336), (1408, 2048), (256, 512), (7, 64)]
+    for n, k in shapes:
+        ref = plan(lib, 1, n, k)
+        assert ref.route == B.NQ_ROUTE_GEMV
+        for m in (1, 2, 3, 5, 8):
+            p = plan(lib, m, n, k)
+            assert (p.route, p.ksplit, p.rows_per_wave) == (ref.route, ref.ksplit,
+                                                            ref.rows_per_wave)
+        for m in (1, 9, 17, 100, 2048):
+            p = plan(lib, m, n, k, row_exact=1)
+            assert (p.route, p.ksplit, p.rows_per_wave) == (ref.route, ref.ksplit,
+                                                            ref.rows_per_wave)
+        again = plan(lib, 1, n, k)
+        assert bytes(again) == bytes(ref)
+
+
+def test_plan_routes(lib):
+    assert plan(lib, 8, 14336, 4096).route == B.NQ_ROUTE_GEMV
+    assert plan(lib, 9, 14336, 4096).route == B.NQ_ROUTE_TILED
+    assert plan(lib, 2048, 14336, 4096).route == B.NQ_ROUTE_TILED
+    assert plan(lib, 2048, 14336, 4096, x=F32, sb=F32).route == B.NQ_ROUTE_GEMV
+    # long inner dimension with a small output splits K
+    assert plan(lib, 4, 1024, 14336).ksplit > 1
+    assert plan(lib, 1, 14336, 4096).ksplit == 1
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+FAKE2 = 0x40000000
+
+
+def _qmm(lib, entry="nq_qmm", x=FAKE, x_dt=BF16, m=4, k=128, codes=FAKE2, scales=FAKE2 + 0x100000,
+         biases=FAKE2 + 0x200000, sb_dt=BF16, n=64, gs=64, bits=4, y=FAKE2 + 0x300000, ws=0,
+         ws_bytes=0):
+    fn = getattr(lib, entry)
+    return fn(x, x_dt, m, k, codes, scales, biases, sb_dt, n, gs, bits, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("entry", ["nq_qmm", "nq_qmm_row_exact"])
+def test_qmm_argument_errors(lib, entry):
+    cases = [
+        (dict(x_dt=7), NQ_ERR_DTYPE, "dtype"),
+        (dict(sb_dt=-1), NQ_ERR_DTYPE, "dtype"),
+        (dict(bits=3), NQ_ERR_QUANT, "bits=3"),
+        (dict(bits=16), NQ_ERR_QUANT, "bits=16"),
+        (dict(gs=16), NQ_ERR_QUANT, "group_size=16"),
+        (dict(k=100), NQ_ERR_SHAPE, "k=100 is not a multiple of group_size=64"),
+        (dict(m=-1), NQ_ERR_SHAPE, "negative"),
+        (dict(n=-2), NQ_ERR_SHAPE, "negative"),
+        (dict(k=1 << 33), NQ_ERR_SHAPE, "too large"),
+        (dict(y=0), NQ_ERR_NULL, "y is null"),
+        (dict(x=0), NQ_ERR_NULL, "non-null"),
+        (dict(codes=0), NQ_ERR_NULL, "non-null"),
+        (dict(x=FAKE + 8), NQ_ERR_ALIGN, "aligned"),
+        (dict(y=FAKE2 + 0x300004), NQ_ERR_ALIGN, "aligned"),
+        (dict(scales=FAKE2 + 0x100001), NQ_ERR_ALIGN, "aligned"),
+        (dict(y=FAKE), NQ_ERR_ALIAS, "y overlaps x"),
+        (dict(y=FAKE2 + 0x100000), NQ_ERR_ALIAS, "y overlaps scales"),
+        (dict(y=FAKE2 + 0x10), NQ_ERR_ALIAS, "y overlaps codes"),
+    ]
+    for kw, want, msg in cases:
+        st = _qmm(lib, entry, **kw)
+        assert st == want, (kw, st, lib.nq_last_error())
+        err = lib.nq_last_error().decode()
+        assert err.startswith(entry + ":") and msg in err, (kw, err)
+
+
+def test_empty_products_enqueue_nothing(lib):
+    # m == 0 or n == 0: OK without touching any pointer (all null here)
+    assert _qmm(lib, m=0, x=0, codes=0, scales=0, biases=0, y=0) == NQ_OK
+    assert lib.nq_last_error() == b""
+    assert _qmm(lib, n=0, x=0, codes=0, scales=0, biases=0, y=0) == NQ_OK
+    st = lib.nq_gather_qmm(0, BF16, 0, 1, 128, 0, 0, 0, BF16, 4, 64, 64, 4, 0, 0, 0, 0, 0, None)
+    assert st == NQ_OK
+
+
+def test_plan_errors(lib):
+    p = B.Plan()
+    p.route = 99
+    st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, BF16, 4, 128, FAKE2, FAKE2 + 0x100000,
+                              FAKE2 + 0x200000, BF16, 64, 64, 4, FAKE2 + 0x300000, 0, 0, None)
+    assert st == NQ_ERR_PLAN and b"unknown route" in lib.nq_last_error()
+    p.route, p.ksplit, p.rows_per_wave = B.NQ_ROUTE_GEMV, 9, 4
+    st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, BF16, 4, 128, FAKE2, FAKE2 + 0x100000,
+                              FAKE2 + 0x200000, BF16, 64, 64, 4, FAKE2 + 0x300000, 0, 0, None)
+    assert st == NQ_ERR_PLAN
+    p.route, p.tile_m, p.tile_n = B.NQ_ROUTE_TILED, 128, 128
+    st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, F32, 4, 128, FAKE2, FAKE2 + 0x100000,
+                              FAKE2 + 0x200000, BF16, 64, 64, 4, FAKE2 + 0x300000, 0, 0, None)
+    assert st == NQ_ERR_PLAN and b"bf16" in lib.nq_last_error()
+    st = lib.nq_qmm_with_plan(None, FAKE, BF16, 4, 128, FAKE2, 0, 0, BF16, 64, 64, 4, 0, 0, 0,
+                              None)
+    assert st == NQ_ERR_NULL
+
+
+def test_quantize_argument_errors(lib):
+    q = lambda **kw: lib.nq_quantize(kw.get("w", FAKE), kw.get("dt", BF16), kw.get("n", 8),
+                                     kw.get("k", 128), kw.get("gs", 64), kw.get("bits", 4),
+                                     kw.get("codes", FAKE2), kw.get("scales", FAKE2 + 0x100000),
+                                     kw.get("biases", FAKE2 + 0x200000), None)
+    assert q(dt=3) == NQ_ERR_DTYPE
+    assert q(bits=7) == NQ_ERR_QUANT
+    assert q(bits=0) == NQ_ERR_QUANT
+    assert q(gs=256) == NQ_ERR_QUANT
+    assert q(k=96) == NQ_ERR_SHAPE
+    assert q(w=0) == NQ_ERR_NULL
+    assert q(w=FAKE + 4) == NQ_ERR_ALIGN
+    assert q(codes=FAKE) == NQ_ERR_ALIAS
+    assert q(scales=FAKE2 + 0x8) == NQ_ERR_ALIAS
+    assert b"nq_quantize:" in lib.nq_last_error()
+    assert q(n=0, w=0, codes=0, scales=0, biases=0) == NQ_OK
+    d = lambda **kw: lib.nq_dequantize(kw.get("codes", FAKE2), kw.get("scales", FAKE2 + 0x100000),
+                                       kw.get("biases", FAKE2 + 0x200000), kw.get("sb", BF16),
+                                       kw.get("n", 8), kw.get("k", 128), kw.get("gs", 64),
+                                       kw.get("bits", 4), kw.get("out", FAKE), kw.get("odt", F32),
+                                       None)
+    assert d(odt=5) == NQ_ERR_DTYPE
+    assert d(bits=7) == NQ_ERR_QUANT
+    assert d(k=33) == NQ_ERR_SHAPE
+    assert d(out=0) == NQ_ERR_NULL
+    assert d(out=FAKE2 + 0x100000) == NQ_ERR_ALIAS
+    assert d(out=FAKE + 2) == NQ_ERR_ALIGN
+
+
+def test_gather_argument_errors(lib):
+    def g(**kw):
+        a = dict(x=FAKE, x_dt=BF16, rows=4, l=1, k=128, codes=FAKE2, scales=FAKE2 + 0x100000,
+                 biases=FAKE2 + 0x200000, sb_dt=BF16, e=8, n=64, gs=64, bits=4,
+                 idx=FAKE2 + 0x300000, sorted_hint=0, y=FAKE2 + 0x400000)
+        a.update(kw)
+        return lib.nq_gather_qmm(a["x"], a["x_dt"], a["rows"], a["l"], a["k"], a["codes"],
+                                 a["scales"], a["biases"], a["sb_dt"], a["e"], a["n"], a["gs"],
+                                 a["bits"], a["idx"], a["sorted_hint"], a["y"], 0, 0, None)
+    assert g(e=-1) == NQ_ERR_SHAPE
+    assert g(k=100) == NQ_ERR_SHAPE
+    assert g(idx=0) == NQ_ERR_NULL
+    assert g(y=FAKE2 + 0x300000) == NQ_ERR_ALIAS
+    assert b"rhs_idx" in lib.nq_last_error()
+    assert g(idx=FAKE2 + 0x300002) == NQ_ERR_ALIGN
+    assert g(bits=5) == NQ_ERR_QUANT
+    assert b"nq_gather_qmm:" in lib.nq_last_error()
+
+
+def test_error_string_is_thread_local(lib):
+    import threading
+    _qmm(lib, k=100)
+    seen = {}
+
+    def other():
+        seen["before"] = lib.nq_last_error()
+        _qmm(lib, bits=3)
+        seen["after"] = lib.nq_last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["before"] == b""
+    assert b"bits=3" in seen["after"]
+    assert b"k=100" in lib.nq_last_error()

@@ -1,0 +1,284 @@
+"""GPU parity: every kernel of libnq against the CPU oracle, through the C ABI.
+
+Bars (fixed by the library's contract, include/nq.h):
+  - codes, scales, biases of quantize and the output of dequantize: bit-exact;
+  - products: per row, max_n |y - y_ref| / max_n |y_ref| <= 1e-3 for fp32
+    outputs and <= 1e-2 for bf16 outputs, y_ref the oracle's fp64 product;
+  - row-exact products, and every row of a matrix-vector product: bit-equal
+    to the one-row product;
+  - gather: each row bit-equal to the plain product with its expert's slab;
+  - the same call twice, or on another stream: identical bits.
+Inputs are seeded (group_wise_affine_quantize_amd.synthetic); sizes span
+several tiles/steps with ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import assert_rows_close, bits_equal, dev, host, tolerance, values
+from group_wise_affine_quantize_amd import _binding as B
+from group_wise_affine_quantize_amd import synthetic
+
+pytestmark = pytest.mark.gpu
+
+DTYPE_COMBOS = [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16")]  # (x, w)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def quantized_case(seed, n, k, gs, bits, w_dtype, m=1, x_dtype=None, sigma=1.0):
+    w, x = synthetic.random_case(seed, (n, k), (m, k), sigma, w_dtype, x_dtype or w_dtype)
+    c, s, b = O.quantize(w, gs, bits)
+    return w, x, c, s, b
+
+
+def gpu_quantized(c, s, b):
+    return dev(c), dev(s), dev(b)
+
+
+# ------------------------------------------------------------------ quantize
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_quantize_bit_exact(bits, gs, w_dtype):
+    n, k = 157, 6 * gs
+    w, _ = synthetic.random_case(bits * 1000 + gs, (n, k), (1, k), 0.5, w_dtype)
+    wv = values(w).astype(np.float32)
+    # special groups: constant, signed zeros, denormals, large magnitudes, exact ties
+    wv[0, :gs] = 0.75
+    wv[1, :gs] = 0.0
+    wv[1, 1:gs:2] = -0.0
+    wv[2, :gs] = np.linspace(-1e-39, 1e-39, gs, dtype=np.float32)
+    wv[3, :gs] = np.linspace(-3e37, 3e37, gs, dtype=np.float32)
+    wv[4, :gs] = np.arange(gs, dtype=np.float32) % ((1 << bits) + 1)
+    w = synthetic.to_bf16_bits(wv) if w_dtype == "bf16" else wv
+    c_ref, s_ref, b_ref = O.quantize(w, gs, bits)
+    c, s, b = B.nq_quantize(dev(w), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c), c_ref)
+    assert np.array_equal(host(s).view(np.uint8), s_ref.view(np.uint8))
+    assert np.array_equal(host(b).view(np.uint8), b_ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("sb_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_dequantize_bit_exact(bits, gs, sb_dtype, out_dtype):
+    n, k = 93, 5 * gs
+    w, _, c, s, b = quantized_case(7 * bits + gs, n, k, gs, bits, sb_dtype)
+    want = O.dequantize(c, s, b, gs, bits, out_dtype=np.float32 if out_dtype == "f32" else np.uint16)
+    got = B.nq_dequantize(*gpu_quantized(c, s, b), gs, bits,
+                          out_dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
+    assert np.array_equal(host(got), want)
+
+
+# ------------------------------------------------------------------ matrix-vector family
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("x_dtype,w_dtype", DTYPE_COMBOS)
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_gemv_parity(bits, gs, x_dtype, w_dtype, m):
+    n, k = 131, 4096 + 384          # 3 K steps, the last one ragged; n not a multiple of 16
+    w, x, c, s, b = quantized_case(bits + gs + m, n, k, gs, bits, w_dtype, m, x_dtype, 0.02)
+    plan = B.nq_qmm_plan(m, n, k, gs, bits, torch.float32 if x_dtype == "f32" else torch.bfloat16,
+                         torch.float32 if w_dtype == "f32" else torch.bfloat16)
+    assert plan.route == B.NQ_ROUTE_GEMV
+    y = B.nq_qmm(dev(x), *gpu_quantized(c, s, b), gs, bits)
+    y_ref = O.qmm_f64(x, c, s, b, gs, bits)
+    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "gemv")
+
+
+@pytest.mark.parametrize("ksplit", [1, 2, 3, 4, 5, 7, 8])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_splitk_parity(ksplit, x_dtype):
+    n, k, m, gs, bits = 37, 2048 * 7 + 64, 4, 64, 4     # 8 K steps, the last one ragged
+    w, x, c, s, b = quantized_case(ksplit, n, k, gs, bits, "bf16", m, x_dtype, 0.02)
+    plan = B.Plan()
+    plan.route, plan.ksplit, plan.rows_per_wave = B.NQ_ROUTE_GEMV, ksplit, 4
+    xs = dev(x)
+    q = gpu_quantized(c, s, b)
+    y = B.nq_qmm_with_plan(plan, xs, *q, gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), tolerance(y.dtype), "splitk")
+    for i in range(m):   # rows independent of the row count under any split
+        yi = B.nq_qmm_with_plan(plan, xs[i:i + 1].contiguous(), *q, gs, bits)
+        assert bits_equal(yi[0], y[i])
+
+
+def test_splitk_is_chosen_for_long_k():
+    p = B.nq_qmm_plan(4, 1024, 14336, 64, 4, torch.bfloat16, torch.bfloat16)
+    assert p.route == B.NQ_ROUTE_GEMV and p.ksplit > 1
+
+
+# ------------------------------------------------------------------ tiled family
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m,n", [(1, 64), (5, 129), (130, 257), (300, 100)])
+def test_tiled_parity(bits, gs, w_dtype, m, n):
+    k = 4 * 128 + gs
+    w, x, c, s, b = quantized_case(m + n + bits, n, k, gs, bits, w_dtype, m, "bf16", 0.02)
+    plan = B.Plan()
+    plan.route, plan.tile_m, plan.tile_n = B.NQ_ROUTE_TILED, 128, 128
+    y = B.nq_qmm_with_plan(plan, dev(x), *gpu_quantized(c, s, b), gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled")
+
+
+def test_tiled_is_chosen_for_many_rows():
+    m, n, k, gs, bits = 200, 192, 1024, 64, 4
+    w, x, c, s, b = quantized_case(5, n, k, gs, bits, "bf16", m, "bf16", 0.02)
+    assert B.nq_qmm_plan(m, n, k, gs, bits, torch.bfloat16, torch.bfloat16).route == B.NQ_ROUTE_TILED
+    y = B.nq_qmm(dev(x), *gpu_quantized(c, s, b), gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled auto")
+
+
+# ------------------------------------------------------------------ row-exact
+
+
+@pytest.mark.parametrize("x_dtype,w_dtype", DTYPE_COMBOS)
+@pytest.mark.parametrize("bits,gs,n,k", [(4, 64, 260, 4096), (8, 128, 96, 4096),
+                                         (4, 64, 96, 14336), (4, 32, 50, 2048 + 96)])
+def test_row_exact_bitwise(x_dtype, w_dtype, bits, gs, n, k):
+    m = 21
+    w, x, c, s, b = quantized_case(n + k, n, k, gs, bits, w_dtype, m, x_dtype, 0.02)
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y = B.nq_qmm_row_exact(xs, *q, gs, bits)
+    y_ref = O.qmm_f64(x, c, s, b, gs, bits)
+    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "row-exact")
+    for i in range(m):
+        y1 = B.nq_qmm(xs[i:i + 1].contiguous(), *q, gs, bits)
+        assert bits_equal(y1[0], y[i]), i
+    for mm in (2, 5, 8):   # plain products of up to 8 rows are row-exact too
+        yb = B.nq_qmm(xs[:mm].contiguous(), *q, gs, bits)
+        assert bits_equal(yb, y[:mm])
+
+
+# ------------------------------------------------------------------ gather
+
+
+@pytest.mark.parametrize("x_dtype,w_dtype", DTYPE_COMBOS)
+@pytest.mark.parametrize("l", [1, 3, 10])
+def test_gather_parity(x_dtype, w_dtype, l):
+    e, n, k, gs, bits, rows = 5, 100, 640, 64, 4, 37
+    rng = np.random.default_rng(l)
+    w, _ = synthetic.random_case(l, (e, n, k), (1, k), 0.02, w_dtype)
+    _, x = synthetic.random_case(l + 1, (1, 1), (rows, l, k), 1.0, "f32", x_dtype)
+    ids = rng.integers(0, e + 1, size=rows, dtype=np.uint32)   # id == e: zero rows
+    ids[0], ids[1] = e, 0
+    c, s, b = O.quantize(w, gs, bits)
+    xs, cs, ss, bs = dev(x), dev(c), dev(s), dev(b)
+    idx = dev(ids)
+    y = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, idx)
+    y_ref = O.gather_qmm_f64(x, c, s, b, gs, bits, ids)
+    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "gather")
+    yh = host(y)
+    for r in range(rows):
+        if ids[r] >= e:
+            assert np.all(values(yh[r]) == 0)
+            continue
+        yr = B.nq_qmm_row_exact(xs[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+        assert bits_equal(yr, y[r]), r
+        if l <= 8:
+            yq = B.nq_qmm(xs[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+            assert bits_equal(yq, y[r]), r
+
+
+def test_gather_sorted_hint_same_bits():
+    e, n, k, gs, bits, rows = 8, 128, 256, 64, 4, 4
+    w, x = synthetic.random_case(3, (e, n, k), (rows, 1, k), 1.0, "f32")
+    c, s, b = O.quantize(w, gs, bits)
+    ids = np.array([0, 0, 3, 5], np.uint32)
+    args = (dev(x), dev(c), dev(s), dev(b), gs, bits, dev(ids))
+    y0 = B.nq_gather_qmm(*args, sorted_hint=False)
+    y1 = B.nq_gather_qmm(*args, sorted_hint=True)
+    assert y0.shape == (4, 1, 128)
+    assert bits_equal(y0, y1)
+    assert_rows_close(host(y0), O.gather_qmm_f64(x, c, s, b, gs, bits, ids), 1e-3, "page example")
+
+
+# ------------------------------------------------------------------ determinism and edges
+
+
+def test_run_to_run_and_stream_determinism():
+    gs, bits = 64, 4
+    cases = [(4, 1024, 14336), (300, 256, 1024), (1, 2048, 4096)]
+    side = torch.cuda.Stream()
+    for m, n, k in cases:
+        w, x, c, s, b = quantized_case(m, n, k, gs, bits, "bf16", m, "bf16", 0.02)
+        xs, q = dev(x), gpu_quantized(c, s, b)
+        y0 = B.nq_qmm(xs, *q, gs, bits)
+        y1 = B.nq_qmm(xs, *q, gs, bits)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            y2 = B.nq_qmm(xs, *q, gs, bits, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert bits_equal(y0, y1) and bits_equal(y0, y2)
+    wq = dev(synthetic.random_case(1, (64, 256), (1, 1), 1.0, "bf16")[0])
+    a = B.nq_quantize(wq, 64, 4)
+    bq = B.nq_quantize(wq, 64, 4)
+    assert all(bits_equal(u, v) for u, v in zip(a, bq))
+
+
+def test_edge_cases():
+    gs, bits = 64, 4
+    # k == 0: the product is all zeros
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((5, 0), dtype=torch.int32, device="cuda")
+    s = torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((3, 5), 7.0, dtype=torch.bfloat16, device="cuda")
+    B.nq_qmm(x, c, s, s.clone(), gs, bits, y=y)
+    assert torch.all(y == 0)
+    # m == 0 and n == 0: nothing to do
+    x0 = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    w, _, cc, ss, bb = quantized_case(0, 8, 64, gs, bits, "bf16")
+    assert B.nq_qmm(x0, *gpu_quantized(cc, ss, bb), gs, bits).shape == (0, 8)
+    # gather with no experts at all: every row is zero
+    xg = dev(synthetic.random_case(2, (1, 1), (4, 1, 64), 1.0, "f32")[1])
+    cz = torch.zeros((0, 8, 8), dtype=torch.int32, device="cuda")
+    sz = torch.zeros((0, 8, 1), dtype=torch.float32, device="cuda")
+    yg = B.nq_gather_qmm(xg, cz, sz, sz.clone(), gs, bits, dev(np.zeros(4, np.uint32)))
+    assert torch.all(yg == 0)
+    # an invalid call writes nothing: y aliasing the codes is rejected
+    x1 = dev(synthetic.random_case(0, (1, 1), (1, 64), 1.0, "bf16")[1])
+    qc = gpu_quantized(cc, ss, bb)
+    before = qc[0].clone()
+    y_alias = qc[0].view(torch.bfloat16)[0:1, 0:8]
+    with pytest.raises(B.NQError) as err:
+        B.nq_qmm(x1, *qc, gs, bits, y=y_alias)
+    assert err.value.status == 6 and "y overlaps codes" in err.value.message
+    torch.cuda.synchronize()
+    assert torch.equal(qc[0], before)
+
+
+def test_one_hot_and_ones_special_cases():
+    """One-hot rows of x pick a column of the dequantized weights (within the
+    output rounding); rows of ones give the row sums of the weights."""
+    n, k, gs, bits = 70, 256, 64, 4
+    w, _, c, s, b = quantized_case(4, n, k, gs, bits, "f32")
+    x = np.zeros((8, k), np.float32)
+    cols = [0, 1, 63, 64, 127, 200, 255]
+    for i, col in enumerate(cols):
+        x[i, col] = 1.0
+    x[7, :] = 1.0
+    y = host(B.nq_qmm(dev(x), *gpu_quantized(c, s, b), gs, bits)).astype(np.float64)
+    w_hat = O.dequantize_f64(c, s, b, gs, bits)
+    top = (1 << bits) - 1
+    for i, col in enumerate(cols):
+        sc, bi = s[:, col // gs].astype(np.float64), b[:, col // gs].astype(np.float64)
+        bound = 2.0 ** -22 * (np.abs(sc) * top + np.abs(bi))   # two fp32 roundings
+        assert np.all(np.abs(y[i] - w_hat[:, col]) <= bound)
+    assert np.allclose(y[7], w_hat.sum(axis=1), rtol=1e-5, atol=1e-5)
