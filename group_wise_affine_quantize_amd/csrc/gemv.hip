@@ -27,11 +27,15 @@
 // launch chunking, so every row of a batched call is bit-equal to its
 // one-row call.  There are no atomics; results are run-to-run identical.
 //
-// 4-bit codes with bf16 activations use v_dot2_f32_bf16: two codes are turned
-// into the bf16 pair (128 + q_a, 128 + q_b) with one and-or (128 + q is exact
-// in bf16 for q < 128), dotted with the matching activation pair, and the
-// 128 * sum(x) offset is removed once per lane chunk.  Other cases convert
-// codes to fp32 and use fp32 FMAs.
+// 4-bit codes with bf16 activations use v_dot2_f32_bf16.  A code word is split
+// into its even and odd nibbles (one and, one shift and and), and each byte
+// pair becomes the bf16 pair (128 + q_a, 128 + q_b) with one v_perm_b32 that
+// takes the 0x43 exponent bytes from a register (128 + q is exact in bf16 for
+// q < 128): 7 VALU operations per 8 codes.  The activations are paired in the
+// same order ((x0,x2) (x4,x6) (x1,x3) (x5,x7) per word) and the
+// 128 * sum(x) offset is removed once per lane chunk.  For one or two
+// activation rows the pairs and chunk sums are prepared once per workgroup in
+// LDS.  Other cases convert codes to fp32 and use fp32 FMAs.
 #include <algorithm>
 
 #include "nq_device.h"
@@ -82,18 +86,156 @@ __device__ __forceinline__ void load_chunk_words(const uint32_t *src, uint32_t *
     }
 }
 
-template <int BITS, int RW>
+// One K step of a wave's work, as loaded: raw scale/bias storage bits
+// (converted only when used, so no conversion forces an early wait on the
+// load), raw code words and, for few activation rows read directly, the
+// lane's activations.  Scales and biases are loaded before the codes, so they
+// have arrived whenever the codes have.
+template <int BITS, int RW, int XW>
 struct Stage {
+    uint32_t s[RW], b[RW];
+    uint4 xr[XW > 0 ? XW : 1];
     uint32_t cw[RW][BITS];
-    float s[RW], b[RW];
 };
 
-template <int BITS, typename XT, typename ST, int MR, int RW>
+template <typename T>
+__device__ __forceinline__ uint32_t load_raw(const T *p, int64_t i)
+{
+    if constexpr (sizeof(T) == 2) return (uint32_t)p[i];
+    else return __float_as_uint(p[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ float raw_to_f32(uint32_t v)
+{
+    if constexpr (sizeof(T) == 2) return __uint_as_float(v << 16);
+    else return __uint_as_float(v);
+}
+
+// v from lane (lane ^ OFF) of the wave: DPP quad permutes for 1 and 2,
+// ds_swizzle (xor mode, within 32 lanes) for 4, 8 and 16, ds_bpermute for 32.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float v, int lane)
+{
+    const int iv = __float_as_int(v);
+    int r;
+    if constexpr (OFF == 1) r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);   // [1,0,3,2]
+    else if constexpr (OFF == 2) r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+    else if constexpr (OFF == 4 || OFF == 8 || OFF == 16)
+        r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (OFF << 10));
+    else r = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, iv);
+    return __int_as_float(r);
+}
+
+__device__ __forceinline__ float pick(bool c, float a, float b)
+{
+    // c ? a : b, written with integer masks so that it stays a register select
+    const int m = -(int)c;
+    return __int_as_float((__float_as_int(a) & m) | (__float_as_int(b) & ~m));
+}
+
+// Sum of V values over the 64 lanes (V a power of two <= 64).  At each xor
+// step a lane keeps half of its values and sends the other half, so every
+// value goes through the same pairwise tree (xor 32, 16, ..., 1) as a plain
+// butterfly, with V - 1 + 6 - log2(V) exchanges instead of 6 V.  Afterwards
+// lane L holds value L >> (6 - log2 V).
+template <int V, int OFF = 32>
+__device__ __forceinline__ float wave_reduce_transposed(float (&v)[V], int lane)
+{
+    if constexpr (OFF == 0) {
+        return v[0];
+    } else if constexpr (V > 1) {
+        const bool upper = (lane & OFF) != 0;
+        float h[V / 2];
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) {
+            const float send = pick(upper, v[i], v[i + V / 2]);
+            const float keep = pick(upper, v[i + V / 2], v[i]);
+            h[i] = keep + xor_lane<OFF>(send, lane);
+        }
+        return wave_reduce_transposed<V / 2, OFF / 2>(h, lane);
+    } else {
+        float r = v[0] + xor_lane<OFF>(v[0], lane);
+        float one[1] = {r};
+        return wave_reduce_transposed<1, OFF / 2>(one, lane);
+    }
+}
+
+template <int V>
+constexpr int ilog2() { return V <= 1 ? 0 : 1 + ilog2<V / 2>(); }
+
+// ---- arithmetic of one 32-element lane chunk, shared by every variant so
+// ---- that a row's bits never depend on which variant ran it.
+
+// Activation pairs of one code word (8 bf16 in dwords d0..d3 = (x1:x0)
+// (x3:x2) (x5:x4) (x7:x6)), in the order of the code pairs below.
+__device__ __forceinline__ void x_pairs_word(uint4 d, uint32_t *xp)
+{
+    xp[0] = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);   // (x0, x2)
+    xp[1] = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);   // (x4, x6)
+    xp[2] = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);   // (x1, x3)
+    xp[3] = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);   // (x5, x7)
+}
+
+// Sum of the 8 activations of a word, accumulated onto X.
+__device__ __forceinline__ float x_sum_word(uint4 d, float X)
+{
+    constexpr uint32_t kOnes = 0x3f803f80u;   // bf16 pair (1, 1)
+    X = dot2_bf16(d.x, kOnes, X);
+    X = dot2_bf16(d.y, kOnes, X);
+    X = dot2_bf16(d.z, kOnes, X);
+    return dot2_bf16(d.w, kOnes, X);
+}
+
+// D += sum over the 8 codes of a 4-bit word of x_i * (128 + q_i).
+__device__ __forceinline__ float word_dot_magic(uint32_t w, const uint32_t *xp, uint32_t mag, float D)
+{
+    const uint32_t lo = w & 0x0f0f0f0fu;          // q0 q2 q4 q6
+    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;   // q1 q3 q5 q7
+    D = dot2_bf16(xp[0], __builtin_amdgcn_perm(mag, lo, 0x04010400u), D);   // (q0, q2)
+    D = dot2_bf16(xp[1], __builtin_amdgcn_perm(mag, lo, 0x04030402u), D);   // (q4, q6)
+    D = dot2_bf16(xp[2], __builtin_amdgcn_perm(mag, hi, 0x04010400u), D);   // (q1, q3)
+    return dot2_bf16(xp[3], __builtin_amdgcn_perm(mag, hi, 0x04030402u), D); // (q5, q7)
+}
+
+// The fp32 activations of a lane chunk's word j (8 values).
+template <typename XT>
+__device__ __forceinline__ void x_f32_word(const uint4 *xw, int j, float *xf)
+{
+    if constexpr (sizeof(XT) == 2) {
+        const uint4 d = xw[j];
+        const uint32_t v[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xf[2 * i] = __uint_as_float(v[i] << 16);
+            xf[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    } else {
+        const uint4 a = xw[2 * j], b = xw[2 * j + 1];
+        xf[0] = __uint_as_float(a.x), xf[1] = __uint_as_float(a.y);
+        xf[2] = __uint_as_float(a.z), xf[3] = __uint_as_float(a.w);
+        xf[4] = __uint_as_float(b.x), xf[5] = __uint_as_float(b.y);
+        xf[6] = __uint_as_float(b.z), xf[7] = __uint_as_float(b.w);
+    }
+}
+
+// LDS image of the staged activations: for activation row m, step t, word j
+// (0..3 of the lane chunk) and lane L, the 4 pairs of that word; then the
+// chunk sums.  Sized MR * steps * (4 * 64 * 16 + 64 * 4) bytes.
+constexpr int kStageBytesPerStep = 4 * 64 * 16 + 64 * 4;
+
+template <int BITS, typename XT, typename ST, int MR, int RW, int STX>
 __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 {
     constexpr bool kMagic = (BITS == 4) && (sizeof(XT) == 2);
+    static_assert(STX == 0 || kMagic, "staged activations hold bf16 pairs for 4-bit codes");
+    // without staging, activations travel with the codes when they are few
+    constexpr int kXW = (STX == 0 && MR <= 2) ? MR * (kLaneChunk * (int)sizeof(XT) / 16) : 0;
+    constexpr int kXWR = kLaneChunk * (int)sizeof(XT) / 16;   // 16-byte pieces per row chunk
+    extern __shared__ uint4 lds_x[];
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int S = p.ksplit;
     const int sl = wave % S;            // K slice of this wave
     const int q = wave / S;             // row group of this wave inside the workgroup
@@ -116,109 +258,120 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
     const ST *sb = p.scales + slab * p.n * p.groups_per_row;
     const ST *bb = p.biases + slab * p.n * p.groups_per_row;
 
+    // Rows past n and lanes past k read row 0 / element 0 of the slab (always
+    // in bounds) and are masked when used.
+    const uint32_t *crow[RW];
+    int64_t srow[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int64_t nr = min(n0 + r, p.n - 1);
+        crow[r] = cb + nr * p.words_per_row;
+        srow[r] = nr * p.groups_per_row;
+    }
+    constexpr uint32_t kMag = 0x43434343u;   // bf16 exponent bytes of 128 + q
+
+    // ---- staged activations: loads first, then (after this wave's first codes
+    // ---- are in flight) pairs and sums into LDS.
+    constexpr int kStageChunks = STX;   // chunks of 32 activations per thread
+    uint4 sx[kStageChunks > 0 ? kStageChunks : 1][4];
+    const int nstage = MR * p.steps * 64;
+    if constexpr (STX > 0) {
+#pragma unroll
+        for (int i = 0; i < kStageChunks; ++i) {
+            const int c = min((int)threadIdx.x + i * (int)blockDim.x, nstage - 1);
+            const int m = c / (p.steps * 64), rem = c % (p.steps * 64);
+            const int64_t e0 = (int64_t)(rem >> 6) * kStepElems + (rem & 63) * kLaneChunk;
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                xb + (int64_t)min(m, mrows - 1) * p.k + (e0 < p.k ? e0 : 0));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sx[i][j] = src[j];
+        }
+    }
+
     float acc[MR][RW];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int r = 0; r < RW; ++r) acc[m][r] = 0.0f;
 
-    auto load_stage = [&](int t, Stage<BITS, RW> &st) {
+    auto load_stage = [&](int t, Stage<BITS, RW, kXW> &st) {
         const int64_t e0 = (int64_t)t * kStepElems + lane * kLaneChunk;
-        const bool on = e0 < p.k;
-        const int64_t g = on ? e0 / p.gs : 0;
+        const bool on = t < p.steps && e0 < p.k;
+        const int64_t ec = on ? e0 : 0;
+        const int64_t g = ec / p.gs;
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            const int64_t nr = n0 + r;
-            if (on && nr < p.n) {
-                load_chunk_words<BITS>(cb + nr * p.words_per_row + e0 * BITS / 32, st.cw[r]);
-                st.s[r] = Elt<ST>::load(sb, nr * p.groups_per_row + g);
-                st.b[r] = Elt<ST>::load(bb, nr * p.groups_per_row + g);
-            } else {
+            st.s[r] = load_raw(sb, srow[r] + g);
+            st.b[r] = load_raw(bb, srow[r] + g);
+        }
+        if constexpr (kXW > 0) {
 #pragma unroll
-                for (int i = 0; i < BITS; ++i) st.cw[r][i] = 0u;
-                st.s[r] = 0.0f;
-                st.b[r] = 0.0f;
+            for (int m = 0; m < MR; ++m) {
+                const uint4 *xs =
+                    reinterpret_cast<const uint4 *>(xb + (int64_t)min(m, mrows - 1) * p.k + ec);
+#pragma unroll
+                for (int i = 0; i < kXWR; ++i) st.xr[m * kXWR + i] = xs[i];
             }
         }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) load_chunk_words<BITS>(crow[r] + ec * BITS / 32, st.cw[r]);
     };
 
-    auto compute_stage = [&](int t, const Stage<BITS, RW> &st) {
+    auto compute_stage = [&](int t, const Stage<BITS, RW, kXW> &st) {
         const int64_t e0 = (int64_t)t * kStepElems + lane * kLaneChunk;
         if (e0 >= p.k) return;
-        const XT *xl = xb + e0;
         float X[MR];
-        float D[MR][RW];
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            X[m] = 0.0f;
-#pragma unroll
-            for (int r = 0; r < RW; ++r) D[m][r] = 0.0f;
-        }
+        float T[MR][RW];   // magic: sum x (128 + q) - 128 X; else sum x q
         if constexpr (kMagic) {
-            constexpr uint32_t kOnes = 0x3f803f80u;   // bf16 pair (1, 1)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {             // word j: elements 8j .. 8j+7
-                uint32_t xp[MR][4];
+            for (int m = 0; m < MR; ++m) {
+                uint32_t xp[16];
+                if constexpr (STX > 0) {
+                    const uint4 *base = lds_x + (int64_t)((m * p.steps + t) * 4) * 64 + lane;
 #pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-                    if (m < mrows) xv = *reinterpret_cast<const uint4 *>(xl + m * p.k + 8 * j);
-                    // pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), matching the code pairs below
-                    xp[m][0] = __builtin_amdgcn_perm(xv.z, xv.x, 0x05040100u);
-                    xp[m][1] = __builtin_amdgcn_perm(xv.z, xv.x, 0x07060302u);
-                    xp[m][2] = __builtin_amdgcn_perm(xv.w, xv.y, 0x05040100u);
-                    xp[m][3] = __builtin_amdgcn_perm(xv.w, xv.y, 0x07060302u);
-                    X[m] = dot2_bf16(xv.x, kOnes, X[m]);
-                    X[m] = dot2_bf16(xv.y, kOnes, X[m]);
-                    X[m] = dot2_bf16(xv.z, kOnes, X[m]);
-                    X[m] = dot2_bf16(xv.w, kOnes, X[m]);
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 v = base[j * 64];
+                        xp[4 * j] = v.x, xp[4 * j + 1] = v.y, xp[4 * j + 2] = v.z, xp[4 * j + 3] = v.w;
+                    }
+                    const float *sums = reinterpret_cast<const float *>(lds_x + MR * p.steps * 256);
+                    X[m] = sums[(m * p.steps + t) * 64 + lane];
+                } else {
+                    X[m] = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        uint4 d;
+                        if constexpr (kXW > 0) d = st.xr[m * kXWR + j];
+                        else d = reinterpret_cast<const uint4 *>(
+                                 xb + (int64_t)min(m, mrows - 1) * p.k + e0)[j];
+                        x_pairs_word(d, xp + 4 * j);
+                        X[m] = x_sum_word(d, X[m]);
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < RW; ++r) {
-                    const uint32_t w = st.cw[r][j];
-                    // bf16 pairs (128 + q_i, 128 + q_{i+4}), i = 0..3
-                    const uint32_t q0 = (w & 0x000f000fu) | 0x43004300u;
-                    const uint32_t q1 = ((w >> 4) & 0x000f000fu) | 0x43004300u;
-                    const uint32_t q2 = ((w >> 8) & 0x000f000fu) | 0x43004300u;
-                    const uint32_t q3 = ((w >> 12) & 0x000f000fu) | 0x43004300u;
+                    float D = 0.0f;
 #pragma unroll
-                    for (int m = 0; m < MR; ++m) {
-                        D[m][r] = dot2_bf16(xp[m][0], q0, D[m][r]);
-                        D[m][r] = dot2_bf16(xp[m][1], q1, D[m][r]);
-                        D[m][r] = dot2_bf16(xp[m][2], q2, D[m][r]);
-                        D[m][r] = dot2_bf16(xp[m][3], q3, D[m][r]);
-                    }
+                    for (int j = 0; j < 4; ++j) D = word_dot_magic(st.cw[r][j], xp + 4 * j, kMag, D);
+                    T[m][r] = fmaf(-128.0f, X[m], D);
                 }
             }
-#pragma unroll
-            for (int m = 0; m < MR; ++m)
-#pragma unroll
-                for (int r = 0; r < RW; ++r) D[m][r] = fmaf(-128.0f, X[m], D[m][r]);
         } else {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                X[m] = 0.0f;
+#pragma unroll
+                for (int r = 0; r < RW; ++r) T[m][r] = 0.0f;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {             // elements 8j .. 8j+7
                 float xf[MR][8];
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
-                    if constexpr (sizeof(XT) == 2) {
-                        uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-                        if (m < mrows) xv = *reinterpret_cast<const uint4 *>(xl + m * p.k + 8 * j);
-                        const uint32_t d[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            xf[m][2 * i] = __uint_as_float(d[i] << 16);
-                            xf[m][2 * i + 1] = __uint_as_float(d[i] & 0xffff0000u);
-                        }
+                    if constexpr (kXW > 0) {
+                        x_f32_word<XT>(st.xr + m * kXWR, j, xf[m]);
                     } else {
-                        uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
-                        if (m < mrows) {
-                            a = *reinterpret_cast<const uint4 *>(xl + m * p.k + 8 * j);
-                            b = *reinterpret_cast<const uint4 *>(xl + m * p.k + 8 * j + 4);
-                        }
-                        xf[m][0] = __uint_as_float(a.x), xf[m][1] = __uint_as_float(a.y);
-                        xf[m][2] = __uint_as_float(a.z), xf[m][3] = __uint_as_float(a.w);
-                        xf[m][4] = __uint_as_float(b.x), xf[m][5] = __uint_as_float(b.y);
-                        xf[m][6] = __uint_as_float(b.z), xf[m][7] = __uint_as_float(b.w);
+                        x_f32_word<XT>(reinterpret_cast<const uint4 *>(
+                                           xb + (int64_t)min(m, mrows - 1) * p.k + e0), j, xf[m]);
                     }
 #pragma unroll
                     for (int i = 0; i < 8; ++i) X[m] += xf[m][i];
@@ -229,62 +382,94 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
                     for (int i = 0; i < 8; ++i) {
                         const float qf = (float)code_at<BITS>(st.cw[r], 8 * j + i);
 #pragma unroll
-                        for (int m = 0; m < MR; ++m) D[m][r] = fmaf(xf[m][i], qf, D[m][r]);
+                        for (int m = 0; m < MR; ++m) T[m][r] = fmaf(xf[m][i], qf, T[m][r]);
                     }
                 }
             }
         }
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
+        for (int r = 0; r < RW; ++r) {
+            const bool rv = n0 + r < p.n;
+            const float sc = rv ? raw_to_f32<ST>(st.s[r]) : 0.0f;
+            const float bi = rv ? raw_to_f32<ST>(st.b[r]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < RW; ++r) {
-                acc[m][r] = fmaf(st.s[r], D[m][r], acc[m][r]);
-                acc[m][r] = fmaf(st.b[r], X[m], acc[m][r]);
+            for (int m = 0; m < MR; ++m) {
+                acc[m][r] = fmaf(sc, T[m][r], acc[m][r]);
+                acc[m][r] = fmaf(bi, X[m], acc[m][r]);
             }
+        }
     };
 
-    if (live) {
-        Stage<BITS, RW> cur, nxt;
-        int t = sl;
-        if (t < p.steps) load_stage(t, cur);
-        for (; t < p.steps; t += S) {
-            if (t + S < p.steps) load_stage(t + S, nxt);
-            compute_stage(t, cur);
-            cur = nxt;
+    // Groups of kGroup steps: every load of a group is issued before the
+    // first of them is used.  Steps past the end read a dummy in-bounds
+    // address and are not computed.
+    constexpr int kGroup = 2;
+    int t0 = sl;
+    // A wave with no step to do (k == 0, where the inputs may be empty and
+    // their pointers null, or a slice past the last step) loads nothing.
+    const bool work = live && t0 < p.steps;
+    Stage<BITS, RW, kXW> st[kGroup];
+    if (work) {
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) load_stage(t0 + u * S, st[u]);
+    }
+    if constexpr (STX > 0) {
+        // pairs and sums of the staged activations (the loads above were issued first)
+        float *sums = reinterpret_cast<float *>(lds_x + MR * p.steps * 256);
+#pragma unroll
+        for (int i = 0; i < kStageChunks; ++i) {
+            const int c = (int)threadIdx.x + i * (int)blockDim.x;
+            if (c < nstage) {
+                const int mt = c >> 6, ln = c & 63;
+                float Xs = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t xp[4];
+                    x_pairs_word(sx[i][j], xp);
+                    Xs = x_sum_word(sx[i][j], Xs);
+                    lds_x[(mt * 4 + j) * 64 + ln] = make_uint4(xp[0], xp[1], xp[2], xp[3]);
+                }
+                sums[mt * 64 + ln] = Xs;
+            }
+        }
+        __syncthreads();
+    }
+    if (work) {
+        for (;;) {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                if (t0 + u * S < p.steps) compute_stage(t0 + u * S, st[u]);
+            t0 += kGroup * S;
+            if (t0 >= p.steps) break;
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) load_stage(t0 + u * S, st[u]);
         }
     }
 
-    // Fixed xor butterfly: every lane ends with the same, order-fixed total.
+    // Fixed-order reduction over the 64 lanes; lane L then holds output
+    // v = L >> kShift, i.e. (m, r) = (v / RW, v % RW).
+    constexpr int V = MR * RW;
+    constexpr int kShift = 6 - ilog2<V>();
+    float vals[V];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            float v = acc[m][r];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-            acc[m][r] = v;
-        }
-
-    // Lane m*RW + r holds output (m, r).
-    float mine = 0.0f;
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-            if (lane == m * RW + r) mine = acc[m][r];
-
-    const int mi = lane / RW, ri = lane % RW;
-    const bool writer = lane < MR * RW && mi < mrows && n0 + ri < p.n;
+        for (int r = 0; r < RW; ++r) vals[m * RW + r] = acc[m][r];
+    const float mine = wave_reduce_transposed<V>(vals, lane);
+    const int vi = lane >> kShift;
+    const bool leader = (lane & ((1 << kShift) - 1)) == 0;
+    const int mi = vi / RW, ri = vi % RW;
+    const bool writer = leader && mi < mrows && n0 + ri < p.n;
     if (S == 1) {
         if (writer) Elt<XT>::store(yb, (int64_t)mi * p.n + n0 + ri, mine);
         return;
     }
-    __shared__ float part[8 * MR * RW];
-    if (lane < MR * RW) part[wave * MR * RW + lane] = mine;
+    __shared__ float part[8 * V];
+    if (leader) part[wave * V + vi] = mine;
     __syncthreads();
     if (sl == 0 && writer) {
-        float tot = part[(q * S) * MR * RW + lane];
-        for (int s2 = 1; s2 < S; ++s2) tot += part[(q * S + s2) * MR * RW + lane];
+        float tot = part[(q * S) * V + vi];
+        for (int s2 = 1; s2 < S; ++s2) tot += part[(q * S + s2) * V + vi];
         Elt<XT>::store(yb, (int64_t)mi * p.n + n0 + ri, tot);
     }
 }
@@ -292,12 +477,11 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 namespace {
 
 constexpr int kMaxGridY = 65535;
+constexpr int kMaxStageBytes = 64 * 1024;
 
-template <int BITS, typename XT, typename ST, int MR>
-hipError_t gemv_mr(const GemvLaunch &a, hipStream_t stream)
+template <int BITS, typename XT, typename ST, int MR, int RW, int STX>
+hipError_t gemv_run(const GemvLaunch &a, hipStream_t stream)
 {
-    constexpr int RW = 4;
-    if (a.rows_per_wave != RW) return hipErrorInvalidValue;
     GemvParams<XT, ST> p;
     p.x = static_cast<const XT *>(a.x);
     p.y = static_cast<XT *>(a.y);
@@ -317,18 +501,40 @@ hipError_t gemv_mr(const GemvLaunch &a, hipStream_t stream)
     p.chunks_per_item = (int)((a.rows_per_item + MR - 1) / MR);
     p.qrows = a.ksplit >= 4 ? 1 : 4 / a.ksplit;
     const int threads = 64 * a.ksplit * p.qrows;
+    const size_t lds = STX > 0 ? (size_t)MR * p.steps * kStageBytesPerStep : 0;
     const int64_t rows_per_block = (int64_t)p.qrows * RW;
     const unsigned gx = (unsigned)((a.n + rows_per_block - 1) / rows_per_block);
     const int64_t items_per_launch = std::max<int64_t>(1, kMaxGridY / p.chunks_per_item);
     for (int64_t i0 = 0; i0 < a.items; i0 += items_per_launch) {
         const int64_t cnt = std::min(items_per_launch, a.items - i0);
         p.item0 = i0;
-        gemv_kernel<BITS, XT, ST, MR, RW>
-            <<<dim3(gx, (unsigned)(cnt * p.chunks_per_item)), dim3(threads), 0, stream>>>(p);
+        gemv_kernel<BITS, XT, ST, MR, RW, STX>
+            <<<dim3(gx, (unsigned)(cnt * p.chunks_per_item)), dim3(threads), lds, stream>>>(p);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
+}
+
+// Rows per wave: 2 for one or two activation rows (more waves, shorter
+// per-wave work), else 4 (more reuse of the activations).  It does not
+// change any row's arithmetic.
+template <int BITS, typename XT, typename ST, int MR>
+hipError_t gemv_mr(const GemvLaunch &a, hipStream_t stream)
+{
+    constexpr int RW = MR <= 2 ? 2 : 4;
+    if (a.rows_per_wave != 0 && a.rows_per_wave != RW) return hipErrorInvalidValue;
+    if constexpr (BITS == 4 && sizeof(XT) == 2 && MR <= 2) {
+        const int steps = (int)((a.k + kStepElems - 1) / kStepElems);
+        const int threads = 64 * a.ksplit * (a.ksplit >= 4 ? 1 : 4 / a.ksplit);
+        const int chunks = MR * steps * 64;
+        if (steps > 0 && (size_t)MR * steps * kStageBytesPerStep <= kMaxStageBytes) {
+            if (chunks <= threads) return gemv_run<BITS, XT, ST, MR, RW, 1>(a, stream);
+            if (chunks <= 2 * threads) return gemv_run<BITS, XT, ST, MR, RW, 2>(a, stream);
+            if (chunks <= 4 * threads) return gemv_run<BITS, XT, ST, MR, RW, 4>(a, stream);
+        }
+    }
+    return gemv_run<BITS, XT, ST, MR, RW, 0>(a, stream);
 }
 
 template <int BITS, typename XT, typename ST>

@@ -114,7 +114,7 @@ nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int
     } else {
         plan->route = NQ_ROUTE_GEMV;
         plan->ksplit = gemv_ksplit(n, k);
-        plan->rows_per_wave = 4;
+        plan->rows_per_wave = 0;   // chosen per launch chunk; no effect on a row's bits
     }
     return NQ_OK;
 }
@@ -125,8 +125,8 @@ nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits)
     if (plan->route == NQ_ROUTE_GEMV) {
         if (plan->ksplit < 1 || plan->ksplit > 8)
             return fail(NQ_ERR_PLAN, "%s: ksplit=%d is not in [1, 8]", op, plan->ksplit);
-        if (plan->rows_per_wave != 4)
-            return fail(NQ_ERR_PLAN, "%s: rows_per_wave=%d is not supported (4)", op,
+        if (plan->rows_per_wave != 0 && plan->rows_per_wave != 2 && plan->rows_per_wave != 4)
+            return fail(NQ_ERR_PLAN, "%s: rows_per_wave=%d is not supported (0, 2 or 4)", op,
                         plan->rows_per_wave);
         return NQ_OK;
     }
@@ -431,7 +431,7 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
     g.gs = group_size;
     g.bits = bits;
     g.ksplit = gemv_ksplit(n, k);   // the plan nq_qmm_row_exact takes
-    g.rows_per_wave = 4;
+    g.rows_per_wave = 0;
     return check_launch(op, nqk::launch_gemv(g, stream));
 }
 

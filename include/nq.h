@@ -116,7 +116,8 @@ typedef enum { NQ_ROUTE_GEMV = 1, NQ_ROUTE_TILED = 2 } nq_route;
 typedef struct {
     int32_t route;          /* nq_route */
     int32_t ksplit;         /* GEMV: K slices per output row, 1..8 (1 = no split) */
-    int32_t rows_per_wave;  /* GEMV: output rows per 64-lane wavefront */
+    int32_t rows_per_wave;  /* GEMV: weight rows per 64-lane wavefront: 2 or 4, 0 = chosen
+                               per launch chunk (it never changes a row's bits) */
     int32_t tile_m;         /* TILED: rows of x per workgroup tile */
     int32_t tile_n;         /* TILED: weight rows per workgroup tile */
     int32_t reserved[3];    /* zero */
@@ -127,8 +128,8 @@ typedef struct {
  * m <= 8 takes the GEMV family and m > 8 the tiled family (x in bf16; fp32 x
  * stays on the GEMV family, which keeps fp32 activations).  With
  * row_exact = 1 every m takes the GEMV family in chunks of at most 8 rows.
- * The GEMV family's ksplit and rows_per_wave depend only on (n, k,
- * group_size, bits, dtypes), never on m, which is what makes its rows
+ * The GEMV family's ksplit depends only on (n, k), never on m, which is
+ * (with the fixed per-row arithmetic of that family) what makes its rows
  * independent of how many rows share a call. */
 nq_status nq_qmm_plan(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits,
                       nq_dtype x_dt, nq_dtype sb_dt, int32_t row_exact, nq_plan *plan);

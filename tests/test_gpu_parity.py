@@ -106,7 +106,7 @@ def test_splitk_parity(ksplit, x_dtype):
     n, k, m, gs, bits = 37, 2048 * 7 + 64, 4, 64, 4     # 8 K steps, the last one ragged
     w, x, c, s, b = quantized_case(ksplit, n, k, gs, bits, "bf16", m, x_dtype, 0.02)
     plan = B.Plan()
-    plan.route, plan.ksplit, plan.rows_per_wave = B.NQ_ROUTE_GEMV, ksplit, 4
+    plan.route, plan.ksplit, plan.rows_per_wave = B.NQ_ROUTE_GEMV, ksplit, 0
     xs = dev(x)
     q = gpu_quantized(c, s, b)
     y = B.nq_qmm_with_plan(plan, xs, *q, gs, bits)
