@@ -109,8 +109,10 @@ nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int
     (void)gs;
     if (tiled) {
         plan->route = NQ_ROUTE_TILED;
-        plan->tile_m = 128;
-        plan->tile_n = 128;
+        // 256 x 256 tiles when the product is large enough to fill them
+        const bool big = m >= 128 && n >= 256 && nqk::tiled_fits(256, 256, bits, m, n, k);
+        plan->tile_m = big ? 256 : 128;
+        plan->tile_n = big ? 256 : 128;
     } else {
         plan->route = NQ_ROUTE_GEMV;
         plan->ksplit = gemv_ksplit(n, k);
@@ -119,7 +121,8 @@ nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int
     return NQ_OK;
 }
 
-nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits)
+nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits, int64_t m, int64_t n,
+                     int64_t k)
 {
     if (!plan) return fail(NQ_ERR_NULL, "%s: plan is null", op);
     if (plan->route == NQ_ROUTE_GEMV) {
@@ -135,6 +138,9 @@ nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits)
         if (!nqk::tiled_supported(plan->tile_m, plan->tile_n, bits))
             return fail(NQ_ERR_PLAN, "%s: tile %dx%d is not supported", op, plan->tile_m,
                         plan->tile_n);
+        if (!nqk::tiled_fits(plan->tile_m, plan->tile_n, bits, m, n, k))
+            return fail(NQ_ERR_PLAN, "%s: tile %dx%d does not fit m=%lld n=%lld k=%lld", op,
+                        plan->tile_m, plan->tile_n, (long long)m, (long long)n, (long long)k);
         return NQ_OK;
     }
     return fail(NQ_ERR_PLAN, "%s: unknown route %d", op, plan->route);
@@ -237,7 +243,7 @@ nq_status qmm_common(const char *op, int row_exact, const nq_plan *forced, const
     if (st || empty) return st;
     nq_plan plan;
     if (forced) {
-        if ((st = check_plan(op, forced, a.x_dt, a.bits))) return st;
+        if ((st = check_plan(op, forced, a.x_dt, a.bits, a.m, a.n, a.k))) return st;
         plan = *forced;
     } else {
         make_plan(op, a.m, a.n, a.k, a.gs, a.bits, a.x_dt, a.sb_dt, row_exact, &plan);

@@ -10,6 +10,8 @@
 // x tile in LDS, dequantizes the weight tile into LDS as bf16 -- the value of
 // the stand-alone dequantize, round_bf16(fmaf(scale, code, bias)) -- and
 // runs v_mfma_f32_32x32x16_bf16 over it.  Four waves split the tile 2 x 2.
+#include <type_traits>
+
 #include "nq_device.h"
 #include "nq_internal.h"
 
@@ -128,9 +130,255 @@ __global__ void __launch_bounds__(256) tiled_kernel(TiledParams<ST> p)
         }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles for large products (K a multiple of 64).
+//
+// Four waves; wave w owns weight rows [64 w, 64 w + 64) of the tile (two
+// 32-column MFMA blocks) and all 256 rows of x (eight 32-row blocks):
+// 16 v_mfma_f32_32x32x16_bf16 accumulators.  Per K block of 64:
+//   - x (256 x 64 bf16 = 32 KB) goes straight from global memory into an LDS
+//     buffer (global_load_lds_dwordx4), double buffered.  In LDS a row is 8
+//     16-byte chunks; chunk c of row r sits at position c ^ (r % 8), which
+//     spreads the MFMA operand reads over the banks.
+//   - each wave dequantizes only its own 64 weight rows, straight into
+//     B-operand registers: lane (n = l % 32, h = l / 32) holds, for k16 step
+//     j, the 8 codes k = 32 h + 8 j + 0..7 of weight row n, i.e. one 4-bit
+//     code word (two 8-bit ones), converted as round_bf16(fmaf(s, q, b)) --
+//     the value of the stand-alone dequantize.  The A operand uses the same
+//     k assignment: x[m][32 h + 8 j + 0..7].
+//   - codes, scales and biases are prefetched two K blocks ahead, x one.
+// Tile order is XCD-aware: workgroups go to the 8 XCDs round-robin, and XCD
+// x takes the x-th eighth of the row-major tile list, so the tiles one XCD
+// runs at a time share their rows of x in that XCD's L2.
+
+constexpr int kBM = 256, kBN = 256, kBK2 = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t u4_at(const uint4 &v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;   // i is a constant after unrolling
+}
+
+template <int BITS>
+struct CodeRegs {
+    uint4 w[BITS / 4];      // the lane's 32 codes of the K block
+    uint32_t s, b;          // raw scale / bias storage bits
+};
+
+// Per-lane offsets into codes (words) and scales/biases (elements) of one
+// weight row for K block 0; block k0 adds k0 * BITS / 32 and k0 / gs, which
+// are uniform.  Offsets are 32-bit: the launcher only takes this kernel
+// when every array it indexes has fewer than 2^31 elements.
+struct RowOffsets {
+    uint32_t code, group;
+};
+
+template <int BITS, typename ST>
+__device__ __forceinline__ void load_codes(const TiledParams<ST> &p, RowOffsets o, int64_t k0,
+                                           CodeRegs<BITS> &c)
+{
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.codes + k0 * BITS / 32 + o.code);
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) c.w[i] = src[i];
+    const ST *sp = p.scales + k0 / p.gs;
+    const ST *bp = p.biases + k0 / p.gs;
+    if constexpr (sizeof(ST) == 2) {
+        c.s = sp[o.group];
+        c.b = bp[o.group];
+    } else {
+        c.s = __float_as_uint(sp[o.group]);
+        c.b = __float_as_uint(bp[o.group]);
+    }
+}
+
+// Codes of k16 step j (8 of the lane's 32) -> one B operand of 8 bf16.
+template <int BITS, typename ST>
+__device__ __forceinline__ bf16x8_t dequant_step(const CodeRegs<BITS> &c, int j)
+{
+    const float s = sizeof(ST) == 2 ? __uint_as_float(c.s << 16) : __uint_as_float(c.s);
+    const float b = sizeof(ST) == 2 ? __uint_as_float(c.b << 16) : __uint_as_float(c.b);
+    float v[8];
+    if constexpr (BITS == 4) {
+        const uint32_t w = u4_at(c.w[0], j);
+        const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+        v[0] = (float)(lo & 0xffu), v[1] = (float)(hi & 0xffu);
+        v[2] = (float)((lo >> 8) & 0xffu), v[3] = (float)((hi >> 8) & 0xffu);
+        v[4] = (float)((lo >> 16) & 0xffu), v[5] = (float)((hi >> 16) & 0xffu);
+        v[6] = (float)(lo >> 24), v[7] = (float)(hi >> 24);
+    } else {
+        const uint32_t w0 = u4_at(c.w[j / 2], 2 * (j % 2));
+        const uint32_t w1 = u4_at(c.w[j / 2], 2 * (j % 2) + 1);
+        v[0] = (float)(w0 & 0xffu), v[1] = (float)((w0 >> 8) & 0xffu);
+        v[2] = (float)((w0 >> 16) & 0xffu), v[3] = (float)(w0 >> 24);
+        v[4] = (float)(w1 & 0xffu), v[5] = (float)((w1 >> 8) & 0xffu);
+        v[6] = (float)((w1 >> 16) & 0xffu), v[7] = (float)(w1 >> 24);
+    }
+    uint4 o;
+    o.x = pack_bf16(fmaf(s, v[0], b), fmaf(s, v[1], b));
+    o.y = pack_bf16(fmaf(s, v[2], b), fmaf(s, v[3], b));
+    o.z = pack_bf16(fmaf(s, v[4], b), fmaf(s, v[5], b));
+    o.w = pack_bf16(fmaf(s, v[6], b), fmaf(s, v[7], b));
+    return __builtin_bit_cast(bf16x8_t, o);
+}
+
+template <int BITS, typename ST>
+__global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int tiles_m, int tiles_n,
+                                                       int per_xcd)
+{
+    extern __shared__ uint4 xs_buf[];   // 2 buffers x 256 rows x 8 chunks
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int xcd = blockIdx.x % 8, j_local = blockIdx.x / 8;
+    const int t = xcd * per_xcd + j_local;
+    if (j_local >= per_xcd || t >= tiles_m * tiles_n) return;
+    const int64_t m0 = (int64_t)(t / tiles_n) * kBM;
+    const int64_t n0 = (int64_t)(t % tiles_n) * kBN;
+    const int nr = lane & 31, h = lane >> 5;
+
+    // this wave's two weight rows per lane (clamped; outputs past n are not stored)
+    RowOffsets ro[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t wr = (uint32_t)min(n0 + wave * 64 + cb * 32 + nr, p.n - 1);
+        ro[cb].code = wr * (uint32_t)p.words_per_row + (uint32_t)(32 * h * BITS / 32);
+        ro[cb].group = wr * (uint32_t)p.groups_per_row + (uint32_t)(32 * h / p.gs);
+    }
+    // x loader: instruction i of wave w fills LDS rows 64 w + 8 i .. + 8; lane
+    // l writes position l % 8 of row 64 w + 8 i + l / 8, i.e. chunk
+    // (l % 8) ^ (row % 8) of that row of x
+    uint32_t xoff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = wave * 64 + i * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        xoff[i] = (uint32_t)min(m0 + r, p.m - 1) * (uint32_t)p.k + (uint32_t)(8 * c);
+    }
+    auto load_x = [&](int buf, int64_t k0) {
+        const bf16_bits *xg = p.x + k0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __attribute__((address_space(3))) void *dst =
+                (__attribute__((address_space(3))) void *)(xs_buf + (buf * kBM + wave * 64 + i * 8) * 8);
+            __builtin_amdgcn_global_load_lds(xg + xoff[i], dst, 16, 0, 0);
+        }
+    };
+
+    f32x16_t acc[8][2];   // first written by the first MFMA (zero C operand)
+
+    const int nk = (int)(p.k / kBK2);
+    CodeRegs<BITS> cr[2][2];   // [K block parity][column block]
+    bf16x8_t bop[2][4];        // [column block][k16 step] of the current block
+
+    // prologue: x block 0, codes of blocks 0 and 1, B operands of block 0
+    load_x(0, 0);
+    load_codes<BITS, ST>(p, ro[0], 0, cr[0][0]);
+    load_codes<BITS, ST>(p, ro[1], 0, cr[0][1]);
+    if (nk > 1) {
+        load_codes<BITS, ST>(p, ro[0], kBK2, cr[1][0]);
+        load_codes<BITS, ST>(p, ro[1], kBK2, cr[1][1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bop[0][j] = dequant_step<BITS, ST>(cr[0][0], j);
+        bop[1][j] = dequant_step<BITS, ST>(cr[0][1], j);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // One K block; PAR = kb % 2 selects code registers and LDS buffer at
+    // compile time.  After the MFMAs of k16 step j have read B operand j,
+    // the next block's step j is dequantized into it (rolling, so B needs
+    // one register set).
+    auto block = [&](int kb, auto par, auto first) {
+        constexpr int PAR = decltype(par)::value;
+        constexpr bool FIRST = decltype(first)::value;
+        const f32x16_t zero = {};
+        const bool more = kb + 1 < nk;
+        if (more) load_x(PAR ^ 1, (int64_t)(kb + 1) * kBK2);
+        if (kb + 2 < nk) {
+            load_codes<BITS, ST>(p, ro[0], (int64_t)(kb + 2) * kBK2, cr[PAR][0]);
+            load_codes<BITS, ST>(p, ro[1], (int64_t)(kb + 2) * kBK2, cr[PAR][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * h + j;
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) {
+                const int r = rb * 32 + nr;
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xs_buf[(PAR * kBM + r) * 8 + (c ^ (r & 7))]);
+                const bool init = FIRST && j == 0;
+                acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[0][j], init ? zero : acc[rb][0], 0, 0, 0);
+                acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[1][j], init ? zero : acc[rb][1], 0, 0, 0);
+            }
+            if (more) {
+                bop[0][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j);
+                bop[1][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j);
+            }
+            // keep each step's operand reads, MFMAs and dequant together
+            // (per 32-row block: one LDS read, two MFMAs, a slice of VALU)
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    block(0, std::integral_constant<int, 0>{}, std::true_type{});
+    if (nk > 1) block(1, std::integral_constant<int, 1>{}, std::false_type{});
+    for (int kb = 2; kb < nk; kb += 2) {
+        block(kb, std::integral_constant<int, 0>{}, std::false_type{});
+        if (kb + 1 < nk) block(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    }
+
+    // epilogue: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
+    // of each 32 x 32 block; offsets from the tile corner are 32-bit
+    bf16_bits *yt = p.y + m0 * p.n + n0 + wave * 64;
+    const bool full = m0 + kBM <= p.m && n0 + kBN <= p.n;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const bool col_ok = full || n0 + wave * 64 + cb * 32 + nr < p.n;
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const uint32_t pk = pack_bf16(acc[rb][cb][v], acc[rb][cb][v + 1]);
+                const int rl = rb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const uint32_t off = (uint32_t)rl * (uint32_t)p.n + (uint32_t)(cb * 32 + nr);
+                if (full) {
+                    yt[off] = (bf16_bits)(pk & 0xffffu);
+                    yt[off + (uint32_t)p.n] = (bf16_bits)(pk >> 16);
+                } else if (col_ok) {
+                    if (m0 + rl < p.m) yt[off] = (bf16_bits)(pk & 0xffffu);
+                    if (m0 + rl + 1 < p.m) yt[off + (uint32_t)p.n] = (bf16_bits)(pk >> 16);
+                }
+            }
+    }
+}
+
+bool tiled_fits(int tile_m, int tile_n, int bits, int64_t m, int64_t n, int64_t k)
+{
+    if (!tiled_supported(tile_m, tile_n, bits)) return false;
+    if (tile_m != kBM) return true;
+    return k % kBK2 == 0 && m * k < ((int64_t)1 << 31) && n * (k * bits / 32) < ((int64_t)1 << 31) &&
+           (m + kBM) * n < ((int64_t)1 << 31) && n * (k / 32) < ((int64_t)1 << 31);
+}
+
 bool tiled_supported(int tile_m, int tile_n, int bits)
 {
-    return tile_m == kTM && tile_n == kTN && (bits == 4 || bits == 8);
+    return ((tile_m == kTM && tile_n == kTN) || (tile_m == kBM && tile_n == kBN)) &&
+           (bits == 4 || bits == 8);
 }
 
 namespace {
@@ -149,6 +397,13 @@ hipError_t tiled_run(const TiledLaunch &a, hipStream_t stream)
     p.words_per_row = a.k * BITS / 32;
     p.groups_per_row = a.k / a.gs;
     p.gs = a.gs;
+    if (a.tile_m == kBM) {
+        if (!tiled_fits(kBM, kBN, BITS, a.m, a.n, a.k)) return hipErrorInvalidValue;
+        const int tm = (int)((a.m + kBM - 1) / kBM), tn = (int)((a.n + kBN - 1) / kBN);
+        const int per = (tm * tn + 7) / 8;
+        tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), 2 * kBM * kBK2 * 2, stream>>>(p, tm, tn, per);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((a.n + kTN - 1) / kTN), (unsigned)((a.m + kTM - 1) / kTM));
     tiled_kernel<BITS, ST><<<grid, dim3(256), 0, stream>>>(p);
     return hipGetLastError();

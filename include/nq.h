@@ -110,7 +110,8 @@ nq_status nq_dequantize(const uint32_t *codes, const void *scales, const void *b
  * matrix-vector family for up to 8 rows per launch chunk; its K loop may be
  * cut into `ksplit` slices of whole 32-element lane chunks whose partial sums
  * are combined in a fixed order (split-K).  NQ_ROUTE_TILED is the tiled
- * matrix-core (bf16 MFMA) product for many rows. */
+ * matrix-core (bf16 MFMA) product for many rows, in 128 x 128 tiles or (for
+ * k a multiple of 64) 256 x 256 tiles. */
 typedef enum { NQ_ROUTE_GEMV = 1, NQ_ROUTE_TILED = 2 } nq_route;
 
 typedef struct {

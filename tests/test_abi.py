@@ -91,7 +91,9 @@ def test_plan_is_pure_and_row_independent(lib):
 def test_plan_routes(lib):
     assert plan(lib, 8, 14336, 4096).route == B.NQ_ROUTE_GEMV
     assert plan(lib, 9, 14336, 4096).route == B.NQ_ROUTE_TILED
+    assert plan(lib, 9, 14336, 4096).tile_m == 128
     assert plan(lib, 2048, 14336, 4096).route == B.NQ_ROUTE_TILED
+    assert plan(lib, 2048, 14336, 4096).tile_m == 256
     assert plan(lib, 2048, 14336, 4096, x=F32, sb=F32).route == B.NQ_ROUTE_GEMV
     # long inner dimension with a small output splits K
     assert plan(lib, 4, 1024, 14336).ksplit > 1
@@ -161,6 +163,10 @@ def test_plan_errors(lib):
     st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, F32, 4, 128, FAKE2, FAKE2 + 0x100000,
                               FAKE2 + 0x200000, BF16, 64, 64, 4, FAKE2 + 0x300000, 0, 0, None)
     assert st == NQ_ERR_PLAN and b"bf16" in lib.nq_last_error()
+    p.tile_m, p.tile_n = 256, 256     # k = 96 is not a multiple of 64
+    st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, BF16, 4, 96, FAKE2, FAKE2 + 0x100000,
+                              FAKE2 + 0x200000, BF16, 64, 32, 4, FAKE2 + 0x300000, 0, 0, None)
+    assert st == NQ_ERR_PLAN and b"does not fit" in lib.nq_last_error()
     st = lib.nq_qmm_with_plan(None, FAKE, BF16, 4, 128, FAKE2, 0, 0, BF16, 64, 64, 4, 0, 0, 0,
                               None)
     assert st == NQ_ERR_NULL

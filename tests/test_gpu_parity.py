@@ -137,12 +137,27 @@ def test_tiled_parity(bits, gs, w_dtype, m, n):
     assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (5, 300, 256), (300, 520, 384), (257, 256, 640)])
+def test_tiled256_parity(bits, gs, w_dtype, m, n, k):
+    """The 256 x 256 tile kernel on ragged shapes spanning several tiles."""
+    w, x, c, s, b = quantized_case(m + 3 * n + bits, n, k, gs, bits, w_dtype, m, "bf16", 0.02)
+    plan = B.Plan()
+    plan.route, plan.tile_m, plan.tile_n = B.NQ_ROUTE_TILED, 256, 256
+    y = B.nq_qmm_with_plan(plan, dev(x), *gpu_quantized(c, s, b), gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled256")
+
+
 def test_tiled_is_chosen_for_many_rows():
-    m, n, k, gs, bits = 200, 192, 1024, 64, 4
-    w, x, c, s, b = quantized_case(5, n, k, gs, bits, "bf16", m, "bf16", 0.02)
-    assert B.nq_qmm_plan(m, n, k, gs, bits, torch.bfloat16, torch.bfloat16).route == B.NQ_ROUTE_TILED
-    y = B.nq_qmm(dev(x), *gpu_quantized(c, s, b), gs, bits)
-    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled auto")
+    for m, n, k, tile in [(200, 192, 1024, 128), (300, 600, 1024, 256)]:
+        gs, bits = 64, 4
+        w, x, c, s, b = quantized_case(5, n, k, gs, bits, "bf16", m, "bf16", 0.02)
+        p = B.nq_qmm_plan(m, n, k, gs, bits, torch.bfloat16, torch.bfloat16)
+        assert p.route == B.NQ_ROUTE_TILED and p.tile_m == tile
+        y = B.nq_qmm(dev(x), *gpu_quantized(c, s, b), gs, bits)
+        assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled auto")
 
 
 # ------------------------------------------------------------------ row-exact
