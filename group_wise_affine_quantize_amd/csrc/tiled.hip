@@ -138,8 +138,9 @@ __global__ void __launch_bounds__(256) tiled_kernel(TiledParams<ST> p)
 // 16 v_mfma_f32_32x32x16_bf16 accumulators.  Per K block of 64:
 //   - x (256 x 64 bf16 = 32 KB) goes straight from global memory into an LDS
 //     buffer (global_load_lds_dwordx4), double buffered.  In LDS a row is 8
-//     16-byte chunks; chunk c of row r sits at position c ^ (r % 8), which
-//     spreads the MFMA operand reads over the banks.
+//     16-byte chunks; chunk c of row r sits at position c ^ ((r / 2) % 8), so
+//     the 16 rows one 16-lane pass of a 128-bit operand read touches land in
+//     16 distinct 16-byte bank groups (64 banks).
 //   - each wave dequantizes only its own 64 weight rows, straight into
 //     B-operand registers: lane (n = l % 32, h = l / 32) holds, for k16 step
 //     j, the 8 codes k = 32 h + 8 j + 0..7 of weight row n, i.e. one 4-bit
@@ -253,12 +254,12 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     }
     // x loader: instruction i of wave w fills LDS rows 64 w + 8 i .. + 8; lane
     // l writes position l % 8 of row 64 w + 8 i + l / 8, i.e. chunk
-    // (l % 8) ^ (row % 8) of that row of x
+    // (l % 8) ^ ((row / 2) % 8) of that row of x
     uint32_t xoff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = wave * 64 + i * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         xoff[i] = (uint32_t)min(m0 + r, p.m - 1) * (uint32_t)p.k + (uint32_t)(8 * c);
     }
     auto load_x = [&](int buf, int64_t k0) {
@@ -274,6 +275,8 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     f32x16_t acc[8][2];   // first written by the first MFMA (zero C operand)
 
     const int nk = (int)(p.k / kBK2);
+    // vector-memory loads one load_codes call issues, for both column blocks
+    constexpr int kCodeLoads = 2 * (BITS / 4 + 2);
     CodeRegs<BITS> cr[2][2];   // [K block parity][column block]
     bf16x8_t bop[2][4];        // [column block][k16 step] of the current block
 
@@ -307,32 +310,47 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
             load_codes<BITS, ST>(p, ro[0], (int64_t)(kb + 2) * kBK2, cr[PAR][0]);
             load_codes<BITS, ST>(p, ro[1], (int64_t)(kb + 2) * kBK2, cr[PAR][1]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        // A operands of k16 step j + 1 are read while the MFMAs of step j
+        // run; B operand j is re-filled for the next block right after its
+        // last use.
+        bf16x8_t a[2][8];
+        auto read_a = [&](int j, bf16x8_t *dst) {
             const int c = 4 * h + j;
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
                 const int r = rb * 32 + nr;
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xs_buf[(PAR * kBM + r) * 8 + (c ^ (r & 7))]);
+                dst[rb] = __builtin_bit_cast(bf16x8_t, xs_buf[(PAR * kBM + r) * 8 + (c ^ ((r >> 1) & 7))]);
+            }
+        };
+        read_a(0, a[0]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < 3) read_a(j + 1, a[(j + 1) & 1]);
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) {
                 const bool init = FIRST && j == 0;
-                acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[0][j], init ? zero : acc[rb][0], 0, 0, 0);
-                acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[1][j], init ? zero : acc[rb][1], 0, 0, 0);
+                acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[0][j], init ? zero : acc[rb][0], 0, 0, 0);
+                acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[1][j], init ? zero : acc[rb][1], 0, 0, 0);
             }
             if (more) {
                 bop[0][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j);
                 bop[1][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j);
             }
-            // keep each step's operand reads, MFMAs and dequant together
-            // (per 32-row block: one LDS read, two MFMAs, a slice of VALU)
+            // per 32-row block: two MFMAs, one LDS read for the next step and
+            // a slice of the dequant VALU
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+                if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        // The next block's x (issued first) must be in LDS; the code loads
+        // issued after it may stay in flight.  s_waitcnt: vmcnt in bits 3:0,
+        // expcnt 6:4 and lgkmcnt 11:8 left at their maxima.
+        if (kb + 2 < nk) __builtin_amdgcn_s_waitcnt(0xF70 | kCodeLoads);
+        else __builtin_amdgcn_s_waitcnt(0xF70);
         __syncthreads();
     };
     block(0, std::integral_constant<int, 0>{}, std::true_type{});
