@@ -28,7 +28,7 @@ struct TiledParams {
     const ST *scales;
     const ST *biases;
     int64_t m, n, k, words_per_row, groups_per_row;
-    int gs;
+    int gs, lg_gs;   // group size and its base-2 logarithm
 };
 
 constexpr int kTM = 128, kTN = 128, kBK = 32, kPad = 8, kLd = kBK + kPad;
@@ -183,20 +183,20 @@ struct RowOffsets {
 };
 
 template <int BITS, typename ST>
-__device__ __forceinline__ void load_codes(const TiledParams<ST> &p, RowOffsets o, int64_t k0,
+__device__ __forceinline__ void load_codes(const TiledParams<ST> &p, RowOffsets o, int kb,
                                            CodeRegs<BITS> &c)
 {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.codes + k0 * BITS / 32 + o.code);
+    // K block kb starts at word kb * 64 * BITS / 32 and group (kb * 64) / gs
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.codes + (uint32_t)(kb * 2 * BITS) + o.code);
 #pragma unroll
     for (int i = 0; i < BITS / 4; ++i) c.w[i] = src[i];
-    const ST *sp = p.scales + k0 / p.gs;
-    const ST *bp = p.biases + k0 / p.gs;
+    const uint32_t g = (uint32_t)(kb * kBK2) >> p.lg_gs;
     if constexpr (sizeof(ST) == 2) {
-        c.s = sp[o.group];
-        c.b = bp[o.group];
+        c.s = p.scales[g + o.group];
+        c.b = p.biases[g + o.group];
     } else {
-        c.s = __float_as_uint(sp[o.group]);
-        c.b = __float_as_uint(bp[o.group]);
+        c.s = __float_as_uint(p.scales[g + o.group]);
+        c.b = __float_as_uint(p.biases[g + o.group]);
     }
 }
 
@@ -209,7 +209,12 @@ __device__ __forceinline__ bf16x8_t dequant_step(const CodeRegs<BITS> &c, int j)
     float v[8];
     if constexpr (BITS == 4) {
         const uint32_t w = u4_at(c.w[0], j);
-        const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+        // lo holds codes 0, 2, 4, 6 and hi codes 1, 3, 5, 7 in its four bytes;
+        // the masks are kept opaque so that each code is one
+        // v_cvt_f32_ubyte{0..3} instead of a bit-field extract plus a convert
+        uint32_t lo, hi;
+        asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+        asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
         v[0] = (float)(lo & 0xffu), v[1] = (float)(hi & 0xffu);
         v[2] = (float)((lo >> 8) & 0xffu), v[3] = (float)((hi >> 8) & 0xffu);
         v[4] = (float)((lo >> 16) & 0xffu), v[5] = (float)((hi >> 16) & 0xffu);
@@ -262,8 +267,8 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         xoff[i] = (uint32_t)min(m0 + r, p.m - 1) * (uint32_t)p.k + (uint32_t)(8 * c);
     }
-    auto load_x = [&](int buf, int64_t k0) {
-        const bf16_bits *xg = p.x + k0;
+    auto load_x = [&](int buf, int kb) {
+        const bf16_bits *xg = p.x + (uint32_t)(kb * kBK2);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             __attribute__((address_space(3))) void *dst =
@@ -284,10 +289,8 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     load_x(0, 0);
     load_codes<BITS, ST>(p, ro[0], 0, cr[0][0]);
     load_codes<BITS, ST>(p, ro[1], 0, cr[0][1]);
-    if (nk > 1) {
-        load_codes<BITS, ST>(p, ro[0], kBK2, cr[1][0]);
-        load_codes<BITS, ST>(p, ro[1], kBK2, cr[1][1]);
-    }
+    load_codes<BITS, ST>(p, ro[0], min(1, nk - 1), cr[1][0]);
+    load_codes<BITS, ST>(p, ro[1], min(1, nk - 1), cr[1][1]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         bop[0][j] = dequant_step<BITS, ST>(cr[0][0], j);
@@ -297,22 +300,19 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     __syncthreads();
 
     // One K block; PAR = kb % 2 selects code registers and LDS buffer at
-    // compile time.  After the MFMAs of k16 step j have read B operand j,
-    // the next block's step j is dequantized into it (rolling, so B needs
-    // one register set).
+    // compile time.  The body has no branches: prefetches past the last
+    // block re-read the last block (into buffers nothing reads any more),
+    // and the B operands dequantized during the last block go unused.
     auto block = [&](int kb, auto par, auto first) {
         constexpr int PAR = decltype(par)::value;
         constexpr bool FIRST = decltype(first)::value;
         const f32x16_t zero = {};
-        const bool more = kb + 1 < nk;
-        if (more) load_x(PAR ^ 1, (int64_t)(kb + 1) * kBK2);
-        if (kb + 2 < nk) {
-            load_codes<BITS, ST>(p, ro[0], (int64_t)(kb + 2) * kBK2, cr[PAR][0]);
-            load_codes<BITS, ST>(p, ro[1], (int64_t)(kb + 2) * kBK2, cr[PAR][1]);
-        }
+        load_x(PAR ^ 1, min(kb + 1, nk - 1));
+        load_codes<BITS, ST>(p, ro[0], min(kb + 2, nk - 1), cr[PAR][0]);
+        load_codes<BITS, ST>(p, ro[1], min(kb + 2, nk - 1), cr[PAR][1]);
         // A operands of k16 step j + 1 are read while the MFMAs of step j
-        // run; B operand j is re-filled for the next block right after its
-        // last use.
+        // run; after step j's MFMAs have read B operand j, the next block's
+        // step j is dequantized into it (rolling, so B needs one register set)
         bf16x8_t a[2][8];
         auto read_a = [&](int j, bf16x8_t *dst) {
             const int c = 4 * h + j;
@@ -332,10 +332,8 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
                 acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[0][j], init ? zero : acc[rb][0], 0, 0, 0);
                 acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[1][j], init ? zero : acc[rb][1], 0, 0, 0);
             }
-            if (more) {
-                bop[0][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j);
-                bop[1][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j);
-            }
+            bop[0][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j);
+            bop[1][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j);
             // per 32-row block: two MFMAs, one LDS read for the next step and
             // a slice of the dequant VALU
 #pragma unroll
@@ -349,16 +347,16 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         // The next block's x (issued first) must be in LDS; the code loads
         // issued after it may stay in flight.  s_waitcnt: vmcnt in bits 3:0,
         // expcnt 6:4 and lgkmcnt 11:8 left at their maxima.
-        if (kb + 2 < nk) __builtin_amdgcn_s_waitcnt(0xF70 | kCodeLoads);
-        else __builtin_amdgcn_s_waitcnt(0xF70);
+        __builtin_amdgcn_s_waitcnt(0xF70 | kCodeLoads);
         __syncthreads();
     };
     block(0, std::integral_constant<int, 0>{}, std::true_type{});
-    if (nk > 1) block(1, std::integral_constant<int, 1>{}, std::false_type{});
-    for (int kb = 2; kb < nk; kb += 2) {
-        block(kb, std::integral_constant<int, 0>{}, std::false_type{});
-        if (kb + 1 < nk) block(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    int kb = 1;
+    for (; kb + 1 < nk; kb += 2) {
+        block(kb, std::integral_constant<int, 1>{}, std::false_type{});
+        block(kb + 1, std::integral_constant<int, 0>{}, std::false_type{});
     }
+    if (kb < nk) block(kb, std::integral_constant<int, 1>{}, std::false_type{});
 
     // epilogue: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
     // of each 32 x 32 block; offsets from the tile corner are 32-bit
@@ -415,6 +413,7 @@ hipError_t tiled_run(const TiledLaunch &a, hipStream_t stream)
     p.words_per_row = a.k * BITS / 32;
     p.groups_per_row = a.k / a.gs;
     p.gs = a.gs;
+    p.lg_gs = a.gs == 32 ? 5 : a.gs == 64 ? 6 : 7;
     if (a.tile_m == kBM) {
         if (!tiled_fits(kBM, kBN, BITS, a.m, a.n, a.k)) return hipErrorInvalidValue;
         const int tm = (int)((a.m + kBM - 1) / kBM), tn = (int)((a.n + kBN - 1) / kBN);
