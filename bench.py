@@ -130,6 +130,15 @@ class Timer:
         return e0.elapsed_time(e1) / 1e3   # seconds
 
 
+def prefill_only(args, B, synthetic, dev, q2, timer, log):
+    """--only prefill: time the prefill product alone (for profiling)."""
+    import torch
+    x4 = dev(synthetic.generate("prefill")["x"])
+    y4 = torch.empty((2048, 14336), dtype=torch.bfloat16, device="cuda")
+    t = timer.run(lambda i: B.nq_qmm(x4, *q2, 64, 4, y=y4), args.prefill_steps, 3, chunk=10)
+    log(f"prefill: {args.prefill_steps} launches, {t / args.prefill_steps * 1e6:.1f} us each")
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -200,6 +209,8 @@ def main():
         log(f"copy: {args.steps} x {src.numel()} bytes, {t / args.steps * 1e6:.3f} us each")
         return
 
+    if args.only == "prefill":
+        return prefill_only(args, B, synthetic, dev, q2, timer, log)
     log("timing decode")
     t_dec = timer.run(decode, args.steps, args.warmup)
     # the graph replays must reproduce the eager result bit for bit
@@ -221,7 +232,7 @@ def main():
     traffic = measured_traffic("decode_gemv")
     out["roofline"] = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                       "traffic": traffic, "kernel": "gemv_kernel<4,bf16,bf16,1,4>",
+                       "traffic": traffic, "kernel": "gemv_kernel<4,bf16,bf16,1,2,1>",
                        "launch_us": round(dec_launch_s * 1e6, 3)}
     del copies2
 
@@ -235,10 +246,6 @@ def main():
     def prefill(i):
         B.nq_qmm(x4, *q2, 64, 4, y=y4)
 
-    if args.only == "prefill":
-        t = timer.run(prefill, args.prefill_steps, 3, chunk=10)
-        log(f"prefill: {args.prefill_steps} launches, {t / args.prefill_steps * 1e6:.1f} us each")
-        return
     log("timing prefill")
     t_pre = timer.run(prefill, args.prefill_steps, 3, chunk=10)
     pre_launch_s = t_pre / args.prefill_steps
@@ -251,7 +258,7 @@ def main():
                    "flops_per_step": flops, "plan": plan4},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill"), "kernel": "tiled_kernel<4,bf16>"},
+                     "traffic": measured_traffic("prefill"), "kernel": "tiled256_kernel<4,bf16>"},
     }
 
     # ---------------------------------------------------------------- other rows
