@@ -105,12 +105,10 @@ nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int
     const bool tiled = !row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 &&
                        nqk::tiled_supported(128, 128, bits);
     (void)op;
-    (void)sb_dt;
-    (void)gs;
     if (tiled) {
         plan->route = NQ_ROUTE_TILED;
         // 256 x 256 tiles when the product is large enough to fill them
-        const bool big = m >= 128 && n >= 256 && nqk::tiled_fits(256, 256, bits, m, n, k);
+        const bool big = m >= 128 && n >= 256 && nqk::tiled_fits(256, 256, bits, gs, sb_dt, m, n, k);
         plan->tile_m = big ? 256 : 128;
         plan->tile_n = big ? 256 : 128;
     } else {
@@ -121,8 +119,8 @@ nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int
     return NQ_OK;
 }
 
-nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits, int64_t m, int64_t n,
-                     int64_t k)
+nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int sb_dt, int gs, int bits,
+                     int64_t m, int64_t n, int64_t k)
 {
     if (!plan) return fail(NQ_ERR_NULL, "%s: plan is null", op);
     if (plan->route == NQ_ROUTE_GEMV) {
@@ -138,7 +136,7 @@ nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int bits, in
         if (!nqk::tiled_supported(plan->tile_m, plan->tile_n, bits))
             return fail(NQ_ERR_PLAN, "%s: tile %dx%d is not supported", op, plan->tile_m,
                         plan->tile_n);
-        if (!nqk::tiled_fits(plan->tile_m, plan->tile_n, bits, m, n, k))
+        if (!nqk::tiled_fits(plan->tile_m, plan->tile_n, bits, gs, sb_dt, m, n, k))
             return fail(NQ_ERR_PLAN, "%s: tile %dx%d does not fit m=%lld n=%lld k=%lld", op,
                         plan->tile_m, plan->tile_n, (long long)m, (long long)n, (long long)k);
         return NQ_OK;
@@ -243,7 +241,7 @@ nq_status qmm_common(const char *op, int row_exact, const nq_plan *forced, const
     if (st || empty) return st;
     nq_plan plan;
     if (forced) {
-        if ((st = check_plan(op, forced, a.x_dt, a.bits, a.m, a.n, a.k))) return st;
+        if ((st = check_plan(op, forced, a.x_dt, a.sb_dt, a.gs, a.bits, a.m, a.n, a.k))) return st;
         plan = *forced;
     } else {
         make_plan(op, a.m, a.n, a.k, a.gs, a.bits, a.x_dt, a.sb_dt, row_exact, &plan);

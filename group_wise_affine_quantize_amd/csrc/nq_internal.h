@@ -57,7 +57,8 @@ struct TiledLaunch {
 hipError_t launch_tiled(const TiledLaunch &a, hipStream_t stream);
 bool tiled_supported(int tile_m, int tile_n, int bits);
 // Whether a tile shape fits these sizes (the 256 x 256 kernel takes K in
-// multiples of 64 and uses 32-bit offsets).
-bool tiled_fits(int tile_m, int tile_n, int bits, int64_t m, int64_t n, int64_t k);
+// multiples of 64, rows of scales and biases that start on 4-byte boundaries,
+// and uses 32-bit offsets).
+bool tiled_fits(int tile_m, int tile_n, int bits, int gs, int sb_dt, int64_t m, int64_t n, int64_t k);
 
 }  // namespace nqk

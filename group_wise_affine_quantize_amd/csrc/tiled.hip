@@ -147,15 +147,39 @@ __global__ void __launch_bounds__(256) tiled_kernel(TiledParams<ST> p)
 //     code word (two 8-bit ones), converted as round_bf16(fmaf(s, q, b)) --
 //     the value of the stand-alone dequantize.  The A operand uses the same
 //     k assignment: x[m][32 h + 8 j + 0..7].
-//   - codes, scales and biases are prefetched two K blocks ahead, x one.
+//   - codes, scales and biases reach the B-operand lanes through wave-private
+//     LDS rings (two stages each; a codes stage is 128 bytes of each of the
+//     wave's rows, 4 K blocks at 4 bits and 2 at 8 bits, swizzled like x; a
+//     scale/bias stage is 8 groups of each row).  The rings are filled by
+//     ordinary loads whose every instruction covers whole 128-byte row
+//     segments (the B-operand layout would touch 32 rows per instruction and
+//     use 16 or 2 bytes of each), kept in registers for two blocks to hide
+//     their latency, then written with ds_write.
+//   - B operands of the next block are dequantized during the MFMAs of the
+//     current one (rolling, one register set); A operands are read one k16
+//     step ahead, across block boundaries too.
 // Tile order is XCD-aware: workgroups go to the 8 XCDs round-robin, and XCD
 // x takes the x-th eighth of the row-major tile list, so the tiles one XCD
 // runs at a time share their rows of x in that XCD's L2.
 
 constexpr int kBM = 256, kBN = 256, kBK2 = 64;
+// LDS map (bytes): the x ring, then per wave a codes ring and a scale/bias ring
+constexpr int kXBytes = 2 * kBM * kBK2 * 2;          // 64 KB
+constexpr int kCodeRowBytes = 128;                    // per row per stage
+constexpr int kCodeStageBytes = 64 * kCodeRowBytes;   // one wave's 64 rows: 8 KB
+constexpr int kCodeBase = kXBytes;
+constexpr int kSbBase = kCodeBase + 4 * 2 * kCodeStageBytes;
+constexpr int kSbGroups = 8;                          // groups per row per stage
+template <typename ST>
+constexpr int sb_row_bytes() { return kSbGroups * (int)sizeof(ST); }
+template <typename ST>
+constexpr int sb_stage_bytes() { return 2 * 64 * sb_row_bytes<ST>(); }   // scales, then biases
+template <typename ST>
+constexpr int tiled_lds_bytes() { return kSbBase + 4 * 2 * sb_stage_bytes<ST>(); }   // 144 or 160 KB
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
@@ -168,37 +192,12 @@ __device__ __forceinline__ uint32_t u4_at(const uint4 &v, int i)
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;   // i is a constant after unrolling
 }
 
+// A lane's codes of one K block (32 codes) with its scale and bias.
 template <int BITS>
 struct CodeRegs {
-    uint4 w[BITS / 4];      // the lane's 32 codes of the K block
+    uint4 w[BITS / 4];
     uint32_t s, b;          // raw scale / bias storage bits
 };
-
-// Per-lane offsets into codes (words) and scales/biases (elements) of one
-// weight row for K block 0; block k0 adds k0 * BITS / 32 and k0 / gs, which
-// are uniform.  Offsets are 32-bit: the launcher only takes this kernel
-// when every array it indexes has fewer than 2^31 elements.
-struct RowOffsets {
-    uint32_t code, group;
-};
-
-template <int BITS, typename ST>
-__device__ __forceinline__ void load_codes(const TiledParams<ST> &p, RowOffsets o, int kb,
-                                           CodeRegs<BITS> &c)
-{
-    // K block kb starts at word kb * 64 * BITS / 32 and group (kb * 64) / gs
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.codes + (uint32_t)(kb * 2 * BITS) + o.code);
-#pragma unroll
-    for (int i = 0; i < BITS / 4; ++i) c.w[i] = src[i];
-    const uint32_t g = (uint32_t)(kb * kBK2) >> p.lg_gs;
-    if constexpr (sizeof(ST) == 2) {
-        c.s = p.scales[g + o.group];
-        c.b = p.biases[g + o.group];
-    } else {
-        c.s = __float_as_uint(p.scales[g + o.group]);
-        c.b = __float_as_uint(p.biases[g + o.group]);
-    }
-}
 
 // Codes of k16 step j (8 of the lane's 32) -> one B operand of 8 bf16.
 template <int BITS, typename ST>
@@ -239,7 +238,8 @@ template <int BITS, typename ST>
 __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int tiles_m, int tiles_n,
                                                        int per_xcd)
 {
-    extern __shared__ uint4 xs_buf[];   // 2 buffers x 256 rows x 8 chunks
+    extern __shared__ uint4 lds[];
+    char *const lds_bytes = reinterpret_cast<char *>(lds);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int xcd = blockIdx.x % 8, j_local = blockIdx.x / 8;
@@ -248,15 +248,26 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     const int64_t m0 = (int64_t)(t / tiles_n) * kBM;
     const int64_t n0 = (int64_t)(t % tiles_n) * kBN;
     const int nr = lane & 31, h = lane >> 5;
+    const int nk = (int)(p.k / kBK2);
+    const uint32_t wpr = (uint32_t)p.words_per_row, gpr = (uint32_t)p.groups_per_row;
+    const uint32_t wrow0 = (uint32_t)(n0 + wave * 64);   // this wave's first weight row
 
-    // this wave's two weight rows per lane (clamped; outputs past n are not stored)
-    RowOffsets ro[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const uint32_t wr = (uint32_t)min(n0 + wave * 64 + cb * 32 + nr, p.n - 1);
-        ro[cb].code = wr * (uint32_t)p.words_per_row + (uint32_t)(32 * h * BITS / 32);
-        ro[cb].group = wr * (uint32_t)p.groups_per_row + (uint32_t)(32 * h / p.gs);
-    }
+    // Ring geometry.  Codes: kCB K blocks per stage, filled in kCB slices of
+    // 64 / kCB rows (kCodeLd 16-byte loads per lane).  Scales and biases:
+    // 2^lg_sb K blocks per stage (8 groups), filled in 4 slices of 16 rows
+    // (kSbLd 4-byte loads per lane per array).
+    constexpr int kCB = 16 / BITS;
+    constexpr int kCodeLd = BITS / 2;
+    constexpr int kSbRow = sb_row_bytes<ST>();
+    constexpr int kSbLanesPerRow = kSbRow / 4;
+    constexpr int kSbLd = 16 * kSbLanesPerRow / 64;
+    constexpr uint32_t kPerDword = 4 / sizeof(ST);
+    const int lg_sb = p.lg_gs - 3;
+    const int last_code_stage = (nk - 1) / kCB;
+    const int last_sb_stage = (int)((gpr - 1) / kSbGroups);
+    char *const code_ring = lds_bytes + kCodeBase + wave * 2 * kCodeStageBytes;
+    char *const sb_ring = lds_bytes + kSbBase + wave * 2 * sb_stage_bytes<ST>();
+
     // x loader: instruction i of wave w fills LDS rows 64 w + 8 i .. + 8; lane
     // l writes position l % 8 of row 64 w + 8 i + l / 8, i.e. chunk
     // (l % 8) ^ ((row / 2) % 8) of that row of x
@@ -270,85 +281,240 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     auto load_x = [&](int buf, int kb) {
         const bf16_bits *xg = p.x + (uint32_t)(kb * kBK2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __attribute__((address_space(3))) void *dst =
-                (__attribute__((address_space(3))) void *)(xs_buf + (buf * kBM + wave * 64 + i * 8) * 8);
-            __builtin_amdgcn_global_load_lds(xg + xoff[i], dst, 16, 0, 0);
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(xg + xoff[i], (lds_void *)(lds + (buf * kBM + wave * 64 + i * 8) * 8),
+                                             16, 0, 0);
+    };
+
+    // Codes slice q of stage T: load l of a lane covers ring row
+    // r = q * 64 / kCB + 8 l + lane / 8, ring position lane % 8, holding
+    // 16-byte chunk (lane % 8) ^ ((r / 2) % 8) of the row's 128 stage bytes.
+    // Stages past the last re-read the last stage (their ring buffer is not
+    // read again); chunks past a row's end re-read its last chunk.
+    struct CodeSlice { uint4 v[kCodeLd]; };
+    auto code_slice_load = [&](int T, int q) {
+        CodeSlice d;
+        const uint32_t w0 = (uint32_t)min(T, last_code_stage) * (kCodeRowBytes / 4);
+#pragma unroll
+        for (int l = 0; l < kCodeLd; ++l) {
+            const int r = q * (64 / kCB) + 8 * l + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            const uint32_t row = min(wrow0 + (uint32_t)r, (uint32_t)p.n - 1);
+            const uint32_t in_row = min(w0 + (uint32_t)(4 * c), wpr - 4);
+            d.v[l] = *reinterpret_cast<const uint4 *>(p.codes + row * wpr + in_row);
+        }
+        return d;
+    };
+    auto code_slice_store = [&](int T, int q, CodeSlice d) {
+        uint4 *dst = reinterpret_cast<uint4 *>(code_ring + (T & 1) * kCodeStageBytes +
+                                               q * (64 / kCB) * kCodeRowBytes);
+#pragma unroll
+        for (int l = 0; l < kCodeLd; ++l) dst[l * 64 + lane] = d.v[l];
+    };
+
+    // Scale/bias slice q of stage U: 16 rows; load l of a lane covers ring
+    // row 16 q + (64 l + lane) / kSbLanesPerRow, dword lane % kSbLanesPerRow.
+    struct SbSlice { uint32_t s[kSbLd], b[kSbLd]; };
+    auto sb_slice_load = [&](int U, int q) {
+        SbSlice d;
+        const uint32_t g = min((uint32_t)(min(U, last_sb_stage) * kSbGroups) +
+                                   (uint32_t)(lane % kSbLanesPerRow) * kPerDword,
+                               gpr - kPerDword);
+#pragma unroll
+        for (int l = 0; l < kSbLd; ++l) {
+            const int r = 16 * q + (64 * l + lane) / kSbLanesPerRow;
+            const uint32_t off = min(wrow0 + (uint32_t)r, (uint32_t)p.n - 1) * gpr + g;
+            d.s[l] = *reinterpret_cast<const uint32_t *>(p.scales + off);
+            d.b[l] = *reinterpret_cast<const uint32_t *>(p.biases + off);
+        }
+        return d;
+    };
+    auto sb_slice_store = [&](int U, int q, SbSlice d) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(sb_ring + (U & 1) * sb_stage_bytes<ST>() +
+                                                     16 * q * kSbRow);
+#pragma unroll
+        for (int l = 0; l < kSbLd; ++l) {
+            dst[l * 64 + lane] = d.s[l];
+            dst[64 * kSbRow / 4 + l * 64 + lane] = d.b[l];
+        }
+    };
+    // The slice a block writes: block kb writes codes slice t % kCB of stage
+    // t / kCB + 1 and scale slice min(t % 2^lg_sb, 3) of stage t / 2^lg_sb + 1,
+    // t = kb + 3, and loads (into registers) those of block kb + 2.
+    auto code_slice_of = [&](int tt, int &T, int &q) { T = tt / kCB + 1; q = tt % kCB; };
+    auto sb_slice_of = [&](int tt, int &U, int &q) {
+        U = (tt >> lg_sb) + 1;
+        q = min(tt & ((1 << lg_sb) - 1), 3);
+    };
+
+    // a lane's codes, scale and bias of K block kb, from the rings
+    auto read_codes = [&](int kb, int cb, CodeRegs<BITS> &c) {
+        const int row = cb * 32 + nr;
+        const uint4 *ring = reinterpret_cast<const uint4 *>(
+            code_ring + ((kb / kCB) & 1) * kCodeStageBytes + row * kCodeRowBytes);
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i) {
+            const int chunk = ((kb % kCB) * 2 + h) * (BITS / 4) + i;
+            c.w[i] = ring[chunk ^ ((row >> 1) & 7)];
+        }
+        const int ss = kb >> lg_sb;
+        const int g = ((kb * kBK2 + 32 * h) >> p.lg_gs) - ss * kSbGroups;
+        const ST *sp = reinterpret_cast<const ST *>(
+            sb_ring + (ss & 1) * sb_stage_bytes<ST>() + row * kSbRow);
+        if constexpr (sizeof(ST) == 2) {
+            c.s = sp[g];
+            c.b = sp[g + 64 * kSbRow / 2];
+        } else {
+            c.s = __float_as_uint(sp[g]);
+            c.b = __float_as_uint(sp[g + 64 * kSbRow / 4]);
         }
     };
 
-    f32x16_t acc[8][2];   // first written by the first MFMA (zero C operand)
-
-    const int nk = (int)(p.k / kBK2);
-    // vector-memory loads one load_codes call issues, for both column blocks
-    constexpr int kCodeLoads = 2 * (BITS / 4 + 2);
-    CodeRegs<BITS> cr[2][2];   // [K block parity][column block]
+    f32x16_t acc[8][2];        // first written by the first MFMA (zero C operand)
     bf16x8_t bop[2][4];        // [column block][k16 step] of the current block
+    bf16x8_t a[2][8];          // A operands: [k16 step parity][row block]
+    CodeRegs<BITS> cr[2][2];   // [K block parity][column block]
+    // ring slices in flight, by the parity of the block that writes them
+    CodeSlice csl0, csl1;
+    SbSlice ssl0, ssl1;
 
-    // prologue: x block 0, codes of blocks 0 and 1, B operands of block 0
+    // A operand of row block rb, k16 step j, from x buffer buf, into the
+    // register set of step j's parity
+    auto read_a = [&](int buf, int j, int rb) {
+        const int c = 4 * h + j, r = rb * 32 + nr;
+        a[j & 1][rb] = __builtin_bit_cast(bf16x8_t, lds[(buf * kBM + r) * 8 + (c ^ ((r >> 1) & 7))]);
+    };
+
+    // Prologue: x blocks 0 and 1; ring stage 0, from which the codes of
+    // blocks 0 and 1 are read at once (the rings are private to the wave, so
+    // its own LDS order suffices), before the slices blocks -3..-1 would have
+    // written (at 8 bits one of them overwrites stage 0); the slice block 0
+    // writes (block 0 loads the one block 1 writes); then block 0's B
+    // operands and first A operands.
     load_x(0, 0);
-    load_codes<BITS, ST>(p, ro[0], 0, cr[0][0]);
-    load_codes<BITS, ST>(p, ro[1], 0, cr[0][1]);
-    load_codes<BITS, ST>(p, ro[0], min(1, nk - 1), cr[1][0]);
-    load_codes<BITS, ST>(p, ro[1], min(1, nk - 1), cr[1][1]);
+    load_x(1, min(1, nk - 1));
+#pragma unroll
+    for (int q = 0; q < kCB; ++q) code_slice_store(0, q, code_slice_load(0, q));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sb_slice_store(0, q, sb_slice_load(0, q));
+    read_codes(0, 0, cr[0][0]);
+    read_codes(0, 1, cr[0][1]);
+    read_codes(1, 0, cr[1][0]);
+    read_codes(1, 1, cr[1][1]);
+#pragma unroll
+    for (int tt = 0; tt < 3; ++tt) {
+        int T, q;
+        code_slice_of(tt, T, q);
+        code_slice_store(T, q, code_slice_load(T, q));
+        sb_slice_of(tt, T, q);
+        sb_slice_store(T, q, sb_slice_load(T, q));
+    }
+    {
+        int T, q;
+        code_slice_of(3, T, q);
+        csl0 = code_slice_load(T, q);
+        sb_slice_of(3, T, q);
+        ssl0 = sb_slice_load(T, q);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         bop[0][j] = dequant_step<BITS, ST>(cr[0][0], j);
         bop[1][j] = dequant_step<BITS, ST>(cr[0][1], j);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) read_a(0, 0, rb);
 
-    // One K block; PAR = kb % 2 selects code registers and LDS buffer at
-    // compile time.  The body has no branches: prefetches past the last
-    // block re-read the last block (into buffers nothing reads any more),
-    // and the B operands dequantized during the last block go unused.
+    // One K block (PAR = kb % 2, the x buffer, at compile time).  Step j's
+    // MFMAs run while step j + 1's A operands are read and the next block's
+    // step j is dequantized into B operand j (rolling).  One barrier per
+    // block, before the last step: every wave has then read all of this
+    // block's A operands and waited for its x loads of the next block, so
+    // that x is visible (its first A operands are read under the last step's
+    // MFMAs) and this block's x buffer is free for x two blocks ahead.  A
+    // ring slice is loaded in a block's first step, written after the
+    // barrier one block later into a stage buffer whose previous stage was
+    // last read before that write (in the same step at the latest), and
+    // first read at least one block after the write.  Prefetches past the
+    // last block re-read the last one, into buffers nothing reads any more
+    // (or with the same bytes); the operands prepared during the last block
+    // go unused.
+    constexpr int kRingLoads = kCodeLd + 2 * kSbLd;   // ring loads per block (after x)
     auto block = [&](int kb, auto par, auto first) {
         constexpr int PAR = decltype(par)::value;
         constexpr bool FIRST = decltype(first)::value;
         const f32x16_t zero = {};
-        load_x(PAR ^ 1, min(kb + 1, nk - 1));
-        load_codes<BITS, ST>(p, ro[0], min(kb + 2, nk - 1), cr[PAR][0]);
-        load_codes<BITS, ST>(p, ro[1], min(kb + 2, nk - 1), cr[PAR][1]);
-        // A operands of k16 step j + 1 are read while the MFMAs of step j
-        // run; after step j's MFMAs have read B operand j, the next block's
-        // step j is dequantized into it (rolling, so B needs one register set)
-        bf16x8_t a[2][8];
-        auto read_a = [&](int j, bf16x8_t *dst) {
-            const int c = 4 * h + j;
-#pragma unroll
-            for (int rb = 0; rb < 8; ++rb) {
-                const int r = rb * 32 + nr;
-                dst[rb] = __builtin_bit_cast(bf16x8_t, xs_buf[(PAR * kBM + r) * 8 + (c ^ ((r >> 1) & 7))]);
-            }
-        };
-        read_a(0, a[0]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < 3) read_a(j + 1, a[(j + 1) & 1]);
+        // Step j: the 16 MFMAs, the next step's A operands (into the other
+        // register set), and one step of dequantization into the B operand
+        // the previous step used: step j - 1 of the next block, or at step 0
+        // step 3 of this one (its codes are still in cr[PAR]).  A register
+        // is never rewritten while MFMAs that read it may still be queued:
+        // an LDS return or a VALU write lands at least a whole step after
+        // the MFMAs that read the register were issued.  `issue` adds memory
+        // operations that the scheduler spreads over the step.
+        auto step = [&](int j, int nbuf, int nj, auto issue) {
+            issue();
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
                 const bool init = FIRST && j == 0;
                 acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[0][j], init ? zero : acc[rb][0], 0, 0, 0);
                 acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[1][j], init ? zero : acc[rb][1], 0, 0, 0);
+                read_a(nbuf, nj, rb);
             }
-            bop[0][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j);
-            bop[1][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j);
-            // per 32-row block: two MFMAs, one LDS read for the next step and
-            // a slice of the dequant VALU
-#pragma unroll
-            for (int rb = 0; rb < 8; ++rb) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-                if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+            if (j == 0) {
+                bop[0][3] = dequant_step<BITS, ST>(cr[PAR][0], 3);
+                bop[1][3] = dequant_step<BITS, ST>(cr[PAR][1], 3);
+            } else {
+                bop[0][j - 1] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j - 1);
+                bop[1][j - 1] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j - 1);
             }
+            // (No sched_group_barrier pattern here: forcing MFMA / LDS / VALU
+            // interleaving made some 8-bit instances return corrupted
+            // values from one run to the next, and was slower than the
+            // scheduler's own order.)
             __builtin_amdgcn_sched_barrier(0);
-        }
-        // The next block's x (issued first) must be in LDS; the code loads
-        // issued after it may stay in flight.  s_waitcnt: vmcnt in bits 3:0,
-        // expcnt 6:4 and lgkmcnt 11:8 left at their maxima.
-        __builtin_amdgcn_s_waitcnt(0xF70 | kCodeLoads);
-        __syncthreads();
+        };
+        // step 0 issues the ring loads a block two blocks from now writes
+        // (slice t = kb + 4, into the registers of the other parity)
+        step(0, PAR, 1, [&] {
+            CodeSlice &csl = PAR ? csl0 : csl1;
+            SbSlice &ssl = PAR ? ssl0 : ssl1;
+            int T, q;
+            code_slice_of(kb + 4, T, q);
+            csl = code_slice_load(T, q);
+            sb_slice_of(kb + 4, T, q);
+            ssl = sb_slice_load(T, q);
+        });
+        step(1, PAR, 2, [] {});
+        step(2, PAR, 3, [] {});
+        // Wait for x of the next block (issued in the previous block's last
+        // step; only this block's ring loads were issued after it), then
+        // the barrier.  __syncthreads() would wait for every load; the memory
+        // clobbers keep the compiler from moving memory accesses across.
+        // s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt (11:8) and
+        // expcnt (6:4) zero.
+        __builtin_amdgcn_s_waitcnt(kRingLoads & 15 | (kRingLoads >> 4) << 14);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // Step 3, with the ring reads (codes of block kb + 2, the parity of
+        // this block's, already used), the ring writes of slice t = kb + 3
+        // (loaded two blocks ago), and x two blocks ahead into this block's
+        // buffer -- in that order, so no load into LDS is in flight while
+        // the rings are read or written.
+        step(3, PAR ^ 1, 0, [&] {
+            read_codes(kb + 2, 0, cr[PAR][0]);
+            read_codes(kb + 2, 1, cr[PAR][1]);
+            const CodeSlice &csl = PAR ? csl1 : csl0;
+            const SbSlice &ssl = PAR ? ssl1 : ssl0;
+            int T, q;
+            code_slice_of(kb + 3, T, q);
+            code_slice_store(T, q, csl);
+            sb_slice_of(kb + 3, T, q);
+            sb_slice_store(T, q, ssl);
+            load_x(PAR, min(kb + 2, nk - 1));
+        });
     };
     block(0, std::integral_constant<int, 0>{}, std::true_type{});
     int kb = 1;
@@ -357,6 +523,9 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         block(kb + 1, std::integral_constant<int, 0>{}, std::false_type{});
     }
     if (kb < nk) block(kb, std::integral_constant<int, 1>{}, std::false_type{});
+    // the last block's prefetches must land before the workgroup's LDS is
+    // handed to another workgroup
+    __builtin_amdgcn_s_waitcnt(0);
 
     // epilogue: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
     // of each 32 x 32 block; offsets from the tile corner are 32-bit
@@ -383,12 +552,17 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     }
 }
 
-bool tiled_fits(int tile_m, int tile_n, int bits, int64_t m, int64_t n, int64_t k)
+bool tiled_fits(int tile_m, int tile_n, int bits, int gs, int sb_dt, int64_t m, int64_t n, int64_t k)
 {
     if (!tiled_supported(tile_m, tile_n, bits)) return false;
     if (tile_m != kBM) return true;
-    return k % kBK2 == 0 && m * k < ((int64_t)1 << 31) && n * (k * bits / 32) < ((int64_t)1 << 31) &&
-           (m + kBM) * n < ((int64_t)1 << 31) && n * (k / 32) < ((int64_t)1 << 31);
+    // K in whole 64-blocks; 32-bit offsets; every row of scales and biases
+    // starts on a 4-byte boundary (4-byte direct-to-LDS loads)
+    const int64_t groups = k / gs;
+    const bool sb_aligned = sb_dt == DT_F32 || groups % 2 == 0;
+    return k % kBK2 == 0 && sb_aligned && m * k < ((int64_t)1 << 31) &&
+           n * (k * bits / 32) < ((int64_t)1 << 31) && (m + kBM) * n < ((int64_t)1 << 31) &&
+           n * groups < ((int64_t)1 << 31);
 }
 
 bool tiled_supported(int tile_m, int tile_n, int bits)
@@ -415,10 +589,10 @@ hipError_t tiled_run(const TiledLaunch &a, hipStream_t stream)
     p.gs = a.gs;
     p.lg_gs = a.gs == 32 ? 5 : a.gs == 64 ? 6 : 7;
     if (a.tile_m == kBM) {
-        if (!tiled_fits(kBM, kBN, BITS, a.m, a.n, a.k)) return hipErrorInvalidValue;
+        if (!tiled_fits(kBM, kBN, BITS, a.gs, a.sb_dt, a.m, a.n, a.k)) return hipErrorInvalidValue;
         const int tm = (int)((a.m + kBM - 1) / kBM), tn = (int)((a.n + kBN - 1) / kBN);
         const int per = (tm * tn + 7) / 8;
-        tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), 2 * kBM * kBK2 * 2, stream>>>(p, tm, tn, per);
+        tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), tiled_lds_bytes<ST>(), stream>>>(p, tm, tn, per);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((a.n + kTN - 1) / kTN), (unsigned)((a.m + kTM - 1) / kTM));

@@ -95,6 +95,12 @@ def test_plan_routes(lib):
     assert plan(lib, 2048, 14336, 4096).route == B.NQ_ROUTE_TILED
     assert plan(lib, 2048, 14336, 4096).tile_m == 256
     assert plan(lib, 2048, 14336, 4096, x=F32, sb=F32).route == B.NQ_ROUTE_GEMV
+    # the 256 x 256 kernel loads scale rows as dwords: an odd number of bf16
+    # groups per row (k = 192, group 64) takes 128 x 128 tiles; f32 scales
+    # are always aligned
+    assert plan(lib, 2048, 1024, 192).tile_m == 128
+    assert plan(lib, 2048, 1024, 192, sb=F32).tile_m == 256
+    assert plan(lib, 2048, 1024, 256).tile_m == 256
     # long inner dimension with a small output splits K
     assert plan(lib, 4, 1024, 14336).ksplit > 1
     assert plan(lib, 1, 14336, 4096).ksplit == 1
