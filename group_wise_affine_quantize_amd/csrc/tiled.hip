@@ -163,19 +163,14 @@ __global__ void __launch_bounds__(256) tiled_kernel(TiledParams<ST> p)
 // runs at a time share their rows of x in that XCD's L2.
 
 constexpr int kBM = 256, kBN = 256, kBK2 = 64;
-// LDS map (bytes): the x ring, then per wave a codes ring and a scale/bias ring
-constexpr int kXBytes = 2 * kBM * kBK2 * 2;          // 64 KB
+// Ring geometry in LDS (bytes)
 constexpr int kCodeRowBytes = 128;                    // per row per stage
 constexpr int kCodeStageBytes = 64 * kCodeRowBytes;   // one wave's 64 rows: 8 KB
-constexpr int kCodeBase = kXBytes;
-constexpr int kSbBase = kCodeBase + 4 * 2 * kCodeStageBytes;
 constexpr int kSbGroups = 8;                          // groups per row per stage
 template <typename ST>
 constexpr int sb_row_bytes() { return kSbGroups * (int)sizeof(ST); }
 template <typename ST>
 constexpr int sb_stage_bytes() { return 2 * 64 * sb_row_bytes<ST>(); }   // scales, then biases
-template <typename ST>
-constexpr int tiled_lds_bytes() { return kSbBase + 4 * 2 * sb_stage_bytes<ST>(); }   // 144 or 160 KB
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -238,8 +233,15 @@ template <int BITS, typename ST>
 __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int tiles_m, int tiles_n,
                                                        int per_xcd)
 {
-    extern __shared__ uint4 lds[];
-    char *const lds_bytes = reinterpret_cast<char *>(lds);
+    constexpr int kSbRow = sb_row_bytes<ST>();
+    // Separate LDS arrays (two x buffers, the rings), so that the compiler
+    // sees that what a wave reads never aliases the x buffer that
+    // direct-to-LDS loads are filling, and adds no wait for them.
+    __shared__ uint4 x_lds0[kBM * 8];                                   // 256 rows x 128 B
+    __shared__ uint4 x_lds1[kBM * 8];
+    __shared__ uint4 code_lds[4 * 2 * kCodeStageBytes / 16];            // [wave][stage] 8 KB
+    __shared__ uint32_t sb_lds[4 * 2 * sb_stage_bytes<ST>() / 4];       // [wave][stage][s|b]
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int xcd = blockIdx.x % 8, j_local = blockIdx.x / 8;
@@ -258,15 +260,12 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     // (kSbLd 4-byte loads per lane per array).
     constexpr int kCB = 16 / BITS;
     constexpr int kCodeLd = BITS / 2;
-    constexpr int kSbRow = sb_row_bytes<ST>();
     constexpr int kSbLanesPerRow = kSbRow / 4;
     constexpr int kSbLd = 16 * kSbLanesPerRow / 64;
     constexpr uint32_t kPerDword = 4 / sizeof(ST);
     const int lg_sb = p.lg_gs - 3;
     const int last_code_stage = (nk - 1) / kCB;
     const int last_sb_stage = (int)((gpr - 1) / kSbGroups);
-    char *const code_ring = lds_bytes + kCodeBase + wave * 2 * kCodeStageBytes;
-    char *const sb_ring = lds_bytes + kSbBase + wave * 2 * sb_stage_bytes<ST>();
 
     // x loader: instruction i of wave w fills LDS rows 64 w + 8 i .. + 8; lane
     // l writes position l % 8 of row 64 w + 8 i + l / 8, i.e. chunk
@@ -278,11 +277,12 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         xoff[i] = (uint32_t)min(m0 + r, p.m - 1) * (uint32_t)p.k + (uint32_t)(8 * c);
     }
+    auto x_buf = [&](int buf) { return buf ? x_lds1 : x_lds0; };   // buf is a constant
     auto load_x = [&](int buf, int kb) {
         const bf16_bits *xg = p.x + (uint32_t)(kb * kBK2);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_global_load_lds(xg + xoff[i], (lds_void *)(lds + (buf * kBM + wave * 64 + i * 8) * 8),
+            __builtin_amdgcn_global_load_lds(xg + xoff[i], (lds_void *)(x_buf(buf) + (wave * 64 + i * 8) * 8),
                                              16, 0, 0);
     };
 
@@ -306,10 +306,9 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         return d;
     };
     auto code_slice_store = [&](int T, int q, CodeSlice d) {
-        uint4 *dst = reinterpret_cast<uint4 *>(code_ring + (T & 1) * kCodeStageBytes +
-                                               q * (64 / kCB) * kCodeRowBytes);
+        const int base = (wave * 2 + (T & 1)) * (kCodeStageBytes / 16) + q * (64 / kCB) * 8;
 #pragma unroll
-        for (int l = 0; l < kCodeLd; ++l) dst[l * 64 + lane] = d.v[l];
+        for (int l = 0; l < kCodeLd; ++l) code_lds[base + l * 64 + lane] = d.v[l];
     };
 
     // Scale/bias slice q of stage U: 16 rows; load l of a lane covers ring
@@ -330,50 +329,50 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         return d;
     };
     auto sb_slice_store = [&](int U, int q, SbSlice d) {
-        uint32_t *dst = reinterpret_cast<uint32_t *>(sb_ring + (U & 1) * sb_stage_bytes<ST>() +
-                                                     16 * q * kSbRow);
+        const int base = (wave * 2 + (U & 1)) * (sb_stage_bytes<ST>() / 4) + 16 * q * kSbRow / 4;
 #pragma unroll
         for (int l = 0; l < kSbLd; ++l) {
-            dst[l * 64 + lane] = d.s[l];
-            dst[64 * kSbRow / 4 + l * 64 + lane] = d.b[l];
+            sb_lds[base + l * 64 + lane] = d.s[l];
+            sb_lds[base + 64 * kSbRow / 4 + l * 64 + lane] = d.b[l];
         }
     };
-    // The slice a block writes: block kb writes codes slice t % kCB of stage
-    // t / kCB + 1 and scale slice min(t % 2^lg_sb, 3) of stage t / 2^lg_sb + 1,
-    // t = kb + 3, and loads (into registers) those of block kb + 2.
+    // Slice t: codes slice t % kCB of stage t / kCB + 1, scale slice
+    // min(t % 2^lg_sb, 3) of stage t / 2^lg_sb + 1 (slices 4.. of a stage
+    // rewrite slice 3 with the same bytes).  Block kb writes slice kb + 3
+    // (loaded during block kb - 1).
     auto code_slice_of = [&](int tt, int &T, int &q) { T = tt / kCB + 1; q = tt % kCB; };
     auto sb_slice_of = [&](int tt, int &U, int &q) {
         U = (tt >> lg_sb) + 1;
         q = min(tt & ((1 << lg_sb) - 1), 3);
     };
 
-    // a lane's codes, scale and bias of K block kb, from the rings
+    // a lane's codes, scale and bias of K block kb, from the rings (indexed
+    // straight off the LDS arrays, so the compiler can tell which array each
+    // read touches)
     auto read_codes = [&](int kb, int cb, CodeRegs<BITS> &c) {
         const int row = cb * 32 + nr;
-        const uint4 *ring = reinterpret_cast<const uint4 *>(
-            code_ring + ((kb / kCB) & 1) * kCodeStageBytes + row * kCodeRowBytes);
+        const int base = (wave * 2 + ((kb / kCB) & 1)) * (kCodeStageBytes / 16) + row * 8;
 #pragma unroll
         for (int i = 0; i < BITS / 4; ++i) {
             const int chunk = ((kb % kCB) * 2 + h) * (BITS / 4) + i;
-            c.w[i] = ring[chunk ^ ((row >> 1) & 7)];
+            c.w[i] = code_lds[base + (chunk ^ ((row >> 1) & 7))];
         }
         const int ss = kb >> lg_sb;
         const int g = ((kb * kBK2 + 32 * h) >> p.lg_gs) - ss * kSbGroups;
-        const ST *sp = reinterpret_cast<const ST *>(
-            sb_ring + (ss & 1) * sb_stage_bytes<ST>() + row * kSbRow);
+        const int sbase = (wave * 2 + (ss & 1)) * (sb_stage_bytes<ST>() / 4) + row * (kSbRow / 4);
         if constexpr (sizeof(ST) == 2) {
-            c.s = sp[g];
-            c.b = sp[g + 64 * kSbRow / 2];
+            const int sh = 16 * (g & 1);
+            c.s = (sb_lds[sbase + (g >> 1)] >> sh) & 0xffffu;
+            c.b = (sb_lds[sbase + 64 * kSbRow / 4 + (g >> 1)] >> sh) & 0xffffu;
         } else {
-            c.s = __float_as_uint(sp[g]);
-            c.b = __float_as_uint(sp[g + 64 * kSbRow / 4]);
+            c.s = sb_lds[sbase + g];
+            c.b = sb_lds[sbase + 64 * kSbRow / 4 + g];
         }
     };
 
     f32x16_t acc[8][2];        // first written by the first MFMA (zero C operand)
-    bf16x8_t bop[2][4];        // [column block][k16 step] of the current block
+    bf16x8_t bop[2][2][4];     // B operands: [K block parity][column block][k16 step]
     bf16x8_t a[2][8];          // A operands: [k16 step parity][row block]
-    CodeRegs<BITS> cr[2][2];   // [K block parity][column block]
     // ring slices in flight, by the parity of the block that writes them
     CodeSlice csl0, csl1;
     SbSlice ssl0, ssl1;
@@ -382,15 +381,16 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     // register set of step j's parity
     auto read_a = [&](int buf, int j, int rb) {
         const int c = 4 * h + j, r = rb * 32 + nr;
-        a[j & 1][rb] = __builtin_bit_cast(bf16x8_t, lds[(buf * kBM + r) * 8 + (c ^ ((r >> 1) & 7))]);
+        a[j & 1][rb] = __builtin_bit_cast(bf16x8_t, x_buf(buf)[r * 8 + (c ^ ((r >> 1) & 7))]);
     };
 
-    // Prologue: x blocks 0 and 1; ring stage 0, from which the codes of
-    // blocks 0 and 1 are read at once (the rings are private to the wave, so
-    // its own LDS order suffices), before the slices blocks -3..-1 would have
-    // written (at 8 bits one of them overwrites stage 0); the slice block 0
-    // writes (block 0 loads the one block 1 writes); then block 0's B
-    // operands and first A operands.
+    CodeRegs<BITS> cr[2][2];   // codes of the next blocks: [K block parity][column block]
+
+    // Prologue: x blocks 0 and 1; ring stage 0, from which blocks 0 and 1
+    // are read before any other slice is written (at 8 bits stage 2 shares
+    // stage 0's buffer); block 0's B operands; slices 0..2 (written by
+    // blocks -3..-1); slice 3, which block 0 writes; block 0's first A
+    // operands.
     load_x(0, 0);
     load_x(1, min(1, nk - 1));
 #pragma unroll
@@ -416,27 +416,31 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         sb_slice_of(3, T, q);
         ssl0 = sb_slice_load(T, q);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bop[0][0][j] = dequant_step<BITS, ST>(cr[0][0], j);
+        bop[0][1][j] = dequant_step<BITS, ST>(cr[0][1], j);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        bop[0][j] = dequant_step<BITS, ST>(cr[0][0], j);
-        bop[1][j] = dequant_step<BITS, ST>(cr[0][1], j);
-    }
-#pragma unroll
     for (int rb = 0; rb < 8; ++rb) read_a(0, 0, rb);
 
-    // One K block (PAR = kb % 2, the x buffer, at compile time).  Step j's
-    // MFMAs run while step j + 1's A operands are read and the next block's
-    // step j is dequantized into B operand j (rolling).  One barrier per
-    // block, before the last step: every wave has then read all of this
-    // block's A operands and waited for its x loads of the next block, so
-    // that x is visible (its first A operands are read under the last step's
-    // MFMAs) and this block's x buffer is free for x two blocks ahead.  A
-    // ring slice is loaded in a block's first step, written after the
-    // barrier one block later into a stage buffer whose previous stage was
-    // last read before that write (in the same step at the latest), and
-    // first read at least one block after the write.  Prefetches past the
+    // One K block (PAR = kb % 2 at compile time: x buffer, B-operand set,
+    // code and slice registers).  Step j runs its 16 MFMAs, reads the next
+    // step's A operands into the other A set, and dequantizes step j of the
+    // next block into the other B set -- registers last read by MFMAs a
+    // whole step (A) or block (B) earlier, never by MFMAs that may still be
+    // queued.  One barrier per block, before the last step: every wave has
+    // then read all of this block's A operands and waited for its x loads of
+    // the next block, so that x is visible (its first A operands are read
+    // under the last step's MFMAs) and this block's x buffer is free for x
+    // two blocks ahead.  Right after the barrier no load into LDS is in
+    // flight, and the rings are read (codes of block kb + 2) and then
+    // written (slice kb + 3, loaded in the previous block's first step)
+    // before x is requested: a slice goes into a stage buffer whose previous
+    // stage was last read before it, at the latest just before in the same
+    // step, and is first read at least one block later.  Prefetches past the
     // last block re-read the last one, into buffers nothing reads any more
     // (or with the same bytes); the operands prepared during the last block
     // go unused.
@@ -445,38 +449,33 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         constexpr int PAR = decltype(par)::value;
         constexpr bool FIRST = decltype(first)::value;
         const f32x16_t zero = {};
-        // Step j: the 16 MFMAs, the next step's A operands (into the other
-        // register set), and one step of dequantization into the B operand
-        // the previous step used: step j - 1 of the next block, or at step 0
-        // step 3 of this one (its codes are still in cr[PAR]).  A register
-        // is never rewritten while MFMAs that read it may still be queued:
-        // an LDS return or a VALU write lands at least a whole step after
-        // the MFMAs that read the register were issued.  `issue` adds memory
-        // operations that the scheduler spreads over the step.
+        // Step j.  The B operands are double-buffered by block for a measured
+        // reason: rewriting a B register in place right after the MFMAs that
+        // read it (the usual rolling scheme) gave corrupted products on this
+        // GPU whenever the write was scheduled within a few instructions of
+        // those MFMAs, from one run to the next -- the matrix core reads its
+        // operands after issue, and nothing stalls the write.
         auto step = [&](int j, int nbuf, int nj, auto issue) {
             issue();
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
                 const bool init = FIRST && j == 0;
-                acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[0][j], init ? zero : acc[rb][0], 0, 0, 0);
-                acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[1][j], init ? zero : acc[rb][1], 0, 0, 0);
+                acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[PAR][0][j], init ? zero : acc[rb][0], 0, 0, 0);
+                acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][rb], bop[PAR][1][j], init ? zero : acc[rb][1], 0, 0, 0);
                 read_a(nbuf, nj, rb);
             }
-            if (j == 0) {
-                bop[0][3] = dequant_step<BITS, ST>(cr[PAR][0], 3);
-                bop[1][3] = dequant_step<BITS, ST>(cr[PAR][1], 3);
-            } else {
-                bop[0][j - 1] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j - 1);
-                bop[1][j - 1] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j - 1);
+            bop[PAR ^ 1][0][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][0], j);
+            bop[PAR ^ 1][1][j] = dequant_step<BITS, ST>(cr[PAR ^ 1][1], j);
+            // spread the VALU over the MFMAs: per row block, its two MFMAs
+            // and six VALU operations
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
-            // (No sched_group_barrier pattern here: forcing MFMA / LDS / VALU
-            // interleaving made some 8-bit instances return corrupted
-            // values from one run to the next, and was slower than the
-            // scheduler's own order.)
             __builtin_amdgcn_sched_barrier(0);
         };
-        // step 0 issues the ring loads a block two blocks from now writes
-        // (slice t = kb + 4, into the registers of the other parity)
+        // step 0 also loads slice kb + 4 (written by the next block)
         step(0, PAR, 1, [&] {
             CodeSlice &csl = PAR ? csl0 : csl1;
             SbSlice &ssl = PAR ? ssl0 : ssl1;
@@ -498,11 +497,6 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // Step 3, with the ring reads (codes of block kb + 2, the parity of
-        // this block's, already used), the ring writes of slice t = kb + 3
-        // (loaded two blocks ago), and x two blocks ahead into this block's
-        // buffer -- in that order, so no load into LDS is in flight while
-        // the rings are read or written.
         step(3, PAR ^ 1, 0, [&] {
             read_codes(kb + 2, 0, cr[PAR][0]);
             read_codes(kb + 2, 1, cr[PAR][1]);
@@ -592,7 +586,7 @@ hipError_t tiled_run(const TiledLaunch &a, hipStream_t stream)
         if (!tiled_fits(kBM, kBN, BITS, a.gs, a.sb_dt, a.m, a.n, a.k)) return hipErrorInvalidValue;
         const int tm = (int)((a.m + kBM - 1) / kBM), tn = (int)((a.n + kBN - 1) / kBN);
         const int per = (tm * tn + 7) / 8;
-        tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), tiled_lds_bytes<ST>(), stream>>>(p, tm, tn, per);
+        tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), 0, stream>>>(p, tm, tn, per);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((a.n + kTN - 1) / kTN), (unsigned)((a.m + kTM - 1) / kTM));
