@@ -254,6 +254,11 @@ def nq_gather_qmm(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hi
         raise ValueError("rhs_idx must have one id per row")
     if y is None:
         y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        need = lib.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, _dt(x),
+                                                 _dt(scales), int(bool(sorted_hint)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
                              _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(rhs_idx),

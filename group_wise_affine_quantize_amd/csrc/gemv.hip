@@ -54,6 +54,13 @@ struct GemvParams {
     int64_t rows_per_item, k, n, e;
     int64_t words_per_row, groups_per_row;
     int64_t item0;          // first item of this launch (items are split over launches)
+    // Grouped gather: when `chunks` is set, workgroup row y runs chunk y of
+    // the table (uint4 {expert, first, count, 0}: activation vectors
+    // perm[first .. first + count) all use that expert); chunks past
+    // *nchunks do nothing.
+    const uint4 *chunks;
+    const uint32_t *perm;
+    const uint32_t *nchunks;
     int gs, ksplit, steps, chunks_per_item, qrows;   // qrows: row groups per workgroup
 };
 
@@ -241,19 +248,54 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
     const int q = wave / S;             // row group of this wave inside the workgroup
     const int64_t n0 = ((int64_t)blockIdx.x * p.qrows + q) * RW;
 
-    const int64_t item = p.item0 + blockIdx.y / p.chunks_per_item;
-    const int64_t r0 = (int64_t)(blockIdx.y % p.chunks_per_item) * MR;
-    const int mrows = (int)min((int64_t)MR, p.rows_per_item - r0);
-    const XT *xb = p.x + (item * p.rows_per_item + r0) * p.k;
-    XT *yb = p.y + (item * p.rows_per_item + r0) * p.n;
-
     bool live = true;
     int64_t slab = 0;
-    if (p.idx) {
-        const uint32_t ex = p.idx[item];
-        if ((int64_t)ex >= p.e) live = false;
-        else slab = ex;
+    int mrows;
+    const XT *xb;   // activation row 0 of this chunk (rows are contiguous unless grouped)
+    XT *yb;
+    uint32_t first = 0;   // grouped: the chunk's first position in perm
+    if (p.chunks) {
+        if (blockIdx.y >= *p.nchunks) return;   // uniform over the workgroup
+        const uint4 ch = p.chunks[blockIdx.y];
+        if ((int64_t)ch.x >= p.e) live = false;
+        else slab = ch.x;
+        first = ch.y;
+        mrows = (int)ch.z;
+        xb = p.x;
+        yb = p.y;
+    } else {
+        const int64_t item = p.item0 + blockIdx.y / p.chunks_per_item;
+        const int64_t r0 = (int64_t)(blockIdx.y % p.chunks_per_item) * MR;
+        mrows = (int)min((int64_t)MR, p.rows_per_item - r0);
+        xb = p.x + (item * p.rows_per_item + r0) * p.k;
+        yb = p.y + (item * p.rows_per_item + r0) * p.n;
+        if (p.idx) {
+            const uint32_t ex = p.idx[item];
+            if ((int64_t)ex >= p.e) live = false;
+            else slab = ex;
+        }
     }
+    // activation rows of the chunk (rows past the chunk's repeat its last),
+    // computed once and kept in scalar registers: they are the same for the
+    // whole workgroup
+    const XT *xr[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const int mm = min(m, mrows - 1);
+        const XT *r = p.chunks ? p.x + (int64_t)p.perm[first + mm] * p.k : xb + (int64_t)mm * p.k;
+        const uint64_t u = reinterpret_cast<uint64_t>(r);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+        xr[m] = reinterpret_cast<const XT *>(((uint64_t)hi << 32) | lo);
+    }
+    auto x_row = [&](int m) -> const XT * {
+        if constexpr (MR == 1) return xr[0];
+        else if constexpr (MR == 2) return m == 0 ? xr[0] : xr[1];
+        else return xr[m];   // m is a constant after unrolling here
+    };
+    auto y_row = [&](int m) -> XT * {
+        return p.chunks ? p.y + (int64_t)p.perm[first + m] * p.n : yb + (int64_t)m * p.n;
+    };
     const uint32_t *cb = p.codes + slab * p.n * p.words_per_row;
     const ST *sb = p.scales + slab * p.n * p.groups_per_row;
     const ST *bb = p.biases + slab * p.n * p.groups_per_row;
@@ -281,8 +323,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
             const int c = min((int)threadIdx.x + i * (int)blockDim.x, nstage - 1);
             const int m = c / (p.steps * 64), rem = c % (p.steps * 64);
             const int64_t e0 = (int64_t)(rem >> 6) * kStepElems + (rem & 63) * kLaneChunk;
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                xb + (int64_t)min(m, mrows - 1) * p.k + (e0 < p.k ? e0 : 0));
+            const uint4 *src = reinterpret_cast<const uint4 *>(x_row(m) + (e0 < p.k ? e0 : 0));
 #pragma unroll
             for (int j = 0; j < 4; ++j) sx[i][j] = src[j];
         }
@@ -307,8 +348,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
         if constexpr (kXW > 0) {
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
-                const uint4 *xs =
-                    reinterpret_cast<const uint4 *>(xb + (int64_t)min(m, mrows - 1) * p.k + ec);
+                const uint4 *xs = reinterpret_cast<const uint4 *>(x_row(m) + ec);
 #pragma unroll
                 for (int i = 0; i < kXWR; ++i) st.xr[m * kXWR + i] = xs[i];
             }
@@ -341,8 +381,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
                     for (int j = 0; j < 4; ++j) {
                         uint4 d;
                         if constexpr (kXW > 0) d = st.xr[m * kXWR + j];
-                        else d = reinterpret_cast<const uint4 *>(
-                                 xb + (int64_t)min(m, mrows - 1) * p.k + e0)[j];
+                        else d = reinterpret_cast<const uint4 *>(x_row(m) + e0)[j];
                         x_pairs_word(d, xp + 4 * j);
                         X[m] = x_sum_word(d, X[m]);
                     }
@@ -370,8 +409,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
                     if constexpr (kXW > 0) {
                         x_f32_word<XT>(st.xr + m * kXWR, j, xf[m]);
                     } else {
-                        x_f32_word<XT>(reinterpret_cast<const uint4 *>(
-                                           xb + (int64_t)min(m, mrows - 1) * p.k + e0), j, xf[m]);
+                        x_f32_word<XT>(reinterpret_cast<const uint4 *>(x_row(m) + e0), j, xf[m]);
                     }
 #pragma unroll
                     for (int i = 0; i < 8; ++i) X[m] += xf[m][i];
@@ -461,7 +499,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
     const int mi = vi / RW, ri = vi % RW;
     const bool writer = leader && mi < mrows && n0 + ri < p.n;
     if (S == 1) {
-        if (writer) Elt<XT>::store(yb, (int64_t)mi * p.n + n0 + ri, mine);
+        if (writer) Elt<XT>::store(y_row(mi), n0 + ri, mine);
         return;
     }
     __shared__ float part[8 * V];
@@ -470,8 +508,115 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
     if (sl == 0 && writer) {
         float tot = part[(q * S) * V + vi];
         for (int s2 = 1; s2 < S; ++s2) tot += part[(q * S + s2) * V + vi];
-        Elt<XT>::store(yb, (int64_t)mi * p.n + n0 + ri, tot);
+        Elt<XT>::store(y_row(mi), n0 + ri, tot);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Grouping pass of the grouped gather ("Mixture of experts" section: a
+// grouped kernel reads each expert's weights once for the rows that chose
+// it).  One workgroup sorts the activation vectors v = r * l + j by expert
+// bucket b = min(ids[r], e) (bucket e: ids past the last expert, whose rows
+// are zero) with a stable counting sort -- within a bucket in increasing v,
+// so the result never depends on timing -- and cuts every bucket into
+// chunks of at most kGroupChunk vectors.  Workspace layout (uint32):
+// perm[V], nchunks, padding to 16 bytes, then the chunk table as uint4
+// {bucket, first position in perm, count, 0}.
+constexpr int kGroupThreads = 1024;
+
+__device__ void block_exclusive_scan(uint32_t *a, int n, uint32_t *part, uint32_t *total)
+{
+    // a[0..n) in LDS, scanned in place; part: kGroupThreads scratch words
+    const int t = threadIdx.x;
+    const int seg = (n + kGroupThreads - 1) / kGroupThreads;
+    const int lo = min(n, t * seg), hi = min(n, lo + seg);
+    uint32_t sum = 0;
+    for (int i = lo; i < hi; ++i) sum += a[i];
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < kGroupThreads; off <<= 1) {   // inclusive Hillis-Steele
+        const uint32_t v = t >= off ? part[t - off] : 0u;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    uint32_t run = t ? part[t - 1] : 0u;
+    if (t == kGroupThreads - 1) *total = part[t];
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t c = a[i];
+        a[i] = run;
+        run += c;
+    }
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kGroupThreads)
+gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_t *ws, int64_t v_total)
+{
+    extern __shared__ uint32_t sh[];   // count[e+1], chunk offset[e+1], part[1024], bucket[1024], totals[2]
+    const int nb = e + 1;
+    uint32_t *cnt = sh, *coff = sh + nb, *part = sh + 2 * nb, *bk = part + kGroupThreads;
+    uint32_t *totals = bk + kGroupThreads;
+    uint32_t *perm = ws, *nchunks = ws + v_total;
+    uint4 *table = reinterpret_cast<uint4 *>(ws + ((v_total + 1 + 3) & ~(int64_t)3));
+    const int t = threadIdx.x;
+    auto bucket = [&](int64_t v) -> uint32_t { return min(ids[v / l], (uint32_t)e); };
+
+    for (int b = t; b < nb; b += kGroupThreads) cnt[b] = 0;
+    __syncthreads();
+    for (int64_t v = t; v < v_total; v += kGroupThreads) atomicAdd(&cnt[bucket(v)], 1u);
+    __syncthreads();
+    for (int b = t; b < nb; b += kGroupThreads) coff[b] = (cnt[b] + kGroupChunk - 1) / kGroupChunk;
+    __syncthreads();
+    block_exclusive_scan(coff, nb, part, &totals[1]);   // first chunk of each bucket
+    // chunk table, before cnt turns into offsets
+    for (int b = t; b < nb; b += kGroupThreads) {
+        const uint32_t c = cnt[b];
+        for (uint32_t i = 0; i * kGroupChunk < c; ++i)
+            table[coff[b] + i] = make_uint4((uint32_t)b, 0u, min((uint32_t)kGroupChunk, c - i * kGroupChunk), 0u);
+    }
+    block_exclusive_scan(cnt, nb, part, &totals[0]);    // first position of each bucket
+    for (int b = t; b < nb; b += kGroupThreads) {
+        const uint32_t c = (b + 1 < nb ? cnt[b + 1] : (uint32_t)v_total) - cnt[b];
+        for (uint32_t i = 0; i * kGroupChunk < c; ++i) table[coff[b] + i].y = cnt[b] + i * kGroupChunk;
+    }
+    if (t == 0) *nchunks = totals[1];
+    // stable placement, kGroupThreads vectors at a time: a vector's rank is
+    // the number of earlier vectors of its bucket in the same batch
+    for (int64_t v0 = 0; v0 < v_total; v0 += kGroupThreads) {
+        const int64_t v = v0 + t;
+        const uint32_t b = v < v_total ? bucket(v) : 0xffffffffu;
+        bk[t] = b;
+        __syncthreads();
+        if (v < v_total) {
+            uint32_t rank = 0;
+            for (int u = 0; u < t; ++u) rank += bk[u] == b;
+            perm[cnt[b] + rank] = (uint32_t)v;
+        }
+        __syncthreads();
+        if (v < v_total) atomicAdd(&cnt[b], 1u);   // the batch's count per bucket (an exact sum)
+        __syncthreads();
+    }
+}
+
+size_t gather_group_ws_bytes(int64_t vectors, int64_t e)
+{
+    const int64_t max_chunks = (vectors + kGroupChunk - 1) / kGroupChunk + e + 1;
+    return (size_t)(((vectors + 1 + 3) & ~(int64_t)3) + 4 * max_chunks) * 4;
+}
+
+int64_t gather_group_max_chunks(int64_t vectors, int64_t e)
+{
+    return (vectors + kGroupChunk - 1) / kGroupChunk + e + 1;
+}
+
+hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, void *ws,
+                                hipStream_t stream)
+{
+    const size_t lds = (size_t)(2 * (e + 1) + 2 * kGroupThreads + 2) * 4;
+    gather_group_kernel<<<1, kGroupThreads, lds, stream>>>(ids, rows, l, (int)e,
+                                                           static_cast<uint32_t *>(ws), rows * l);
+    return hipGetLastError();
 }
 
 namespace {
@@ -489,6 +634,9 @@ hipError_t gemv_run(const GemvLaunch &a, hipStream_t stream)
     p.scales = static_cast<const ST *>(a.scales);
     p.biases = static_cast<const ST *>(a.biases);
     p.idx = a.idx;
+    p.chunks = reinterpret_cast<const uint4 *>(a.chunks);
+    p.perm = a.perm;
+    p.nchunks = a.nchunks;
     p.rows_per_item = a.rows_per_item;
     p.k = a.k;
     p.n = a.n;
@@ -504,6 +652,13 @@ hipError_t gemv_run(const GemvLaunch &a, hipStream_t stream)
     const size_t lds = STX > 0 ? (size_t)MR * p.steps * kStageBytesPerStep : 0;
     const int64_t rows_per_block = (int64_t)p.qrows * RW;
     const unsigned gx = (unsigned)((a.n + rows_per_block - 1) / rows_per_block);
+    if (a.chunks) {   // grouped gather: one launch over the whole chunk table
+        if (a.max_chunks > kMaxGridY) return hipErrorInvalidValue;
+        p.item0 = 0;
+        gemv_kernel<BITS, XT, ST, MR, RW, STX>
+            <<<dim3(gx, (unsigned)a.max_chunks), dim3(threads), lds, stream>>>(p);
+        return hipGetLastError();
+    }
     const int64_t items_per_launch = std::max<int64_t>(1, kMaxGridY / p.chunks_per_item);
     for (int64_t i0 = 0; i0 < a.items; i0 += items_per_launch) {
         const int64_t cnt = std::min(items_per_launch, a.items - i0);

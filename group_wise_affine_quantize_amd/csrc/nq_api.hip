@@ -368,13 +368,27 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
     return qmm_common("nq_qmm_with_plan", 0, plan, a, stream);
 }
 
+namespace {
+// The grouped gather ("Mixture of experts" section): worth it once experts
+// are shared by several vectors.  A pure function of the sizes; it never
+// changes a row's bits (the matrix-vector family's rows do not depend on
+// how many rows share a launch chunk).
+bool gather_grouped(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n)
+{
+    const int64_t v = rows * l;
+    return k > 0 && n > 0 && rows > 0 && l > 0 && e > 0 && e <= 4096 && v >= 16 && v >= 4 * e &&
+           v < ((int64_t)1 << 31) && nqk::gather_group_max_chunks(v, e) <= 65535;
+}
+}  // namespace
+
 size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n,
                                      int32_t group_size, int32_t bits, nq_dtype x_dt,
                                      nq_dtype sb_dt, int32_t sorted_hint)
 {
-    (void)rows, (void)l, (void)k, (void)e, (void)n, (void)group_size, (void)bits, (void)x_dt,
-        (void)sb_dt, (void)sorted_hint;
-    return 0;
+    (void)group_size, (void)bits, (void)x_dt, (void)sb_dt, (void)sorted_hint;
+    if (rows < 0 || l < 0 || e < 0 || k < 0 || n < 0) return 0;
+    if (!gather_grouped(rows, l, k, e, n)) return 0;
+    return nqk::gather_group_ws_bytes(rows * l, e);
 }
 
 nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
@@ -418,6 +432,19 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
     for (int i = 0; i < 5; ++i)
         if (overlap(sy, ins[i])) return fail(NQ_ERR_ALIAS, "%s: y overlaps %s", op, names[i]);
 
+    const bool grouped = gather_grouped(rows, l, k, e, n);
+    if (grouped) {
+        const size_t need = nqk::gather_group_ws_bytes(rows * l, e);
+        if (!workspace || workspace_bytes < need)
+            return fail(NQ_ERR_WORKSPACE, "%s: the grouped route needs a workspace of %zu bytes (got %zu)",
+                        op, need, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(NQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", op);
+        const Span sw{workspace, (int64_t)need};
+        if (overlap(sw, sy)) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps y", op);
+        for (int i = 0; i < 5; ++i)
+            if (overlap(sw, ins[i])) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps %s", op, names[i]);
+    }
+
     nqk::GemvLaunch g;
     g.x = x;
     g.y = y;
@@ -436,6 +463,19 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
     g.bits = bits;
     g.ksplit = gemv_ksplit(n, k);   // the plan nq_qmm_row_exact takes
     g.rows_per_wave = 0;
+    if (grouped) {
+        if (hipError_t err = nqk::launch_gather_groups(rhs_idx, rows, l, e, workspace, stream))
+            return check_launch(op, err);
+        const int64_t v = rows * l;
+        uint32_t *ws = static_cast<uint32_t *>(workspace);
+        g.idx = nullptr;
+        g.perm = ws;
+        g.nchunks = ws + v;
+        g.chunks = ws + ((v + 1 + 3) & ~(int64_t)3);
+        g.max_chunks = nqk::gather_group_max_chunks(v, e);
+        g.items = 1;
+        g.rows_per_item = nqk::kGroupChunk;   // chunks of up to 8 vectors
+    }
     return check_launch(op, nqk::launch_gemv(g, stream));
 }
 

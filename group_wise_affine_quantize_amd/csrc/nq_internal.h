@@ -28,6 +28,11 @@ hipError_t launch_dequantize(const uint32_t *codes, const void *scales, const vo
 // consecutive rows of x (starting at row i * rows_per_item) with the weights
 // of expert idx[i] (or the only weight matrix when idx is null), writing the
 // same rows of y.  Items whose expert id is >= e produce zero rows.
+//
+// Grouped gather (chunks set): instead of items, the launch runs the chunk
+// table a grouping pass built (launch_gather_groups); chunk c multiplies the
+// activation vectors perm[first .. first + count) by expert `bucket`'s
+// weights (bucket >= e: zero rows).
 struct GemvLaunch {
     const void *x;
     void *y;
@@ -39,8 +44,22 @@ struct GemvLaunch {
     int64_t items, rows_per_item, k, n, e;
     int gs, bits;
     int ksplit, rows_per_wave;
+    const uint32_t *perm = nullptr, *chunks = nullptr, *nchunks = nullptr;
+    int64_t max_chunks = 0;
 };
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
+
+// Vectors per chunk of the grouped gather (the matrix-vector family's
+// largest row count per launch chunk).
+constexpr int kGroupChunk = 8;
+// Workspace of the grouping pass over `vectors` activation vectors and e
+// experts, and the chunk-table bound it implies.
+size_t gather_group_ws_bytes(int64_t vectors, int64_t e);
+int64_t gather_group_max_chunks(int64_t vectors, int64_t e);
+// Groups the vectors r * l + j by expert ids[r] (one workgroup): perm,
+// chunk count and chunk table into ws (layout in gemv.hip).
+hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, void *ws,
+                                hipStream_t stream);
 
 // Tiled bf16-MFMA product: y[m, n] = x[m, k] . w_hat[n, k]^T, x and y bf16.
 struct TiledLaunch {

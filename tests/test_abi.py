@@ -226,6 +226,35 @@ def test_gather_argument_errors(lib):
     assert b"nq_gather_qmm:" in lib.nq_last_error()
 
 
+def test_gather_grouped_route_workspace(lib):
+    """Many rows per expert take the grouped route, which needs a workspace;
+    few rows per expert (or few rows) do not."""
+    def need(rows, l, e, n=1408, k=2048):
+        return lib.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, 64, 4, BF16, BF16, 1)
+    assert need(512, 1, 32) > 0                 # the mixture-of-experts workload
+    assert need(512, 1, 32) % 16 == 0 or need(512, 1, 32) >= 512 * 4
+    assert need(4, 1, 8) == 0                   # the page example: 4 rows, 8 experts
+    assert need(100, 1, 32) == 0                # fewer than 4 vectors per expert
+    assert need(8, 2, 2) > 0                    # 16 vectors over 2 experts
+    assert need(512, 1, 32) == need(256, 2, 32)  # vectors = rows * l
+    assert need(0, 1, 32) == 0 and need(512, 1, 0) == 0
+
+    # codes of 32 experts take 46 MB: every array sits 64 MB from the next
+    y = FAKE2 + 0x8000000
+    def g(ws, ws_bytes, rows=512):
+        return lib.nq_gather_qmm(FAKE, BF16, rows, 1, 2048, FAKE2, FAKE2 + 0x4000000,
+                                 FAKE2 + 0x5000000, BF16, 32, 1408, 64, 4, FAKE2 + 0x6000000, 1,
+                                 y, ws, ws_bytes, None)
+    nb = need(512, 1, 32)
+    ws = FAKE2 + 0x10000000
+    assert g(0, 0) == NQ_ERR_WORKSPACE
+    assert b"workspace" in lib.nq_last_error()
+    assert g(ws, nb - 1) == NQ_ERR_WORKSPACE
+    assert g(ws + 8, nb) == NQ_ERR_ALIGN
+    assert g(y, nb) == NQ_ERR_ALIAS                       # workspace overlaps y
+    assert g(FAKE2 + 0x6000000, nb) == NQ_ERR_ALIAS       # ... or the ids
+
+
 def test_error_string_is_thread_local(lib):
     import threading
     _qmm(lib, k=100)

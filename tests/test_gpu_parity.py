@@ -219,6 +219,44 @@ def test_gather_parity(x_dtype, w_dtype, l):
             assert bits_equal(yq, y[r]), r
 
 
+@pytest.mark.parametrize("case", ["one_expert", "l2_random", "sorted_many", "ids_past_e"])
+def test_gather_grouped(case):
+    """Shapes that take the grouped route (vectors sorted by expert on the
+    device, chunks of up to 8): every row bit-equal to the one-row product
+    with its expert's weights, zero rows for ids past the last expert."""
+    gs, bits, n, k = 64, 4, 96, 1024
+    e, rows, l = {"one_expert": (3, 100, 1), "l2_random": (8, 64, 2),
+                  "sorted_many": (32, 300, 1), "ids_past_e": (4, 17, 1)}[case]
+    rng = np.random.default_rng(len(case))
+    if case == "one_expert":
+        ids = np.full(rows, 1, np.uint32)
+    elif case == "sorted_many":
+        ids = np.sort(rng.integers(0, e, size=rows, dtype=np.uint32))
+    elif case == "ids_past_e":
+        ids = rng.integers(0, e + 3, size=rows, dtype=np.uint32)
+    else:
+        ids = rng.integers(0, e, size=rows, dtype=np.uint32)
+    assert B.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, gs, bits, torch.bfloat16,
+                                           torch.bfloat16) > 0
+    w, _ = synthetic.random_case(e, (e, n, k), (1, k), 0.02, "bf16")
+    _, x = synthetic.random_case(rows, (1, 1), (rows, l, k), 1.0, "f32", "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    xs, cs, ss, bs = dev(x), dev(c), dev(s), dev(b)
+    y = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids), sorted_hint=case == "sorted_many")
+    assert_rows_close(values(host(y)).reshape(rows * l, n),
+                      O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows * l, n), 1e-2,
+                      "grouped gather")
+    for r in range(0, rows, max(1, rows // 12)):
+        if ids[r] >= e:
+            assert np.all(values(host(y[r])) == 0)
+            continue
+        yr = B.nq_qmm_row_exact(xs[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+        assert bits_equal(yr, y[r]), r
+    # the same call twice gives the same bits
+    y2 = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids))
+    assert bits_equal(y, y2)
+
+
 def test_gather_sorted_hint_same_bits():
     e, n, k, gs, bits, rows = 8, 128, 256, 64, 4, 4
     w, x = synthetic.random_case(3, (e, n, k), (rows, 1, k), 1.0, "f32")
