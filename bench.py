@@ -312,11 +312,18 @@ def main():
         q = B.nq_quantize(dev(d["w"]), wl.group_size, wl.bits)
         xs, ids = dev(d["x"]), dev(d["ids"])
         yg = torch.empty((512, 1, 1408), dtype=torch.bfloat16, device="cuda")
+        wsg = torch.empty(B.nq_gather_qmm_workspace_bytes(512, 1, 2048, 32, 1408, 64, 4,
+                                                          torch.bfloat16, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
         cps = rotated(q)
-        t = timer.run(lambda i: B.nq_gather_qmm(xs, *cps[i % len(cps)], 64, 4, ids, y=yg), steps, 10)
-        put("moe_gather", t, steps, nbytes(*q), "GB/s",
-            {"workload": "x bf16 [512,1,2048], 32 experts W[1408,2048] 4-bit g64, unsorted ids",
-             "tflops": round(2 * 512 * 1408 * 2048 / (t / steps) / 1e12, 3)})
+        for entry, tag in ((B.nq_gather_qmm, "moe_gather"),
+                           (B.nq_gather_qmm_row_exact, "moe_gather_row_exact")):
+            t = timer.run(lambda i: entry(xs, *cps[i % len(cps)], 64, 4, ids, y=yg, workspace=wsg),
+                          steps, 10)
+            put(tag, t, steps, nbytes(*q), "GB/s",
+                {"workload": "x bf16 [512,1,2048], 32 experts W[1408,2048] 4-bit g64, "
+                             "unsorted ids (grouped by expert on the device)",
+                 "tflops": round(2 * 512 * 1408 * 2048 / (t / steps) / 1e12, 3)})
         del cps
 
         wl = synthetic.WORKLOADS["affine_f32_256x512"]

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     load_library,
     nq_dequantize,
     nq_gather_qmm,
+    nq_gather_qmm_row_exact,
     nq_gather_qmm_workspace_bytes,
     nq_qmm,
     nq_qmm_plan,

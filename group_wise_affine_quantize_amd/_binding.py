@@ -58,6 +58,8 @@ _SIGNATURES = {
                                       _I32],
     "nq_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P,
                       _I32, _P, _P, _SZ, _P],
+    "nq_gather_qmm_row_exact": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32,
+                                _I32, _P, _I32, _P, _P, _SZ, _P],
     "nq_status_string": [_I32],
     "nq_last_error": [],
     "nq_version": [],
@@ -237,10 +239,8 @@ def nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, x_dtype, s
                                                         sd, int(bool(sorted_hint)))
 
 
-def nq_gather_qmm(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint=False, y=None,
-                  workspace=None, stream=None):
-    """x [rows, l, k]; codes [e, n, k*bits/32]; scales/biases [e, n, k/gs];
-    rhs_idx [rows] (int32/uint32 bit patterns) -> y [rows, l, n] in x's dtype."""
+def _gather_call(entry, x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint, y,
+                 workspace, stream):
     torch = _torch()
     lib = load_library()
     for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases),
@@ -260,8 +260,24 @@ def nq_gather_qmm(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hi
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.nq_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
-                             _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(rhs_idx),
-                             int(bool(sorted_hint)), _ptr(y), _ptr(workspace), ws_bytes,
-                             _stream(stream)))
+    _check(getattr(lib, entry)(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
+                               _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(rhs_idx),
+                               int(bool(sorted_hint)), _ptr(y), _ptr(workspace), ws_bytes,
+                               _stream(stream)))
     return y
+
+
+def nq_gather_qmm(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint=False, y=None,
+                  workspace=None, stream=None):
+    """x [rows, l, k]; codes [e, n, k*bits/32]; scales/biases [e, n, k/gs];
+    rhs_idx [rows] (int32/uint32 bit patterns) -> y [rows, l, n] in x's dtype.
+    A workspace is allocated when the call needs one and none is given."""
+    return _gather_call("nq_gather_qmm", x, codes, scales, biases, group_size, bits, rhs_idx,
+                        sorted_hint, y, workspace, stream)
+
+
+def nq_gather_qmm_row_exact(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint=False,
+                            y=None, workspace=None, stream=None):
+    """As nq_gather_qmm, every row bit-equal to its one-row product."""
+    return _gather_call("nq_gather_qmm_row_exact", x, codes, scales, biases, group_size, bits,
+                        rhs_idx, sorted_hint, y, workspace, stream)

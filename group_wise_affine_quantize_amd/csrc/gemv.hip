@@ -519,7 +519,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 // bucket b = min(ids[r], e) (bucket e: ids past the last expert, whose rows
 // are zero) with a stable counting sort -- within a bucket in increasing v,
 // so the result never depends on timing -- and cuts every bucket into
-// chunks of at most kGroupChunk vectors.  Workspace layout (uint32):
+// chunks of at most `chunk` vectors.  Workspace layout (uint32):
 // perm[V], nchunks, padding to 16 bytes, then the chunk table as uint4
 // {bucket, first position in perm, count, 0}.
 constexpr int kGroupThreads = 1024;
@@ -551,12 +551,14 @@ __device__ void block_exclusive_scan(uint32_t *a, int n, uint32_t *part, uint32_
 }
 
 __global__ void __launch_bounds__(kGroupThreads)
-gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_t *ws, int64_t v_total)
+gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_t *ws, int64_t v_total,
+                    uint32_t chunk)
 {
-    extern __shared__ uint32_t sh[];   // count[e+1], chunk offset[e+1], part[1024], bucket[1024], totals[2]
+    extern __shared__ uint4 sh4[];   // bucket[1024], part[1024], count[e+1], chunk offset[e+1], totals[2]
+    uint32_t *sh = reinterpret_cast<uint32_t *>(sh4);
     const int nb = e + 1;
-    uint32_t *cnt = sh, *coff = sh + nb, *part = sh + 2 * nb, *bk = part + kGroupThreads;
-    uint32_t *totals = bk + kGroupThreads;
+    uint32_t *bk = sh, *part = sh + kGroupThreads, *cnt = part + kGroupThreads, *coff = cnt + nb;
+    uint32_t *totals = coff + nb;
     uint32_t *perm = ws, *nchunks = ws + v_total;
     uint4 *table = reinterpret_cast<uint4 *>(ws + ((v_total + 1 + 3) & ~(int64_t)3));
     const int t = threadIdx.x;
@@ -566,19 +568,19 @@ gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_
     __syncthreads();
     for (int64_t v = t; v < v_total; v += kGroupThreads) atomicAdd(&cnt[bucket(v)], 1u);
     __syncthreads();
-    for (int b = t; b < nb; b += kGroupThreads) coff[b] = (cnt[b] + kGroupChunk - 1) / kGroupChunk;
+    for (int b = t; b < nb; b += kGroupThreads) coff[b] = (cnt[b] + chunk - 1) / chunk;
     __syncthreads();
     block_exclusive_scan(coff, nb, part, &totals[1]);   // first chunk of each bucket
     // chunk table, before cnt turns into offsets
     for (int b = t; b < nb; b += kGroupThreads) {
         const uint32_t c = cnt[b];
-        for (uint32_t i = 0; i * kGroupChunk < c; ++i)
-            table[coff[b] + i] = make_uint4((uint32_t)b, 0u, min((uint32_t)kGroupChunk, c - i * kGroupChunk), 0u);
+        for (uint32_t i = 0; i * chunk < c; ++i)
+            table[coff[b] + i] = make_uint4((uint32_t)b, 0u, min(chunk, c - i * chunk), 0u);
     }
     block_exclusive_scan(cnt, nb, part, &totals[0]);    // first position of each bucket
     for (int b = t; b < nb; b += kGroupThreads) {
         const uint32_t c = (b + 1 < nb ? cnt[b + 1] : (uint32_t)v_total) - cnt[b];
-        for (uint32_t i = 0; i * kGroupChunk < c; ++i) table[coff[b] + i].y = cnt[b] + i * kGroupChunk;
+        for (uint32_t i = 0; i * chunk < c; ++i) table[coff[b] + i].y = cnt[b] + i * chunk;
     }
     if (t == 0) *nchunks = totals[1];
     // stable placement, kGroupThreads vectors at a time: a vector's rank is
@@ -589,8 +591,15 @@ gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_
         bk[t] = b;
         __syncthreads();
         if (v < v_total) {
+            // 16-byte reads of the earlier buckets (every lane of a wave
+            // reads the same address at a time: broadcasts)
+            const uint4 *bk4 = reinterpret_cast<const uint4 *>(bk);
             uint32_t rank = 0;
-            for (int u = 0; u < t; ++u) rank += bk[u] == b;
+            for (int u = 0; u < (t >> 2); ++u) {
+                const uint4 q = bk4[u];
+                rank += (q.x == b) + (q.y == b) + (q.z == b) + (q.w == b);
+            }
+            for (int u = t & ~3; u < t; ++u) rank += bk[u] == b;
             perm[cnt[b] + rank] = (uint32_t)v;
         }
         __syncthreads();
@@ -599,23 +608,23 @@ gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_
     }
 }
 
-size_t gather_group_ws_bytes(int64_t vectors, int64_t e)
+int64_t gather_group_max_chunks(int64_t vectors, int64_t e, int chunk)
 {
-    const int64_t max_chunks = (vectors + kGroupChunk - 1) / kGroupChunk + e + 1;
-    return (size_t)(((vectors + 1 + 3) & ~(int64_t)3) + 4 * max_chunks) * 4;
+    return (vectors + chunk - 1) / chunk + e + 1;
 }
 
-int64_t gather_group_max_chunks(int64_t vectors, int64_t e)
+size_t gather_group_ws_bytes(int64_t vectors, int64_t e, int chunk)
 {
-    return (vectors + kGroupChunk - 1) / kGroupChunk + e + 1;
+    return (size_t)(((vectors + 1 + 3) & ~(int64_t)3) + 4 * gather_group_max_chunks(vectors, e, chunk)) * 4;
 }
 
-hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, void *ws,
-                                hipStream_t stream)
+hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, int chunk,
+                                void *ws, hipStream_t stream)
 {
     const size_t lds = (size_t)(2 * (e + 1) + 2 * kGroupThreads + 2) * 4;
     gather_group_kernel<<<1, kGroupThreads, lds, stream>>>(ids, rows, l, (int)e,
-                                                           static_cast<uint32_t *>(ws), rows * l);
+                                                           static_cast<uint32_t *>(ws), rows * l,
+                                                           (uint32_t)chunk);
     return hipGetLastError();
 }
 

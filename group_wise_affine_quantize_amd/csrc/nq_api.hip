@@ -369,37 +369,35 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
 }
 
 namespace {
-// The grouped gather ("Mixture of experts" section): worth it once experts
-// are shared by several vectors.  A pure function of the sizes; it never
-// changes a row's bits (the matrix-vector family's rows do not depend on
-// how many rows share a launch chunk).
-bool gather_grouped(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n)
+// Gather routes ("Mixture of experts" section).  Once experts are shared by
+// several vectors (at least 16 vectors, 4 per expert on average) the
+// vectors are grouped by expert on the device and each expert's weights are
+// read once per chunk: by the matrix-core kernel (bf16 x, K a multiple of
+// 64; rows within the product tolerance), or in row-exact mode by the
+// matrix-vector family, whose rows never depend on how many rows share a
+// chunk.  Otherwise every row runs as its own matrix-vector product.  Pure
+// functions of the sizes, dtypes and mode.
+bool gather_shared(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n)
 {
     const int64_t v = rows * l;
     return k > 0 && n > 0 && rows > 0 && l > 0 && e > 0 && e <= 4096 && v >= 16 && v >= 4 * e &&
-           v < ((int64_t)1 << 31) && nqk::gather_group_max_chunks(v, e) <= 65535;
-}
-}  // namespace
-
-size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n,
-                                     int32_t group_size, int32_t bits, nq_dtype x_dt,
-                                     nq_dtype sb_dt, int32_t sorted_hint)
-{
-    (void)group_size, (void)bits, (void)x_dt, (void)sb_dt, (void)sorted_hint;
-    if (rows < 0 || l < 0 || e < 0 || k < 0 || n < 0) return 0;
-    if (!gather_grouped(rows, l, k, e, n)) return 0;
-    return nqk::gather_group_ws_bytes(rows * l, e);
+           v < ((int64_t)1 << 31) && nqk::gather_group_max_chunks(v, e, nqk::kGroupChunk) <= 65535;
 }
 
-nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
-                        const uint32_t *codes, const void *scales, const void *biases,
-                        nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
-                        const uint32_t *rhs_idx, int32_t sorted_hint, void *y, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream)
+bool gather_mfma(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n, int x_dt, int bits,
+                 int row_exact)
 {
-    const char *op = "nq_gather_qmm";
+    return !row_exact && x_dt == NQ_BF16 && (bits == 4 || bits == 8) && k % 64 == 0 &&
+           gather_shared(rows, l, k, e, n);
+}
+
+nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_dt, int64_t rows,
+                      int64_t l, int64_t k, const uint32_t *codes, const void *scales,
+                      const void *biases, nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size,
+                      int32_t bits, const uint32_t *rhs_idx, void *y, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
     g_last_error.clear();
-    (void)sorted_hint, (void)workspace, (void)workspace_bytes;
     if (!dtype_ok(x_dt) || !dtype_ok(sb_dt))
         return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, sb_dt=%d)", op, (int)x_dt, (int)sb_dt);
     nq_status st = check_quant(op, group_size, bits, true);
@@ -432,9 +430,11 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
     for (int i = 0; i < 5; ++i)
         if (overlap(sy, ins[i])) return fail(NQ_ERR_ALIAS, "%s: y overlaps %s", op, names[i]);
 
-    const bool grouped = gather_grouped(rows, l, k, e, n);
-    if (grouped) {
-        const size_t need = nqk::gather_group_ws_bytes(rows * l, e);
+    const bool shared = gather_shared(rows, l, k, e, n);
+    const bool mfma = gather_mfma(rows, l, k, e, n, x_dt, bits, row_exact);
+    const int64_t v = rows * l;
+    if (shared) {
+        const size_t need = nqk::gather_group_ws_bytes(v, e, nqk::kGroupChunk);
         if (!workspace || workspace_bytes < need)
             return fail(NQ_ERR_WORKSPACE, "%s: the grouped route needs a workspace of %zu bytes (got %zu)",
                         op, need, workspace ? workspace_bytes : (size_t)0);
@@ -443,6 +443,31 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
         if (overlap(sw, sy)) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps y", op);
         for (int i = 0; i < 5; ++i)
             if (overlap(sw, ins[i])) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps %s", op, names[i]);
+    }
+    uint32_t *ws = static_cast<uint32_t *>(workspace);
+    const int chunk = mfma ? nqk::kGroupChunkMfma : nqk::kGroupChunk;
+    if (shared) {
+        if (hipError_t err = nqk::launch_gather_groups(rhs_idx, rows, l, e, chunk, workspace, stream))
+            return check_launch(op, err);
+    }
+    if (mfma) {
+        nqk::GatherMfmaLaunch g;
+        g.x = x;
+        g.y = y;
+        g.codes = codes;
+        g.scales = scales;
+        g.biases = biases;
+        g.perm = ws;
+        g.nchunks = ws + v;
+        g.chunks = ws + ((v + 1 + 3) & ~(int64_t)3);
+        g.sb_dt = sb_dt;
+        g.n = n;
+        g.k = k;
+        g.e = e;
+        g.max_chunks = nqk::gather_group_max_chunks(v, e, chunk);
+        g.gs = group_size;
+        g.bits = bits;
+        return check_launch(op, nqk::launch_gather_mfma(g, stream));
     }
 
     nqk::GemvLaunch g;
@@ -463,20 +488,51 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
     g.bits = bits;
     g.ksplit = gemv_ksplit(n, k);   // the plan nq_qmm_row_exact takes
     g.rows_per_wave = 0;
-    if (grouped) {
-        if (hipError_t err = nqk::launch_gather_groups(rhs_idx, rows, l, e, workspace, stream))
-            return check_launch(op, err);
-        const int64_t v = rows * l;
-        uint32_t *ws = static_cast<uint32_t *>(workspace);
+    if (shared) {
         g.idx = nullptr;
         g.perm = ws;
         g.nchunks = ws + v;
         g.chunks = ws + ((v + 1 + 3) & ~(int64_t)3);
-        g.max_chunks = nqk::gather_group_max_chunks(v, e);
+        g.max_chunks = nqk::gather_group_max_chunks(v, e, chunk);
         g.items = 1;
         g.rows_per_item = nqk::kGroupChunk;   // chunks of up to 8 vectors
     }
     return check_launch(op, nqk::launch_gemv(g, stream));
+}
+}  // namespace
+
+size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n,
+                                     int32_t group_size, int32_t bits, nq_dtype x_dt,
+                                     nq_dtype sb_dt, int32_t sorted_hint)
+{
+    (void)group_size, (void)bits, (void)x_dt, (void)sb_dt, (void)sorted_hint;
+    if (rows < 0 || l < 0 || e < 0 || k < 0 || n < 0) return 0;
+    if (!gather_shared(rows, l, k, e, n)) return 0;
+    // enough for either grouped route (the matrix-vector one has more chunks)
+    return nqk::gather_group_ws_bytes(rows * l, e, nqk::kGroupChunk);
+}
+
+nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                        const uint32_t *codes, const void *scales, const void *biases,
+                        nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                        const uint32_t *rhs_idx, int32_t sorted_hint, void *y, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    (void)sorted_hint;
+    return gather_impl("nq_gather_qmm", 0, x, x_dt, rows, l, k, codes, scales, biases, sb_dt, e, n,
+                       group_size, bits, rhs_idx, y, workspace, workspace_bytes, stream);
+}
+
+nq_status nq_gather_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                                  const uint32_t *codes, const void *scales, const void *biases,
+                                  nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size,
+                                  int32_t bits, const uint32_t *rhs_idx, int32_t sorted_hint,
+                                  void *y, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream)
+{
+    (void)sorted_hint;
+    return gather_impl("nq_gather_qmm_row_exact", 1, x, x_dt, rows, l, k, codes, scales, biases,
+                       sb_dt, e, n, group_size, bits, rhs_idx, y, workspace, workspace_bytes, stream);
 }
 
 const char *nq_status_string(nq_status s)

@@ -49,17 +49,34 @@ struct GemvLaunch {
 };
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 
-// Vectors per chunk of the grouped gather (the matrix-vector family's
-// largest row count per launch chunk).
+// Vectors per chunk of the grouped matrix-vector gather (that family's
+// largest row count per launch chunk) and of the grouped matrix-core gather.
 constexpr int kGroupChunk = 8;
+constexpr int kGroupChunkMfma = 32;
 // Workspace of the grouping pass over `vectors` activation vectors and e
-// experts, and the chunk-table bound it implies.
-size_t gather_group_ws_bytes(int64_t vectors, int64_t e);
-int64_t gather_group_max_chunks(int64_t vectors, int64_t e);
+// experts cut into chunks of `chunk`, and the chunk-table bound it implies.
+size_t gather_group_ws_bytes(int64_t vectors, int64_t e, int chunk);
+int64_t gather_group_max_chunks(int64_t vectors, int64_t e, int chunk);
 // Groups the vectors r * l + j by expert ids[r] (one workgroup): perm,
 // chunk count and chunk table into ws (layout in gemv.hip).
-hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, void *ws,
-                                hipStream_t stream);
+hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, int chunk,
+                                void *ws, hipStream_t stream);
+
+// Grouped matrix-core gather: chunk c of the table multiplies its (up to 32)
+// bf16 activation vectors perm[first ..] by expert `bucket`'s weights (K a
+// multiple of 64; bucket >= e: zero rows).
+struct GatherMfmaLaunch {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const void *scales;
+    const void *biases;
+    const uint32_t *perm, *chunks, *nchunks;
+    int sb_dt;
+    int64_t n, k, e, max_chunks;
+    int gs, bits;
+};
+hipError_t launch_gather_mfma(const GatherMfmaLaunch &a, hipStream_t stream);
 
 // Tiled bf16-MFMA product: y[m, n] = x[m, k] . w_hat[n, k]^T, x and y bf16.
 struct TiledLaunch {

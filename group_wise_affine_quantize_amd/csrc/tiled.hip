@@ -546,6 +546,177 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
     }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped matrix-core gather ("Mixture of experts" section: a grouped kernel
+// reads each expert's weights once for the rows that chose it).  A
+// workgroup computes a 32 x 32 tile of y (its four waves take a quarter of
+// K each; the partial tiles are added in LDS in wave order): the up to 32 activation
+// vectors of one chunk (all of one expert, gathered through perm) against 32
+// weight rows of that expert, with v_mfma_f32_32x32x16_bf16 over K blocks
+// of 64.  Lane (c = l % 32, h = l / 32) loads, per K block, the 32
+// activations k = 32 h .. 32 h + 31 of vector c (A operand rows) and the 32
+// codes of weight row c at the same k (B operand columns, dequantized in
+// registers as round_bf16(fmaf(s, q, b))); k16 step j uses k = 32 h + 8 j
+// .. + 8 on both sides.  Operands of block kb + 1 are loaded while block kb
+// runs, into the other register set (no register is rewritten while an
+// MFMA that reads it may still be queued).
+
+template <typename ST>
+struct GatherParams {
+    const bf16_bits *x;
+    bf16_bits *y;
+    const uint32_t *codes;
+    const ST *scales;
+    const ST *biases;
+    const uint32_t *perm;
+    const uint4 *chunks;
+    const uint32_t *nchunks;
+    int64_t n, k, e, words_per_row, groups_per_row;
+    int lg_gs;
+};
+
+constexpr int kGatherWaves = 4;   // K is split over the waves of a workgroup
+constexpr int kGatherCols = 1;    // 32-column blocks per workgroup (sharing the activations)
+
+template <int BITS, typename ST>
+__global__ void __launch_bounds__(64 * kGatherWaves) gather_mfma_kernel(GatherParams<ST> p)
+{
+    if (blockIdx.y >= *p.nchunks) return;   // uniform over the workgroup
+    const uint4 ch = p.chunks[blockIdx.y];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 31, h = lane >> 5;
+    const int count = (int)ch.z;
+    const int64_t n0 = (int64_t)blockIdx.x * 32 * kGatherCols;
+    // this lane's activation vector (A row) and weight rows (B columns),
+    // clamped into range; results past count / n are not stored
+    const int64_t vec = p.perm[ch.y + min(c, count - 1)];
+    const bf16_bits *xrow = p.x + vec * p.k + 32 * h;
+    const bool live = (int64_t)ch.x < p.e;
+    // wave w takes the K blocks [kb0, kb1)
+    const int nk = (int)(p.k / kBK2);
+    const int kb0 = (int)((int64_t)nk * wave / kGatherWaves);
+    const int kb1 = (int)((int64_t)nk * (wave + 1) / kGatherWaves);
+    f32x16_t acc[kGatherCols];
+#pragma unroll
+    for (int cb = 0; cb < kGatherCols; ++cb) acc[cb] = f32x16_t{};
+    if (live && kb0 < kb1) {
+        const int64_t slab = ch.x;
+        const uint32_t *crow[kGatherCols];
+        const ST *srow[kGatherCols];
+        const ST *brow[kGatherCols];
+#pragma unroll
+        for (int cb = 0; cb < kGatherCols; ++cb) {
+            const int64_t wr = min(n0 + cb * 32 + c, p.n - 1);
+            crow[cb] = p.codes + (slab * p.n + wr) * p.words_per_row + 32 * h * BITS / 32;
+            srow[cb] = p.scales + (slab * p.n + wr) * p.groups_per_row;
+            brow[cb] = p.biases + (slab * p.n + wr) * p.groups_per_row;
+        }
+        uint4 xa[2][4];
+        CodeRegs<BITS> cw[2][kGatherCols];
+        auto load = [&](int kb, int par) {
+            const uint4 *xs = reinterpret_cast<const uint4 *>(xrow + (int64_t)kb * kBK2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xa[par][j] = xs[j];
+            const int64_t g = ((int64_t)kb * kBK2 + 32 * h) >> p.lg_gs;
+#pragma unroll
+            for (int cb = 0; cb < kGatherCols; ++cb) {
+                const uint4 *cs = reinterpret_cast<const uint4 *>(crow[cb] + (int64_t)kb * 2 * BITS);
+#pragma unroll
+                for (int i = 0; i < BITS / 4; ++i) cw[par][cb].w[i] = cs[i];
+                if constexpr (sizeof(ST) == 2) {
+                    cw[par][cb].s = srow[cb][g];
+                    cw[par][cb].b = brow[cb][g];
+                } else {
+                    cw[par][cb].s = __float_as_uint(srow[cb][g]);
+                    cw[par][cb].b = __float_as_uint(brow[cb][g]);
+                }
+            }
+        };
+        auto compute = [&](int par) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int cb = 0; cb < kGatherCols; ++cb) {
+                    const bf16x8_t bv = dequant_step<BITS, ST>(cw[par][cb], j);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, xa[par][j]), bv, acc[cb], 0, 0, 0);
+                }
+        };
+        load(kb0, 0);
+        int kb = kb0;
+        for (; kb + 1 < kb1; kb += 2) {
+            load(kb + 1, 1);
+            compute(0);
+            if (kb + 2 < kb1) load(kb + 2, 0);
+            compute(1);
+        }
+        if (kb < kb1) compute(0);
+    }
+    // the waves' partial tiles are added in wave order
+    __shared__ f32x16_t part[kGatherWaves - 1][kGatherCols][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int cb = 0; cb < kGatherCols; ++cb) part[wave - 1][cb][lane] = acc[cb];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kGatherWaves - 1; ++w)
+#pragma unroll
+        for (int cb = 0; cb < kGatherCols; ++cb) acc[cb] += part[w][cb][lane];
+    // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
+#pragma unroll
+    for (int cb = 0; cb < kGatherCols; ++cb) {
+        const int64_t col = n0 + cb * 32 + c;
+        if (col < p.n) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+                if (r < count) {
+                    const int64_t yv = p.perm[ch.y + r];
+                    p.y[yv * p.n + col] = (bf16_bits)(pack_bf16(acc[cb][v], 0.0f) & 0xffffu);
+                }
+            }
+        }
+    }
+}
+
+template <int BITS, typename ST>
+hipError_t gather_mfma_run(const GatherMfmaLaunch &a, hipStream_t stream)
+{
+    GatherParams<ST> p;
+    p.x = static_cast<const bf16_bits *>(a.x);
+    p.y = static_cast<bf16_bits *>(a.y);
+    p.codes = a.codes;
+    p.scales = static_cast<const ST *>(a.scales);
+    p.biases = static_cast<const ST *>(a.biases);
+    p.perm = a.perm;
+    p.chunks = reinterpret_cast<const uint4 *>(a.chunks);
+    p.nchunks = a.nchunks;
+    p.n = a.n;
+    p.k = a.k;
+    p.e = a.e;
+    p.words_per_row = a.k * BITS / 32;
+    p.groups_per_row = a.k / a.gs;
+    p.lg_gs = a.gs == 32 ? 5 : a.gs == 64 ? 6 : 7;
+    if (a.k % kBK2 != 0 || a.max_chunks > 65535) return hipErrorInvalidValue;
+    const unsigned gx = (unsigned)((a.n + 32 * kGatherCols - 1) / (32 * kGatherCols));
+    gather_mfma_kernel<BITS, ST><<<dim3(gx, (unsigned)a.max_chunks), dim3(64 * kGatherWaves), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_mfma(const GatherMfmaLaunch &a, hipStream_t stream)
+{
+    if (a.bits != 4 && a.bits != 8) return hipErrorInvalidValue;
+    if (a.sb_dt == DT_F32) {
+        if (a.bits == 4) return gather_mfma_run<4, float>(a, stream);
+        return gather_mfma_run<8, float>(a, stream);
+    }
+    if (a.bits == 4) return gather_mfma_run<4, bf16_bits>(a, stream);
+    return gather_mfma_run<8, bf16_bits>(a, stream);
+}
+
 bool tiled_fits(int tile_m, int tile_n, int bits, int gs, int sb_dt, int64_t m, int64_t n, int64_t k)
 {
     if (!tiled_supported(tile_m, tile_n, bits)) return false;

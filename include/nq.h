@@ -171,7 +171,12 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
 
 /* ---------------------------------------------------------------- mixture of experts */
 
-/* Workspace bytes nq_gather_qmm needs for these arguments. */
+/* Workspace bytes nq_gather_qmm and nq_gather_qmm_row_exact need for these
+ * arguments: nonzero once experts are shared by several vectors (rows * l
+ * >= 16 and >= 4 * e, e <= 4096), when the vectors are grouped by expert on
+ * the device and each expert's weights are read once per chunk of vectors.
+ * The workspace holds that grouping (a permutation of the vectors and a
+ * chunk table) and is fully rewritten by every call. */
 size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n,
                                      int32_t group_size, int32_t bits, nq_dtype x_dt,
                                      nq_dtype sb_dt, int32_t sorted_hint);
@@ -181,15 +186,32 @@ size_t nq_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t
  * rhs_idx [rows] uint32 (the expert of each row).  y [rows, l, n] (x_dt):
  * y[r, j, :] = x[r, j, :] times the transposed weights of expert rhs_idx[r].
  * Weights are indexed in place, never copied.  An id >= e gives an all-zero
- * row of y (the id is never used to address memory).  sorted_hint = 1 says
- * the ids are non-decreasing; it may change the kernel, never the result:
- * every row is bit-equal to nq_qmm_row_exact of x[r] with expert
- * rhs_idx[r]'s weights (and so to nq_qmm of it when l <= 8). */
+ * row of y (the id is never used to address memory).  The ids need not be
+ * sorted; sorted_hint is accepted and changes nothing.  The route is a pure
+ * function of the sizes and dtypes: with a nonzero workspace size (see
+ * above), bf16 x and k a multiple of 64, vectors are grouped by expert into
+ * chunks of up to 32 and multiplied on the matrix cores (rows within the
+ * product tolerance of the exact result, like nq_qmm's tiled rows);
+ * otherwise every row is bit-equal to nq_qmm_row_exact of x[r] with expert
+ * rhs_idx[r]'s weights.  NQ_ERR_WORKSPACE if the workspace is needed and
+ * missing or short; it must not overlap any argument. */
 nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
                         const uint32_t *codes, const void *scales, const void *biases,
                         nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
                         const uint32_t *rhs_idx, int32_t sorted_hint, void *y, void *workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* As nq_gather_qmm in row-exact mode ("Products on the GPU" section; nuvec
+ * API index, with_row_exact): every row of y is bit-equal to
+ * nq_qmm_row_exact of x[r] with expert rhs_idx[r]'s weights, whatever the
+ * ids.  Grouped vectors (same workspace rule) run as chunks of up to 8
+ * through the matrix-vector family, whose rows never depend on the chunk. */
+nq_status nq_gather_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                                  const uint32_t *codes, const void *scales, const void *biases,
+                                  nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size,
+                                  int32_t bits, const uint32_t *rhs_idx, int32_t sorted_hint,
+                                  void *y, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------- errors */
 

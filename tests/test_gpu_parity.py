@@ -204,10 +204,15 @@ def test_gather_parity(x_dtype, w_dtype, l):
     c, s, b = O.quantize(w, gs, bits)
     xs, cs, ss, bs = dev(x), dev(c), dev(s), dev(b)
     idx = dev(ids)
-    y = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, idx)
     y_ref = O.gather_qmm_f64(x, c, s, b, gs, bits, ids)
-    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "gather")
+    # the default entry (grouped on the matrix cores for bf16 x): tolerance
+    yd = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, idx)
+    assert_rows_close(values(host(yd)), y_ref, tolerance(yd.dtype), "gather")
+    # row-exact mode: every row bit-equal to its one-row product
+    y = B.nq_gather_qmm_row_exact(xs, cs, ss, bs, gs, bits, idx)
+    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "gather row-exact")
     yh = host(y)
+    assert np.all(values(host(yd))[ids >= e] == 0)
     for r in range(rows):
         if ids[r] >= e:
             assert np.all(values(yh[r]) == 0)
@@ -242,19 +247,38 @@ def test_gather_grouped(case):
     _, x = synthetic.random_case(rows, (1, 1), (rows, l, k), 1.0, "f32", "bf16")
     c, s, b = O.quantize(w, gs, bits)
     xs, cs, ss, bs = dev(x), dev(c), dev(s), dev(b)
-    y = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids), sorted_hint=case == "sorted_many")
-    assert_rows_close(values(host(y)).reshape(rows * l, n),
-                      O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows * l, n), 1e-2,
-                      "grouped gather")
+    y_ref = O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows * l, n)
+    hint = case == "sorted_many"
+    yd = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids), sorted_hint=hint)   # matrix cores
+    assert_rows_close(values(host(yd)).reshape(rows * l, n), y_ref, 1e-2, "grouped gather")
+    y = B.nq_gather_qmm_row_exact(xs, cs, ss, bs, gs, bits, dev(ids), sorted_hint=hint)
+    assert_rows_close(values(host(y)).reshape(rows * l, n), y_ref, 1e-2, "grouped row-exact")
     for r in range(0, rows, max(1, rows // 12)):
         if ids[r] >= e:
-            assert np.all(values(host(y[r])) == 0)
+            assert np.all(values(host(y[r])) == 0) and np.all(values(host(yd[r])) == 0)
             continue
         yr = B.nq_qmm_row_exact(xs[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
         assert bits_equal(yr, y[r]), r
-    # the same call twice gives the same bits
-    y2 = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids))
-    assert bits_equal(y, y2)
+    # the same call twice gives the same bits, on either route
+    assert bits_equal(y, B.nq_gather_qmm_row_exact(xs, cs, ss, bs, gs, bits, dev(ids)))
+    assert bits_equal(yd, B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids)))
+
+
+@pytest.mark.parametrize("bits,gs,w_dtype", [(4, 32, "bf16"), (8, 128, "bf16"), (4, 64, "f32"),
+                                             (8, 64, "f32")])
+def test_gather_mfma_modes(bits, gs, w_dtype):
+    """The grouped matrix-core gather over bit widths, group sizes and scale
+    dtypes, with a ragged n and expert sizes above and below one chunk."""
+    e, n, k, rows = 6, 72, 512, 150
+    rng = np.random.default_rng(bits + gs)
+    ids = rng.integers(0, e, size=rows, dtype=np.uint32)
+    ids[:45] = 2                                   # one expert with two chunks of 32
+    w, _ = synthetic.random_case(bits, (e, n, k), (1, k), 0.02, w_dtype)
+    _, x = synthetic.random_case(gs, (1, 1), (rows, 1, k), 1.0, "f32", "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    y = B.nq_gather_qmm(dev(x), dev(c), dev(s), dev(b), gs, bits, dev(ids))
+    assert_rows_close(values(host(y)).reshape(rows, n),
+                      O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows, n), 1e-2, "mfma gather")
 
 
 def test_gather_sorted_hint_same_bits():

@@ -134,10 +134,12 @@ def test_moe_gather():
     wl = d["wl"]
     c, s, b = quantize_on_gpu_and_check(d)
     xs, ids = dev(d["x"]), dev(d["ids"])
-    y = B.nq_gather_qmm(xs, c, s, b, wl.group_size, wl.bits, ids)
-    assert y.shape == (512, 1, 1408) and y.dtype == torch.bfloat16
     y_ref = O.gather_qmm_f64(d["x"], *d["q"], wl.group_size, wl.bits, d["ids"])
-    assert_rows_close(values(host(y)), y_ref, 1e-2, "gather")
+    yd = B.nq_gather_qmm(xs, c, s, b, wl.group_size, wl.bits, ids)     # matrix cores
+    assert yd.shape == (512, 1, 1408) and yd.dtype == torch.bfloat16
+    assert_rows_close(values(host(yd)), y_ref, 1e-2, "gather")
+    y = B.nq_gather_qmm_row_exact(xs, c, s, b, wl.group_size, wl.bits, ids)
+    assert_rows_close(values(host(y)), y_ref, 1e-2, "gather row-exact")
     outs = [B.nq_qmm(xs[r], c[e], s[e], b[e], wl.group_size, wl.bits)
             for r, e in enumerate(d["ids"].tolist())]
     torch.cuda.synchronize()
