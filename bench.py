@@ -336,6 +336,28 @@ def main():
             {"workload": "x f32 [4,512] . W[256,512]^T 4-bit g64 f32 scales (launch-bound)"})
     out["rows"] = rows
 
+    # ---------------------------------------------------------------- measured ceilings
+    # Context only (no product code): what this GPU's library paths reach on
+    # the same data sizes -- a 1 GiB device copy (HBM read + write) and a
+    # dense bf16 matmul (hipBLASLt through torch) of the prefill shape with
+    # the weights already dequantized.
+    if not args.no_rows:
+        log("timing the context ceilings")
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        t = timer.run(lambda i: dst.copy_(src), 20, 3, chunk=10)
+        copy_gbs = 2 * src.numel() / (t / 20) / 1e9
+        del src, dst
+        w_hat = B.nq_dequantize(*q2, 64, 4)
+        yd = torch.empty((2048, 14336), dtype=torch.bfloat16, device="cuda")
+        t = timer.run(lambda i: torch.matmul(x4, w_hat.t(), out=yd), 20, 3, chunk=10)
+        out["context"] = {
+            "hbm_copy_1GiB_GBs": round(copy_gbs, 1),
+            "dense_bf16_matmul_prefill_shape_TFLOPs": round(flops / (t / 20) / 1e12, 1),
+            "note": "torch copy_ and torch.matmul (hipBLASLt) on the same GPU; not the product path",
+        }
+        del w_hat, yd
+
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
