@@ -608,6 +608,121 @@ gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_
     }
 }
 
+// The same grouping for up to kGroupSmallBuckets buckets (e < 256): each
+// wave ranks its 64 vectors by bucket with ballots (one pass per distinct
+// bucket in the wave), per-wave counts go to a [wave][bucket] table whose
+// prefix over the waves gives every vector's position; one wave scans the
+// bucket sizes with shuffles.  Same stable order, same table.
+constexpr int kGroupSmallBuckets = 256;
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+__global__ void __launch_bounds__(kGroupThreads)
+gather_group_small_kernel(const uint32_t *ids, int64_t l, int e, uint32_t *ws, int64_t v_total, uint32_t chunk)
+{
+    __shared__ uint32_t wc[kGroupWaves][kGroupSmallBuckets];   // per-wave counts, then positions
+    __shared__ uint32_t hist[kGroupSmallBuckets];
+    __shared__ uint32_t start[kGroupSmallBuckets];              // next position of each bucket
+    __shared__ uint32_t coff[kGroupSmallBuckets + 1];           // first chunk of each bucket
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int nb = e + 1;
+    uint32_t *perm = ws, *nchunks = ws + v_total;
+    uint4 *table = reinterpret_cast<uint4 *>(ws + ((v_total + 1 + 3) & ~(int64_t)3));
+    const uint64_t lanes_below = (lane ? ~0ull >> (64 - lane) : 0ull);
+    auto bucket = [&](int64_t v) -> uint32_t {
+        return v < v_total ? min(ids[v / l], (uint32_t)e) : 0xffffffffu;
+    };
+    // For every distinct bucket among this wave's valid lanes (in lane
+    // order of first appearance): fn(bucket, lanes holding it).
+    auto match = [&](uint32_t b, auto fn) {
+        uint64_t active = __ballot(b != 0xffffffffu);
+        while (active) {
+            const int leader = __ffsll((long long)active) - 1;
+            const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)b, leader);
+            const uint64_t m = __ballot(b == lb) & active;
+            fn(lb, m, leader);
+            active &= ~m;
+        }
+    };
+
+    for (int b = t; b < nb; b += kGroupThreads) hist[b] = 0;
+    __syncthreads();
+    for (int64_t v0 = 0; v0 < v_total; v0 += kGroupThreads) {
+        const uint32_t b = bucket(v0 + t);
+        match(b, [&](uint32_t lb, uint64_t m, int leader) {
+            if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+        });
+    }
+    __syncthreads();
+    if (w == 0) {
+        // exclusive scans of the bucket sizes and chunk counts; lane i holds
+        // buckets 4 i .. 4 i + 3
+        uint32_t h[4], cn[4], sh = 0, sc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * lane + j;
+            h[j] = b < nb ? hist[b] : 0u;
+            cn[j] = (h[j] + chunk - 1) / chunk;
+            sh += h[j];
+            sc += cn[j];
+        }
+        uint32_t ih = sh, ic = sc;   // inclusive over lanes
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t a = __shfl_up(ih, off), c2 = __shfl_up(ic, off);
+            if (lane >= off) ih += a, ic += c2;
+        }
+        uint32_t ph = ih - sh, pc = ic - sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * lane + j;
+            if (b < nb) start[b] = ph, coff[b] = pc;
+            ph += h[j];
+            pc += cn[j];
+        }
+        if (lane == 63) {
+            coff[nb] = ic;
+            *nchunks = ic;
+        }
+    }
+    __syncthreads();
+    // chunk table: entry j belongs to the last bucket whose first chunk is <= j
+    const uint32_t total = coff[nb];
+    for (uint32_t j = t; j < total; j += kGroupThreads) {
+        int lo = 0, hi = nb;   // coff[lo] <= j < coff[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (coff[mid] <= j) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t i = j - coff[lo];
+        table[j] = make_uint4((uint32_t)lo, start[lo] + i * chunk, min(chunk, hist[lo] - i * chunk), 0u);
+    }
+    __syncthreads();
+    // stable placement, kGroupThreads vectors a round
+    for (int64_t v0 = 0; v0 < v_total; v0 += kGroupThreads) {
+        for (int i = t; i < kGroupWaves * kGroupSmallBuckets; i += kGroupThreads) (&wc[0][0])[i] = 0;
+        __syncthreads();
+        const uint32_t b = bucket(v0 + t);
+        uint32_t rank = 0;
+        match(b, [&](uint32_t lb, uint64_t m, int leader) {
+            if (b == lb) rank = (uint32_t)__popcll(m & lanes_below);
+            if (lane == leader) wc[w][lb] = (uint32_t)__popcll(m);
+        });
+        __syncthreads();
+        for (int bb = t; bb < nb; bb += kGroupThreads) {
+            uint32_t run = start[bb];
+            for (int w2 = 0; w2 < kGroupWaves; ++w2) {
+                const uint32_t cnt = wc[w2][bb];
+                wc[w2][bb] = run;
+                run += cnt;
+            }
+            start[bb] = run;
+        }
+        __syncthreads();
+        if (b != 0xffffffffu) perm[wc[w][b] + rank] = (uint32_t)(v0 + t);
+        __syncthreads();
+    }
+}
+
 int64_t gather_group_max_chunks(int64_t vectors, int64_t e, int chunk)
 {
     return (vectors + chunk - 1) / chunk + e + 1;
@@ -621,6 +736,11 @@ size_t gather_group_ws_bytes(int64_t vectors, int64_t e, int chunk)
 hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, int chunk,
                                 void *ws, hipStream_t stream)
 {
+    if (e + 1 <= kGroupSmallBuckets) {
+        gather_group_small_kernel<<<1, kGroupThreads, 0, stream>>>(ids, l, (int)e, static_cast<uint32_t *>(ws),
+                                                                   rows * l, (uint32_t)chunk);
+        return hipGetLastError();
+    }
     const size_t lds = (size_t)(2 * (e + 1) + 2 * kGroupThreads + 2) * 4;
     gather_group_kernel<<<1, kGroupThreads, lds, stream>>>(ids, rows, l, (int)e,
                                                            static_cast<uint32_t *>(ws), rows * l,

@@ -446,7 +446,9 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     }
     uint32_t *ws = static_cast<uint32_t *>(workspace);
     const int chunk = mfma ? nqk::kGroupChunkMfma : nqk::kGroupChunk;
-    if (shared) {
+    // the matrix-core route groups small id sets inside its own workgroups
+    const bool self_group = mfma && nqk::gather_self_group_fits(v, e);
+    if (shared && !self_group) {
         if (hipError_t err = nqk::launch_gather_groups(rhs_idx, rows, l, e, chunk, workspace, stream))
             return check_launch(op, err);
     }
@@ -460,13 +462,17 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
         g.perm = ws;
         g.nchunks = ws + v;
         g.chunks = ws + ((v + 1 + 3) & ~(int64_t)3);
+        g.ids = rhs_idx;
         g.sb_dt = sb_dt;
         g.n = n;
         g.k = k;
         g.e = e;
         g.max_chunks = nqk::gather_group_max_chunks(v, e, chunk);
+        g.l = l;
+        g.v_total = v;
         g.gs = group_size;
         g.bits = bits;
+        g.self_group = self_group;
         return check_launch(op, nqk::launch_gather_mfma(g, stream));
     }
 

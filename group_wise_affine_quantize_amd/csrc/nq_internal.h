@@ -71,11 +71,16 @@ struct GatherMfmaLaunch {
     const uint32_t *codes;
     const void *scales;
     const void *biases;
-    const uint32_t *perm, *chunks, *nchunks;
+    const uint32_t *perm, *chunks, *nchunks;   // grouping tables (unless self_group)
+    const uint32_t *ids;                       // expert ids (self_group)
     int sb_dt;
-    int64_t n, k, e, max_chunks;
+    int64_t n, k, e, max_chunks, l, v_total;
     int gs, bits;
+    bool self_group;   // each workgroup groups the ids itself (gather_self_group_fits)
 };
+// Whether the matrix-core gather can group the vector ids by itself in
+// every workgroup: few experts and few vectors.
+inline bool gather_self_group_fits(int64_t vectors, int64_t e) { return e < 256 && vectors <= 2048; }
 hipError_t launch_gather_mfma(const GatherMfmaLaunch &a, hipStream_t stream);
 
 // Tiled bf16-MFMA product: y[m, n] = x[m, k] . w_hat[n, k]^T, x and y bf16.

@@ -550,17 +550,43 @@ __global__ void __launch_bounds__(256) tiled256_kernel(TiledParams<ST> p, int ti
 // ---------------------------------------------------------------------------
 // Grouped matrix-core gather ("Mixture of experts" section: a grouped kernel
 // reads each expert's weights once for the rows that chose it).  A
-// workgroup computes a 32 x 32 tile of y (its four waves take a quarter of
-// K each; the partial tiles are added in LDS in wave order): the up to 32 activation
-// vectors of one chunk (all of one expert, gathered through perm) against 32
-// weight rows of that expert, with v_mfma_f32_32x32x16_bf16 over K blocks
-// of 64.  Lane (c = l % 32, h = l / 32) loads, per K block, the 32
-// activations k = 32 h .. 32 h + 31 of vector c (A operand rows) and the 32
-// codes of weight row c at the same k (B operand columns, dequantized in
-// registers as round_bf16(fmaf(s, q, b))); k16 step j uses k = 32 h + 8 j
-// .. + 8 on both sides.  Operands of block kb + 1 are loaded while block kb
-// runs, into the other register set (no register is rewritten while an
-// MFMA that reads it may still be queued).
+// workgroup computes a 32 x (32 CB) tile of y: the up to 32 activation
+// vectors of one chunk (all of one expert, gathered through perm) against
+// 32 CB weight rows of that expert.  Its CB x KS waves form KS groups that
+// take consecutive equal ranges of K blocks (64 wide); in a group, wave w
+// owns 32 weight rows.  Each wave runs v_mfma_f32_32x32x16_bf16 over its K
+// blocks, and the groups' partial tiles are added in LDS in group order.
+// Many small workgroups of equal work keep every SIMD equally loaded.
+//
+// Activations: each K block of the chunk (32 rows x 128 bytes) goes global
+// -> LDS with direct-to-LDS loads (8 lanes per 128-byte row segment; the CB
+// waves of a group share the loading) into a ring of D LDS arrays per group,
+// and the group's waves read their A operands from there.  Row r's 16-byte
+// chunk q sits in slot q ^ ((r / 2) % 8), so the operand reads (16 lanes =
+// rows c .. c + 15 of one chunk column) cover all 64 banks once.
+// Weights: lane (c = l % 32, h = l / 32) loads the 32 codes of weight row c
+// at k = 32 h .. 32 h + 31 of the block into a ring of D register sets, and
+// dequantizes them into B operands as round_bf16(fmaf(s, q, b)); k16 step j
+// takes k = 32 h + 8 j .. + 8 on both sides.  Scales and biases come in
+// stages of 8 groups per row: one direct-to-LDS load per 16 bytes of a
+// row's run (lanes 0-31 scales, 32-63 biases of the wave's 32 rows) into a
+// wave-private two-stage LDS ring, one stage ahead; each block reads its
+// group's pair from there.  (One scale and one bias load per lane and block
+// would touch 16 cache lines each for 2 bytes a lane; those narrow loads
+// cost more than all the rest of the traffic.)  Where the ring does not
+// fit (scales or biases not 16-byte aligned, or a K range that is not a
+// whole number of stages) each block loads its own pair with its codes:
+// the same values, so the same results.
+//
+// Schedule of block kb (ring index kb % D): wait until this wave's LDS loads
+// of block kb have landed; barrier over the workgroup when CB > 1 (then all
+// 32 rows of block kb are in LDS, and every wave has finished reading block
+// kb - 1); load block kb + D - 1 into the LDS array block kb - 1 used,
+// compute block kb, load the weights of block kb + D into the register set
+// block kb used.  The wait counts the loads issued after the ones it waits
+// for, from this fixed issue order, so the later blocks stay in flight; the
+// compiler keeps the order (memory clobbers and scheduling barriers around
+// each block's loads).
 
 template <typename ST>
 struct GatherParams {
@@ -572,120 +598,378 @@ struct GatherParams {
     const uint32_t *perm;
     const uint4 *chunks;
     const uint32_t *nchunks;
-    int64_t n, k, e, words_per_row, groups_per_row;
+    const uint32_t *ids;
+    int64_t n, k, e, words_per_row, groups_per_row, l, v_total;
     int lg_gs;
 };
 
-constexpr int kGatherWaves = 4;   // K is split over the waves of a workgroup
-constexpr int kGatherCols = 1;    // 32-column blocks per workgroup (sharing the activations)
+constexpr int kGatherRows = 32;      // activation vectors per chunk (MFMA rows)
+constexpr int kGatherColWaves = 2;   // waves along N per K range (sharing the activations)
+constexpr int kGatherDepth = 2;      // K blocks in flight per wave
 
-template <int BITS, typename ST>
-__global__ void __launch_bounds__(64 * kGatherWaves) gather_mfma_kernel(GatherParams<ST> p)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
 {
-    if (blockIdx.y >= *p.nchunks) return;   // uniform over the workgroup
-    const uint4 ch = p.chunks[blockIdx.y];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 31, h = lane >> 5;
-    const int count = (int)ch.z;
-    const int64_t n0 = (int64_t)blockIdx.x * 32 * kGatherCols;
-    // this lane's activation vector (A row) and weight rows (B columns),
-    // clamped into range; results past count / n are not stored
-    const int64_t vec = p.perm[ch.y + min(c, count - 1)];
-    const bf16_bits *xrow = p.x + vec * p.k + 32 * h;
-    const bool live = (int64_t)ch.x < p.e;
-    // wave w takes the K blocks [kb0, kb1)
-    const int nk = (int)(p.k / kBK2);
-    const int kb0 = (int)((int64_t)nk * wave / kGatherWaves);
-    const int kb1 = (int)((int64_t)nk * (wave + 1) / kGatherWaves);
-    f32x16_t acc[kGatherCols];
-#pragma unroll
-    for (int cb = 0; cb < kGatherCols; ++cb) acc[cb] = f32x16_t{};
-    if (live && kb0 < kb1) {
-        const int64_t slab = ch.x;
-        const uint32_t *crow[kGatherCols];
-        const ST *srow[kGatherCols];
-        const ST *brow[kGatherCols];
-#pragma unroll
-        for (int cb = 0; cb < kGatherCols; ++cb) {
-            const int64_t wr = min(n0 + cb * 32 + c, p.n - 1);
-            crow[cb] = p.codes + (slab * p.n + wr) * p.words_per_row + 32 * h * BITS / 32;
-            srow[cb] = p.scales + (slab * p.n + wr) * p.groups_per_row;
-            brow[cb] = p.biases + (slab * p.n + wr) * p.groups_per_row;
-        }
-        uint4 xa[2][4];
-        CodeRegs<BITS> cw[2][kGatherCols];
-        auto load = [&](int kb, int par) {
-            const uint4 *xs = reinterpret_cast<const uint4 *>(xrow + (int64_t)kb * kBK2);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xa[par][j] = xs[j];
-            const int64_t g = ((int64_t)kb * kBK2 + 32 * h) >> p.lg_gs;
-#pragma unroll
-            for (int cb = 0; cb < kGatherCols; ++cb) {
-                const uint4 *cs = reinterpret_cast<const uint4 *>(crow[cb] + (int64_t)kb * 2 * BITS);
-#pragma unroll
-                for (int i = 0; i < BITS / 4; ++i) cw[par][cb].w[i] = cs[i];
-                if constexpr (sizeof(ST) == 2) {
-                    cw[par][cb].s = srow[cb][g];
-                    cw[par][cb].b = brow[cb][g];
-                } else {
-                    cw[par][cb].s = __float_as_uint(srow[cb][g]);
-                    cw[par][cb].b = __float_as_uint(brow[cb][g]);
-                }
-            }
-        };
-        auto compute = [&](int par) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int cb = 0; cb < kGatherCols; ++cb) {
-                    const bf16x8_t bv = dequant_step<BITS, ST>(cw[par][cb], j);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, xa[par][j]), bv, acc[cb], 0, 0, 0);
-                }
-        };
-        load(kb0, 0);
-        int kb = kb0;
-        for (; kb + 1 < kb1; kb += 2) {
-            load(kb + 1, 1);
-            compute(0);
-            if (kb + 2 < kb1) load(kb + 2, 0);
-            compute(1);
-        }
-        if (kb < kb1) compute(0);
-    }
-    // the waves' partial tiles are added in wave order
-    __shared__ f32x16_t part[kGatherWaves - 1][kGatherCols][64];
-    if (wave > 0) {
-#pragma unroll
-        for (int cb = 0; cb < kGatherCols; ++cb) part[wave - 1][cb][lane] = acc[cb];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < kGatherWaves - 1; ++w)
-#pragma unroll
-        for (int cb = 0; cb < kGatherCols; ++cb) acc[cb] += part[w][cb][lane];
-    // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
-#pragma unroll
-    for (int cb = 0; cb < kGatherCols; ++cb) {
-        const int64_t col = n0 + cb * 32 + c;
-        if (col < p.n) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-                if (r < count) {
-                    const int64_t yv = p.perm[ch.y + r];
-                    p.y[yv * p.n + col] = (bf16_bits)(pack_bf16(acc[cb][v], 0.0f) & 0xffffu);
-                }
-            }
-        }
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
     }
 }
 
-template <int BITS, typename ST>
+// s_waitcnt with vmcnt = N and the other counters left at their maximum
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// In-workgroup grouping (gather_self_group_fits): every workgroup counts
+// the vectors per bucket (expert id, ids past the last expert in bucket
+// e), scans the counts into chunk offsets, and finds its chunk -- the
+// blockIdx.y-th in bucket order, chunks of at most 32 vectors in increasing
+// vector order within a bucket, exactly the separate grouping pass's table
+// -- and the chunk's vectors, by ballots over its ids.  Returns false if
+// the workgroup has no chunk.  ch = {bucket, -, count}; list[r] = vector r.
+constexpr int kSelfGroupRounds = 16;
+
+template <int NT>
+__device__ bool gather_self_group(const uint32_t *ids, int64_t l, int64_t v_total, int e, uint4 &ch,
+                                  uint32_t *list)
+{
+    constexpr int NWV = NT / 64;
+    __shared__ uint32_t gh[256], gst[256], gcoff[257], gw[NWV];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int nb = e + 1;
+    const int rounds = (int)((v_total + NT - 1) / NT);
+    const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
+    uint32_t bk[kSelfGroupRounds];
+    for (int b = t; b < nb; b += NT) gh[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSelfGroupRounds; ++r) {
+        bk[r] = 0xffffffffu;
+        if (r < rounds) {   // uniform
+            const int64_t v = (int64_t)r * NT + t;
+            if (v < v_total) bk[r] = min(ids[v / l], (uint32_t)e);
+            // one atomic per distinct bucket of the wave
+            uint64_t active = __ballot(bk[r] != 0xffffffffu);
+            while (active) {
+                const int leader = __ffsll((long long)active) - 1;
+                const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bk[r], leader);
+                const uint64_t m = __ballot(bk[r] == lb) & active;
+                if (lane == leader) atomicAdd(&gh[lb], (uint32_t)__popcll(m));
+                active &= ~m;
+            }
+        }
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // exclusive scans of the bucket sizes and chunk counts (lane i: buckets 4 i .. 4 i + 3)
+        uint32_t hv[4], cn[4], sh = 0, sc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * lane + j;
+            hv[j] = b < nb ? gh[b] : 0u;
+            cn[j] = (hv[j] + kGatherRows - 1) / kGatherRows;
+            sh += hv[j];
+            sc += cn[j];
+        }
+        uint32_t ih = sh, ic = sc;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t a = __shfl_up(ih, off), c2 = __shfl_up(ic, off);
+            if (lane >= off) ih += a, ic += c2;
+        }
+        uint32_t ph = ih - sh, pc = ic - sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * lane + j;
+            if (b < nb) gst[b] = ph, gcoff[b] = pc;
+            ph += hv[j];
+            pc += cn[j];
+        }
+        if (lane == 63) gcoff[nb] = ic;
+    }
+    __syncthreads();
+    const uint32_t j = blockIdx.y;
+    if (j >= gcoff[nb]) return false;   // uniform
+    int lo = 0, hi = nb;                // gcoff[lo] <= j < gcoff[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (gcoff[mid] <= j) lo = mid;
+        else hi = mid;
+    }
+    const uint32_t bj = (uint32_t)lo, first = (j - gcoff[lo]) * kGatherRows;
+    const uint32_t cnt = min((uint32_t)kGatherRows, gh[lo] - first);
+    uint32_t run = 0;   // vectors of bucket bj in earlier rounds
+#pragma unroll
+    for (int r = 0; r < kSelfGroupRounds; ++r) {
+        if (r < rounds) {   // uniform
+            const uint64_t m = __ballot(bk[r] == bj);
+            if (lane == 0) gw[wv] = (uint32_t)__popcll(m);
+            __syncthreads();
+            uint32_t before = run, all = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < NWV; ++w2) {
+                const uint32_t g = gw[w2];
+                before += w2 < wv ? g : 0u;
+                all += g;
+            }
+            if (bk[r] == bj) {
+                const uint32_t rank = before + (uint32_t)__popcll(m & below) - first;
+                if (rank < cnt) list[rank] = (uint32_t)((int64_t)r * NT + t);
+            }
+            run += all;
+            __syncthreads();
+        }
+    }
+    ch = make_uint4(bj, 0u, cnt, 0u);
+    return true;
+}
+
+template <int BITS, typename ST, int CB, int KS, int D, bool SBR, bool SELF>
+__global__ void __launch_bounds__(64 * CB * KS) gather_mfma_kernel(GatherParams<ST> p)
+{
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    static_assert(CB == 1 || CB == 2 || CB == 4, "column waves per group");
+    static_assert(CB * KS <= 16, "workgroup size");
+    constexpr int NX = 4 / CB;                  // activation loads per wave and block (8 rows each)
+    constexpr int NS = (int)sizeof(ST) / 2;     // scale/bias loads per wave and stage
+    constexpr int CW = BITS / 4;                // 16-byte code loads per lane and block
+    __shared__ uint4 xs0[KS][kGatherRows * 8], xs1[KS][kGatherRows * 8], xs2[KS][kGatherRows * 8],
+        xs3[KS][kGatherRows * 8];
+    // per wave, two stages of [NS][scales of 32 rows, biases of 32 rows] x 16 bytes
+    __shared__ uint4 sb_lds[CB * KS][SBR ? 2 : 1][SBR ? NS * 64 : 1];
+    __shared__ uint32_t vec_list[kGatherRows];
+    uint4 ch;
+    if constexpr (SELF) {
+        if (!gather_self_group<64 * CB * KS>(p.ids, p.l, p.v_total, (int)p.e, ch, vec_list)) return;
+    } else {
+        if (blockIdx.y >= *p.nchunks) return;   // uniform over the workgroup
+        ch = p.chunks[blockIdx.y];
+    }
+    // vector r of the chunk (r < count)
+    auto vec_at = [&](int r) -> uint32_t { return SELF ? vec_list[r] : p.perm[ch.y + r]; };
+    const int lane = threadIdx.x & 63;
+    const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cbw = wave_id % CB, grp = wave_id / CB;
+    const int c = lane & 31, h = lane >> 5;
+    const int count = (int)ch.z;
+    const int64_t n0 = ((int64_t)blockIdx.x * CB + cbw) * 32;
+    const bool live = (int64_t)ch.x < p.e;
+    // wave group grp takes the K blocks [kb0, kb0 + nk)
+    const int nk = (int)(p.k / kBK2) / KS;
+    const int kb0 = grp * nk;
+    // the vector whose output row is this lane's A row (clamped; rows past
+    // count are computed and not stored)
+    const uint32_t vec_c = vec_at(min(c, count - 1));
+    f32x16_t acc = f32x16_t{};
+    if (live && nk > 0) {
+        const int64_t slab = ch.x;
+        // activation loads: rows r0 + 8 i + lane / 8 of the chunk, slot lane % 8
+        const int r0 = cbw * (32 / CB);
+        const bf16_bits *xsrc[NX];
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int xr = r0 + 8 * i + (lane >> 3);
+            const int64_t xvec = vec_at(min(xr, count - 1));
+            xsrc[i] = p.x + xvec * p.k + (int64_t)kb0 * kBK2 + 8 * ((lane & 7) ^ ((xr >> 1) & 7));
+        }
+        // this lane's codes: weight row c, k = 32 h .. 32 h + 31 of each block
+        const int64_t wr = min(n0 + c, p.n - 1);
+        const uint32_t *crow = p.codes + (slab * p.n + wr) * p.words_per_row + h * BITS + (int64_t)kb0 * 2 * BITS;
+        // scale/bias stages: 8 groups, i.e. 2^(lg_gs - 3) blocks, from group g0
+        const int64_t g0 = ((int64_t)kb0 * kBK2) >> p.lg_gs;
+        const ST *srow = p.scales + (slab * p.n + wr) * p.groups_per_row + g0;
+        const ST *brow = p.biases + (slab * p.n + wr) * p.groups_per_row + g0;
+        const ST *sbsrc = h ? brow : srow;
+        const int lg_sb = p.lg_gs - 3;
+        const int nsb = ((nk * kBK2) >> p.lg_gs) >> 3;   // scale/bias stages
+        uint4 *sbw = sb_lds[wave_id][0];
+        CodeRegs<BITS> cw[D];
+        // register loads per block, and all loads per block (the scale/bias
+        // stage loads in between only make the counted waits stricter)
+        constexpr int NW = CW + (SBR ? 0 : 2);
+        constexpr int NB = NW + NX;
+        auto ring = [&](auto s) -> uint4 * {
+            constexpr int S = decltype(s)::value;
+            if constexpr (S == 0) return xs0[grp];
+            else if constexpr (S == 1) return xs1[grp];
+            else if constexpr (S == 2) return xs2[grp];
+            else return xs3[grp];
+        };
+        auto fence = [] {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto load_x = [&](int kb, auto s) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < NX; ++i)
+                __builtin_amdgcn_global_load_lds((const void *)(xsrc[i] + (int64_t)kb * kBK2),
+                                                 (lds_void *)(ring(s) + (r0 + 8 * i) * 8), 16, 0, 0);
+            fence();
+        };
+        auto load_w = [&](int kb, int slot) {
+            const uint4 *cs = reinterpret_cast<const uint4 *>(crow + (int64_t)kb * 2 * BITS);
+#pragma unroll
+            for (int i = 0; i < CW; ++i) cw[slot].w[i] = cs[i];
+            if constexpr (!SBR) {
+                const int gr = (kb * kBK2 + 32 * h) >> p.lg_gs;   // group, relative to g0
+                if constexpr (sizeof(ST) == 2) {
+                    cw[slot].s = srow[gr];
+                    cw[slot].b = brow[gr];
+                } else {
+                    cw[slot].s = __float_as_uint(srow[gr]);
+                    cw[slot].b = __float_as_uint(brow[gr]);
+                }
+            }
+            fence();
+        };
+        // scale/bias stage t into ring buffer t % 2
+        auto load_sb = [&](int t) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                __builtin_amdgcn_global_load_lds((const void *)(sbsrc + 8 * t + (16 / (int)sizeof(ST)) * j),
+                                                 (lds_void *)(sbw + (t & 1) * (NS * 64) + j * 64), 16, 0, 0);
+            fence();
+        };
+        // At the first block of scale/bias stage t >= 1, stage t + 1 goes
+        // into the buffer stage t - 1 used (this wave's alone, and its reads
+        // are done: the barrier before waited for this wave's LDS reads).
+        auto stage_next = [&](int kb) {
+            if constexpr (!SBR) return;
+            const int t = kb >> lg_sb;
+            if (kb > 0 && (kb & ((1 << lg_sb) - 1)) == 0 && t + 1 < nsb) load_sb(t + 1);
+        };
+        // This lane's scale and bias for block kb, read in one asm block that
+        // waits for its own results: the compiler cannot tell the stage read
+        // here from the one whose load may be in flight, and would wait for
+        // every load this wave has in flight.  The counted waits already
+        // cover this stage: its load is older than the activation loads of
+        // the block that first uses it.
+        const uint32_t sb_base = (uint32_t)(uintptr_t)(lds_void *)sbw + c * 16;
+        auto read_sb = [&](int kb, CodeRegs<BITS> &w) {
+            if constexpr (!SBR) return;   // loaded with the codes
+            const int gr = (kb * kBK2 + 32 * h) >> p.lg_gs;   // group, relative to g0
+            const int t = gr >> 3, e = gr & 7;
+            const uint32_t sa = sb_base + (uint32_t)((t & 1) * (NS * 1024) + (e * (int)sizeof(ST) / 16) * 1024 +
+                                                     (e * (int)sizeof(ST)) % 16);
+            uint32_t sv, bv;
+            if constexpr (sizeof(ST) == 2)
+                asm volatile("ds_read_u16 %0, %2\n\tds_read_u16 %1, %2 offset:512\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(sv), "=&v"(bv) : "v"(sa));
+            else
+                asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:512\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(sv), "=&v"(bv) : "v"(sa));
+            w.s = sv;
+            w.b = bv;
+        };
+        auto barrier = [&] {
+            // this wave's LDS reads are done (lgkmcnt 0); with CB > 1 the
+            // waves of a group share the activation ring
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            asm volatile("" ::: "memory");
+            if constexpr (CB > 1) __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        auto compute = [&](auto s, int slot, int kb) {
+            CodeRegs<BITS> &w = cw[slot];
+            read_sb(kb, w);
+            const uint4 *xb = ring(s);
+            uint4 a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = xb[c * 8 + ((4 * h + j) ^ ((c >> 1) & 7))];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8_t bv = dequant_step<BITS, ST>(w, j);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[j]), bv, acc,
+                                                              0, 0, 0);
+            }
+        };
+        // prologue: scale/bias stages 0 and 1, then in the steady-state
+        // order W(0), X(j), W(j + 1) for j = 0 .. D - 2 (blocks past the end
+        // are clamped; they are never computed)
+        if constexpr (SBR) {
+            load_sb(0);
+            if (nsb > 1) load_sb(1);
+        }
+        load_w(0, 0);
+        static_for<0, D - 1>([&](auto jj) {
+            constexpr int J = decltype(jj)::value;
+            load_x(min(J, nk - 1), std::integral_constant<int, J>{});
+            load_w(min(J + 1, nk - 1), J + 1);
+        });
+        // Block kb: wait for this wave's activation loads of block kb (the
+        // loads issued after them: the codes of block kb + 1 and those of
+        // D - 2 later blocks), barrier, load the activations of block
+        // kb + D - 1 into the buffer block kb - 1 used, start the next
+        // scale/bias stage where due, compute, load the codes of block kb + D
+        // into the register set block kb used.
+        int base = 0;
+        for (; base + 2 * D <= nk; base += D) {
+            static_for<0, D>([&](auto dd) {
+                constexpr int d = decltype(dd)::value;
+                wait_vmcnt<NW + (D - 2) * NB>();
+                barrier();
+                load_x(base + d + D - 1, std::integral_constant<int, (d + D - 1) % D>{});
+                stage_next(base + d);
+                compute(dd, d, base + d);
+                load_w(base + d + D, d);
+            });
+        }
+        // the last D .. 2D - 1 blocks (or all of them when nk < D)
+        static_for<0, 2 * D - 1>([&](auto dd) {
+            constexpr int d = decltype(dd)::value;
+            const int kb = base + d;
+            if (kb < nk) {   // uniform
+                if constexpr (d == 0) wait_vmcnt<NW + (D - 2) * NB>();
+                else if constexpr (d < D) wait_vmcnt<(D - 1 - d) * NB>();
+                else wait_vmcnt<0>();
+                barrier();
+                if constexpr (d == 0) load_x(min(kb + D - 1, nk - 1), std::integral_constant<int, D - 1>{});
+                else if (kb + D - 1 < nk) load_x(kb + D - 1, std::integral_constant<int, (d + D - 1) % D>{});
+                stage_next(kb);
+                compute(std::integral_constant<int, d % D>{}, d % D, kb);
+                if (kb + D < nk) load_w(kb + D, d % D);
+            }
+        });
+    }
+    if constexpr (KS > 1) {
+        // the later groups' partial tiles are added in LDS, in group order
+        __shared__ f32x16_t part[KS - 1][CB][64];
+        if (grp > 0) part[grp - 1][cbw][lane] = acc;
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g2 = 0; g2 < KS - 1; ++g2) acc += part[g2][cbw][lane];
+    }
+    // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
+    const int64_t col = n0 + c;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+        const uint32_t yv = __shfl(vec_c, r);
+        if (r < count && col < p.n)
+            p.y[(int64_t)yv * p.n + col] = (bf16_bits)(pack_bf16(acc[v], 0.0f) & 0xffffu);
+    }
+}
+
+// The scale/bias ring needs K split into KS equal ranges that are whole
+// numbers of stages (8 groups), and 16-byte aligned scales and biases (its
+// loads move 16 bytes a lane).  Otherwise each block loads its own pair;
+// the values, and so the results, are the same either way.
+bool gather_sb_ring_fits(int ks, int64_t k, int gs, const void *scales, const void *biases)
+{
+    return gs >= 32 && (k / ks) % (8 * (int64_t)gs) == 0 &&
+           (((uintptr_t)scales | (uintptr_t)biases) & 15) == 0;
+}
+
+template <int BITS, typename ST, int KS, bool SBR, bool SELF>
 hipError_t gather_mfma_run(const GatherMfmaLaunch &a, hipStream_t stream)
 {
+    constexpr int CB = kGatherColWaves, D = kGatherDepth;
     GatherParams<ST> p;
     p.x = static_cast<const bf16_bits *>(a.x);
     p.y = static_cast<bf16_bits *>(a.y);
@@ -695,27 +979,55 @@ hipError_t gather_mfma_run(const GatherMfmaLaunch &a, hipStream_t stream)
     p.perm = a.perm;
     p.chunks = reinterpret_cast<const uint4 *>(a.chunks);
     p.nchunks = a.nchunks;
+    p.ids = a.ids;
     p.n = a.n;
     p.k = a.k;
     p.e = a.e;
+    p.l = a.l;
+    p.v_total = a.v_total;
     p.words_per_row = a.k * BITS / 32;
     p.groups_per_row = a.k / a.gs;
     p.lg_gs = a.gs == 32 ? 5 : a.gs == 64 ? 6 : 7;
-    if (a.k % kBK2 != 0 || a.max_chunks > 65535) return hipErrorInvalidValue;
-    const unsigned gx = (unsigned)((a.n + 32 * kGatherCols - 1) / (32 * kGatherCols));
-    gather_mfma_kernel<BITS, ST><<<dim3(gx, (unsigned)a.max_chunks), dim3(64 * kGatherWaves), 0, stream>>>(p);
+    if (a.k % (kBK2 * KS) != 0 || a.max_chunks > 65535) return hipErrorInvalidValue;
+    if (SELF && (!gather_self_group_fits(a.v_total, a.e) || a.v_total > (int64_t)kSelfGroupRounds * 64 * CB * KS ||
+                 a.l <= 0))
+        return hipErrorInvalidValue;
+    if (SBR && !gather_sb_ring_fits(KS, a.k, a.gs, a.scales, a.biases)) return hipErrorInvalidValue;
+    const unsigned gx = (unsigned)((a.n + 32 * CB - 1) / (32 * CB));
+    gather_mfma_kernel<BITS, ST, CB, KS, D, SBR, SELF>
+        <<<dim3(gx, (unsigned)a.max_chunks), dim3(64 * CB * KS), 0, stream>>>(p);
     return hipGetLastError();
+}
+
+template <int BITS, typename ST, bool SELF>
+hipError_t gather_mfma_pick(const GatherMfmaLaunch &a, hipStream_t stream)
+{
+    // the K split depends on k alone: it fixes each row's summation order
+    if (a.k % (2 * kBK2) == 0) {
+        if (gather_sb_ring_fits(2, a.k, a.gs, a.scales, a.biases))
+            return gather_mfma_run<BITS, ST, 2, true, SELF>(a, stream);
+        return gather_mfma_run<BITS, ST, 2, false, SELF>(a, stream);
+    }
+    if (gather_sb_ring_fits(1, a.k, a.gs, a.scales, a.biases)) return gather_mfma_run<BITS, ST, 1, true, SELF>(a, stream);
+    return gather_mfma_run<BITS, ST, 1, false, SELF>(a, stream);
+}
+
+template <int BITS, typename ST>
+hipError_t gather_mfma_pick(const GatherMfmaLaunch &a, hipStream_t stream)
+{
+    if (a.self_group) return gather_mfma_pick<BITS, ST, true>(a, stream);
+    return gather_mfma_pick<BITS, ST, false>(a, stream);
 }
 
 hipError_t launch_gather_mfma(const GatherMfmaLaunch &a, hipStream_t stream)
 {
     if (a.bits != 4 && a.bits != 8) return hipErrorInvalidValue;
     if (a.sb_dt == DT_F32) {
-        if (a.bits == 4) return gather_mfma_run<4, float>(a, stream);
-        return gather_mfma_run<8, float>(a, stream);
+        if (a.bits == 4) return gather_mfma_pick<4, float>(a, stream);
+        return gather_mfma_pick<8, float>(a, stream);
     }
-    if (a.bits == 4) return gather_mfma_run<4, bf16_bits>(a, stream);
-    return gather_mfma_run<8, bf16_bits>(a, stream);
+    if (a.bits == 4) return gather_mfma_pick<4, bf16_bits>(a, stream);
+    return gather_mfma_pick<8, bf16_bits>(a, stream);
 }
 
 bool tiled_fits(int tile_m, int tile_n, int bits, int gs, int sb_dt, int64_t m, int64_t n, int64_t k)

@@ -264,12 +264,41 @@ def test_gather_grouped(case):
     assert bits_equal(yd, B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids)))
 
 
-@pytest.mark.parametrize("bits,gs,w_dtype", [(4, 32, "bf16"), (8, 128, "bf16"), (4, 64, "f32"),
-                                             (8, 64, "f32")])
-def test_gather_mfma_modes(bits, gs, w_dtype):
-    """The grouped matrix-core gather over bit widths, group sizes and scale
-    dtypes, with a ragged n and expert sizes above and below one chunk."""
-    e, n, k, rows = 6, 72, 512, 150
+@pytest.mark.parametrize("case", ["many_vectors", "many_experts"])
+def test_gather_large_id_sets(case):
+    """Id sets past what a matrix-core workgroup groups by itself (more than
+    2048 vectors), and more experts than the fast grouping pass takes (the
+    general one then runs): both entries against the oracle, and row-exact
+    rows bit-equal to their one-row products."""
+    gs, bits = 64, 4
+    e, rows, l, n, k = {"many_vectors": (16, 700, 3, 96, 512), "many_experts": (300, 1300, 1, 64, 256)}[case]
+    rng = np.random.default_rng(rows)
+    ids = rng.integers(0, e + 2, size=rows, dtype=np.uint32)   # a few ids past the last expert
+    w, _ = synthetic.random_case(e, (e, n, k), (1, k), 0.02, "bf16")
+    _, x = synthetic.random_case(rows, (1, 1), (rows, l, k), 1.0, "f32", "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    xs, cs, ss, bs, di = dev(x), dev(c), dev(s), dev(b), dev(ids)
+    y_ref = O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows * l, n)
+    yd = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, di)
+    assert_rows_close(values(host(yd)).reshape(rows * l, n), y_ref, 1e-2, "matrix-core gather")
+    y = B.nq_gather_qmm_row_exact(xs, cs, ss, bs, gs, bits, di)
+    assert_rows_close(values(host(y)).reshape(rows * l, n), y_ref, 1e-2, "row-exact gather")
+    for r in range(0, rows, max(1, rows // 10)):
+        if ids[r] >= e:
+            assert np.all(values(host(y[r])) == 0) and np.all(values(host(yd[r])) == 0)
+            continue
+        yr = B.nq_qmm_row_exact(xs[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+        assert bits_equal(yr, y[r]), r
+
+
+@pytest.mark.parametrize("bits,gs,w_dtype,k", [(4, 32, "bf16", 512), (8, 128, "bf16", 512), (4, 64, "f32", 512),
+                                               (8, 64, "f32", 512), (4, 64, "bf16", 2048), (8, 128, "f32", 2048),
+                                               (4, 32, "bf16", 576), (8, 64, "bf16", 1280)])
+def test_gather_mfma_modes(bits, gs, w_dtype, k):
+    """The grouped matrix-core gather over bit widths, group sizes, scale
+    dtypes and K (split in two or not; scales through the LDS ring or per
+    block), with a ragged n and expert sizes above and below one chunk."""
+    e, n, rows = 6, 72, 150
     rng = np.random.default_rng(bits + gs)
     ids = rng.integers(0, e, size=rows, dtype=np.uint32)
     ids[:45] = 2                                   # one expert with two chunks of 32
@@ -278,6 +307,32 @@ def test_gather_mfma_modes(bits, gs, w_dtype):
     c, s, b = O.quantize(w, gs, bits)
     y = B.nq_gather_qmm(dev(x), dev(c), dev(s), dev(b), gs, bits, dev(ids))
     assert_rows_close(values(host(y)).reshape(rows, n),
+                      O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows, n), 1e-2, "mfma gather")
+
+
+@pytest.mark.parametrize("bits,gs,w_dtype", [(4, 64, "bf16"), (8, 32, "f32")])
+def test_gather_mfma_scale_paths_same_bits(bits, gs, w_dtype):
+    """Scales and biases that are only element-aligned take per-block loads
+    instead of the LDS ring; the results are the same bits."""
+    e, n, k, rows = 4, 96, 2048, 64
+    rng = np.random.default_rng(7)
+    ids = rng.integers(0, e, size=rows, dtype=np.uint32)
+    w, x = synthetic.random_case(bits, (e, n, k), (rows, 1, k), 0.02, w_dtype, "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    xs, cs, ss, bs, di = dev(x), dev(c), dev(s), dev(b), dev(ids)
+
+    def offset_copy(t):
+        # same values one element past a 16-byte boundary
+        flat = torch.zeros(t.numel() + 16, dtype=t.dtype, device=t.device)
+        v = flat[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 != 0
+        return v
+
+    y0 = B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, di)
+    y1 = B.nq_gather_qmm(xs, cs, offset_copy(ss), offset_copy(bs), gs, bits, di)
+    assert bits_equal(y0, y1)
+    assert_rows_close(values(host(y0)).reshape(rows, n),
                       O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows, n), 1e-2, "mfma gather")
 
 
