@@ -835,7 +835,12 @@ template <typename XT, typename ST>
 hipError_t gemv_dt(const GemvLaunch &a, hipStream_t stream)
 {
     switch (a.bits) {
+    case 1: return gemv_bits<1, XT, ST>(a, stream);
+    case 2: return gemv_bits<2, XT, ST>(a, stream);
+    case 3: return gemv_bits<3, XT, ST>(a, stream);
     case 4: return gemv_bits<4, XT, ST>(a, stream);
+    case 5: return gemv_bits<5, XT, ST>(a, stream);
+    case 6: return gemv_bits<6, XT, ST>(a, stream);
     case 8: return gemv_bits<8, XT, ST>(a, stream);
     default: return hipErrorInvalidValue;
     }

@@ -34,7 +34,7 @@ const char *dtype_name(int dt) { return dt == NQ_F32 ? "f32" : dt == NQ_BF16 ? "
 // product kernels ("an unsupported combination fails in the operation that
 // uses it").
 bool storage_bits_ok(int b) { return b == 1 || b == 2 || b == 3 || b == 4 || b == 5 || b == 6 || b == 8; }
-bool product_bits_ok(int b) { return b == 4 || b == 8; }
+bool product_bits_ok(int b) { return storage_bits_ok(b); }
 bool group_ok(int gs) { return gs == 32 || gs == 64 || gs == 128; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
@@ -61,7 +61,7 @@ nq_status check_quant(const char *op, int gs, int bits, bool product)
     if (!group_ok(gs)) return fail(NQ_ERR_QUANT, "%s: group_size=%d is not 32, 64 or 128", op, gs);
     if (product ? !product_bits_ok(bits) : !storage_bits_ok(bits))
         return fail(NQ_ERR_QUANT, "%s: bits=%d is not supported (%s)", op, bits,
-                    product ? "products take 4 or 8" : "1, 2, 3, 4, 5, 6 or 8");
+                    "1, 2, 3, 4, 5, 6 or 8");
     return NQ_OK;
 }
 

@@ -70,10 +70,18 @@ __global__ void __launch_bounds__(256) tiled_kernel(TiledParams<ST> p)
             const int64_t e0 = k0 + 16 * lhalf;
             const float s = Elt<ST>::load(p.scales, wr * p.groups_per_row + e0 / p.gs);
             const float b = Elt<ST>::load(p.biases, wr * p.groups_per_row + e0 / p.gs);
-            uint32_t cw[BITS / 2];
-            const uint32_t *src = p.codes + wr * p.words_per_row + e0 * BITS / 32;
+            // the 16 codes start at bit e0 * BITS of the row: 16 bits into a
+            // word for odd widths and odd halves.  Load the (BITS + 1) / 2
+            // words they touch (no more: all inside the row) and realign.
+            constexpr int NW = (BITS + 1) / 2;
+            const int64_t bit0 = e0 * BITS;
+            const uint32_t *src = p.codes + wr * p.words_per_row + (bit0 >> 5);
+            const uint32_t sh = (uint32_t)(bit0 & 31);
+            uint32_t raw[NW], cw[NW];
 #pragma unroll
-            for (int i = 0; i < BITS / 2; ++i) cw[i] = src[i];
+            for (int i = 0; i < NW; ++i) raw[i] = src[i];
+#pragma unroll
+            for (int i = 0; i < NW; ++i) cw[i] = __builtin_amdgcn_alignbit(i + 1 < NW ? raw[i + 1] : 0u, raw[i], sh);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float v0 = fmaf(s, (float)code_at<BITS>(cw, 2 * i), b);
@@ -1045,8 +1053,9 @@ bool tiled_fits(int tile_m, int tile_n, int bits, int gs, int sb_dt, int64_t m, 
 
 bool tiled_supported(int tile_m, int tile_n, int bits)
 {
-    return ((tile_m == kTM && tile_n == kTN) || (tile_m == kBM && tile_n == kBN)) &&
-           (bits == 4 || bits == 8);
+    const bool any_width = bits == 1 || bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8;
+    if (tile_m == kTM && tile_n == kTN) return any_width;
+    return tile_m == kBM && tile_n == kBN && (bits == 4 || bits == 8);
 }
 
 namespace {
@@ -1066,28 +1075,43 @@ hipError_t tiled_run(const TiledLaunch &a, hipStream_t stream)
     p.groups_per_row = a.k / a.gs;
     p.gs = a.gs;
     p.lg_gs = a.gs == 32 ? 5 : a.gs == 64 ? 6 : 7;
-    if (a.tile_m == kBM) {
-        if (!tiled_fits(kBM, kBN, BITS, a.gs, a.sb_dt, a.m, a.n, a.k)) return hipErrorInvalidValue;
-        const int tm = (int)((a.m + kBM - 1) / kBM), tn = (int)((a.n + kBN - 1) / kBN);
-        const int per = (tm * tn + 7) / 8;
-        tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), 0, stream>>>(p, tm, tn, per);
-        return hipGetLastError();
+    if constexpr (BITS == 4 || BITS == 8) {
+        if (a.tile_m == kBM) {
+            if (!tiled_fits(kBM, kBN, BITS, a.gs, a.sb_dt, a.m, a.n, a.k)) return hipErrorInvalidValue;
+            const int tm = (int)((a.m + kBM - 1) / kBM), tn = (int)((a.n + kBN - 1) / kBN);
+            const int per = (tm * tn + 7) / 8;
+            tiled256_kernel<BITS, ST><<<dim3(8 * per), dim3(256), 0, stream>>>(p, tm, tn, per);
+            return hipGetLastError();
+        }
+    } else if (a.tile_m != kTM) {
+        return hipErrorInvalidValue;
     }
     const dim3 grid((unsigned)((a.n + kTN - 1) / kTN), (unsigned)((a.m + kTM - 1) / kTM));
     tiled_kernel<BITS, ST><<<grid, dim3(256), 0, stream>>>(p);
     return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t tiled_bits(const TiledLaunch &a, hipStream_t stream)
+{
+    switch (a.bits) {
+    case 1: return tiled_run<1, ST>(a, stream);
+    case 2: return tiled_run<2, ST>(a, stream);
+    case 3: return tiled_run<3, ST>(a, stream);
+    case 4: return tiled_run<4, ST>(a, stream);
+    case 5: return tiled_run<5, ST>(a, stream);
+    case 6: return tiled_run<6, ST>(a, stream);
+    case 8: return tiled_run<8, ST>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 }  // namespace
 
 hipError_t launch_tiled(const TiledLaunch &a, hipStream_t stream)
 {
     if (!tiled_supported(a.tile_m, a.tile_n, a.bits)) return hipErrorInvalidValue;
-    if (a.sb_dt == DT_F32) {
-        if (a.bits == 4) return tiled_run<4, float>(a, stream);
-        return tiled_run<8, float>(a, stream);
-    }
-    if (a.bits == 4) return tiled_run<4, bf16_bits>(a, stream);
-    return tiled_run<8, bf16_bits>(a, stream);
+    if (a.sb_dt == DT_F32) return tiled_bits<float>(a, stream);
+    return tiled_bits<bf16_bits>(a, stream);
 }
 
 }  // namespace nqk

@@ -65,8 +65,8 @@ typedef enum {
     NQ_OK = 0,
     NQ_ERR_NULL = 1,      /* a required pointer is null */
     NQ_ERR_DTYPE = 2,     /* unknown dtype, or a dtype pair not supported */
-    NQ_ERR_QUANT = 3,     /* group_size not in {32, 64, 128}, or bits not supported by the
-                             operation: quantize/dequantize take 1-6 and 8, products 4 and 8 */
+    NQ_ERR_QUANT = 3,     /* group_size not in {32, 64, 128}, or bits not in {1, 2, 3, 4, 5,
+                             6, 8} (every operation takes the same widths) */
     NQ_ERR_SHAPE = 4,     /* negative size, k % group_size != 0, bad expert count, size overflow */
     NQ_ERR_ALIGN = 5,     /* a base pointer is not aligned as documented above */
     NQ_ERR_ALIAS = 6,     /* an output overlaps an input or another output */

@@ -122,7 +122,7 @@ def test_qmm_argument_errors(lib, entry):
     cases = [
         (dict(x_dt=7), NQ_ERR_DTYPE, "dtype"),
         (dict(sb_dt=-1), NQ_ERR_DTYPE, "dtype"),
-        (dict(bits=3), NQ_ERR_QUANT, "bits=3"),
+        (dict(bits=7), NQ_ERR_QUANT, "bits=7"),
         (dict(bits=16), NQ_ERR_QUANT, "bits=16"),
         (dict(gs=16), NQ_ERR_QUANT, "group_size=16"),
         (dict(k=100), NQ_ERR_SHAPE, "k=100 is not a multiple of group_size=64"),
@@ -153,6 +153,21 @@ def test_empty_products_enqueue_nothing(lib):
     assert _qmm(lib, n=0, x=0, codes=0, scales=0, biases=0, y=0) == NQ_OK
     st = lib.nq_gather_qmm(0, BF16, 0, 1, 128, 0, 0, 0, BF16, 4, 64, 64, 4, 0, 0, 0, 0, 0, None)
     assert st == NQ_OK
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 5, 6])
+def test_plan_routes_other_widths(lib, bits):
+    """Every stored width has a product route: matrix-vector for few rows,
+    128-row tiles for many (the 256-row tiles take 4 and 8 bits)."""
+    assert plan(lib, 8, 4096, 4096, bits=bits).route == B.NQ_ROUTE_GEMV
+    p = plan(lib, 2048, 4096, 4096, bits=bits)
+    assert p.route == B.NQ_ROUTE_TILED and p.tile_m == 128 and p.tile_n == 128
+    assert plan(lib, 2048, 4096, 4096, bits=bits, row_exact=1).route == B.NQ_ROUTE_GEMV
+    forced = plan(lib, 2048, 256, 256, bits=4)
+    assert forced.tile_m == 256
+    st = lib.nq_qmm_with_plan(ctypes.byref(forced), FAKE, BF16, 2048, 256, FAKE2, FAKE2 + 0x100000,
+                              FAKE2 + 0x200000, BF16, 256, 64, bits, FAKE2 + 0x300000, 0, 0, None)
+    assert st == NQ_ERR_PLAN and b"not supported" in lib.nq_last_error()
 
 
 def test_plan_errors(lib):
@@ -222,7 +237,7 @@ def test_gather_argument_errors(lib):
     assert g(y=FAKE2 + 0x300000) == NQ_ERR_ALIAS
     assert b"rhs_idx" in lib.nq_last_error()
     assert g(idx=FAKE2 + 0x300002) == NQ_ERR_ALIGN
-    assert g(bits=5) == NQ_ERR_QUANT
+    assert g(bits=7) == NQ_ERR_QUANT
     assert b"nq_gather_qmm:" in lib.nq_last_error()
 
 
@@ -262,12 +277,12 @@ def test_error_string_is_thread_local(lib):
 
     def other():
         seen["before"] = lib.nq_last_error()
-        _qmm(lib, bits=3)
+        _qmm(lib, bits=7)
         seen["after"] = lib.nq_last_error()
 
     t = threading.Thread(target=other)
     t.start()
     t.join()
     assert seen["before"] == b""
-    assert b"bits=3" in seen["after"]
+    assert b"bits=7" in seen["after"]
     assert b"k=100" in lib.nq_last_error()

@@ -349,6 +349,56 @@ def test_gather_sorted_hint_same_bits():
     assert_rows_close(host(y0), O.gather_qmm_f64(x, c, s, b, gs, bits, ids), 1e-3, "page example")
 
 
+# ------------------------------------------------------------------ other widths
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 5, 6])
+@pytest.mark.parametrize("m,n,k,gs,x_dtype,w_dtype", [
+    (1, 200, 1024, 64, "bf16", "bf16"),     # decode
+    (3, 130, 4160, 32, "f32", "f32"),       # few rows, a ragged last K step
+    (8, 96, 2560, 128, "bf16", "f32"),
+    (4, 96, 14336, 64, "bf16", "bf16"),     # split-K
+    (200, 260, 544, 32, "bf16", "bf16"),    # 128-row tiles, ragged m, n and k
+    (130, 300, 1024, 64, "bf16", "f32"),
+])
+def test_other_widths_qmm(bits, m, n, k, gs, x_dtype, w_dtype):
+    """Products over 1-, 2-, 3-, 5- and 6-bit codes (3, 5 and 6 straddle
+    words) on every route: against the oracle, and row-exact rows bit-equal
+    to their one-row products."""
+    w, x, c, s, b = quantized_case(bits * 1000 + m, n, k, gs, bits, w_dtype, m, x_dtype, 0.02)
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y_ref = O.qmm_f64(x, c, s, b, gs, bits)
+    y = B.nq_qmm(xs, *q, gs, bits)
+    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), f"{bits}-bit qmm")
+    yr = B.nq_qmm_row_exact(xs, *q, gs, bits)
+    assert_rows_close(values(host(yr)), y_ref, tolerance(yr.dtype), f"{bits}-bit row-exact")
+    for r in range(0, m, max(1, m // 6)):
+        y1 = B.nq_qmm(xs[r:r + 1].contiguous(), *q, gs, bits)
+        assert bits_equal(y1, yr[r:r + 1]), r
+        if m <= 8:
+            assert bits_equal(y1, y[r:r + 1]), r
+
+
+@pytest.mark.parametrize("bits", [3, 5])
+@pytest.mark.parametrize("rows", [6, 40])
+def test_other_widths_gather(bits, rows):
+    """gather over straddling widths, per row (6 vectors) and grouped by
+    expert (40): every row bit-equal to its expert's one-row product."""
+    e, n, k, gs = 5, 72, 1024, 64
+    rng = np.random.default_rng(bits * rows)
+    ids = rng.integers(0, e, size=rows, dtype=np.uint32)
+    w, x = synthetic.random_case(bits + rows, (e, n, k), (rows, 1, k), 0.02, "bf16", "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    xs, cs, ss, bs = dev(x), dev(c), dev(s), dev(b)
+    y_ref = O.gather_qmm_f64(x, c, s, b, gs, bits, ids).reshape(rows, n)
+    for entry in (B.nq_gather_qmm, B.nq_gather_qmm_row_exact):
+        y = entry(xs, cs, ss, bs, gs, bits, dev(ids))
+        assert_rows_close(values(host(y)).reshape(rows, n), y_ref, 1e-2, f"{bits}-bit gather")
+        for r in range(rows):
+            yr = B.nq_qmm_row_exact(xs[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+            assert bits_equal(yr, y[r]), r
+
+
 # ------------------------------------------------------------------ determinism and edges
 
 
