@@ -40,9 +40,17 @@ def lib():
                                             _c_int, _c_p, _c_p, _c_i64, _c_p]
         L.oracle_gather_qmm_f64.argtypes = [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                                             _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p]
+        L.oracle_qmm_nt_f64.argtypes = [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_int,
+                                        _c_i64, _c_int, _c_int, _c_p]
+        L.oracle_qmm_grad_sb_f64.argtypes = [_c_p, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_p,
+                                             _c_i64, _c_int, _c_int, _c_p, _c_p]
+        L.oracle_gather_qmm_lhs_f64.argtypes = [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
+                                                _c_p, _c_p, _c_int, _c_i64, _c_i64, _c_int, _c_int,
+                                                _c_p, _c_p, _c_p]
         L.oracle_bf16_round.argtypes = [_c_p, _c_p, _c_i64]
         for f in ("oracle_quantize", "oracle_dequantize", "oracle_dequantize_f64",
                   "oracle_qmm_f64", "oracle_qmm_sample_f64", "oracle_gather_qmm_f64",
+                  "oracle_qmm_nt_f64", "oracle_qmm_grad_sb_f64", "oracle_gather_qmm_lhs_f64",
                   "oracle_bits_supported", "oracle_group_supported", "oracle_threads"):
             getattr(L, f).restype = _c_int
         L.oracle_bf16_round.restype = None
@@ -177,4 +185,57 @@ def gather_qmm_f64(x, codes, scales, biases, group_size, bits, idx):
                                      _ptr(idx), _ptr(y))
     if rc:
         raise ValueError("oracle_gather_qmm_f64 rejected its arguments")
+    return y
+
+
+def qmm_nt_f64(x, codes, scales, biases, group_size, bits):
+    """x [m, ni] times the dequantized weights as stored, [ni, nc] (grouped
+    along nc) -> y [m, nc] float64: the transpose = false product."""
+    x, codes, scales, biases = _c(x), _c(codes), _c(scales), _c(biases)
+    m, ni = x.shape
+    assert scales.shape[0] == ni
+    nc = scales.shape[1] * group_size
+    y = np.zeros((m, nc), dtype=np.float64)
+    rc = lib().oracle_qmm_nt_f64(_ptr(x), _dt(x), m, ni, _ptr(codes), _ptr(scales), _ptr(biases),
+                                 _dt(scales), nc, group_size, bits, _ptr(y))
+    if rc:
+        raise ValueError("oracle_qmm_nt_f64 rejected its arguments")
+    return y
+
+
+def qmm_grad_sb_f64(x, dy, codes, group_size, bits):
+    """Derivatives of sum(dy * qmm(x, w)) for the scales and biases of w:
+    x [m, k], dy [m, n], codes [n, k*bits/32] -> (ds, db) [n, k/gs] float64."""
+    x, dy, codes = _c(x), _c(dy), _c(codes)
+    m, k = x.shape
+    n = dy.shape[1]
+    assert dy.shape[0] == m and codes.shape[0] == n
+    ds = np.zeros((n, k // group_size), dtype=np.float64)
+    db = np.zeros_like(ds)
+    rc = lib().oracle_qmm_grad_sb_f64(_ptr(x), _dt(x), _ptr(dy), _dt(dy), m, k, _ptr(codes), n,
+                                      group_size, bits, _ptr(ds), _ptr(db))
+    if rc:
+        raise ValueError("oracle_qmm_grad_sb_f64 rejected its arguments")
+    return ds, db
+
+
+def gather_qmm_lhs_f64(x, codes, scales, biases, group_size, bits, lhs, rhs):
+    """x [b, l, k]; lhs [rows] (x item per output row, or None for the
+    identity) and rhs [rows] (expert) -> y [rows, l, n] float64."""
+    x, codes, scales, biases = _c(x), _c(codes), _c(scales), _c(biases)
+    rhs = _c(np.asarray(rhs, dtype=np.uint32))
+    lhs_p = None
+    if lhs is not None:
+        lhs = _c(np.asarray(lhs, dtype=np.uint32))
+        assert lhs.shape == rhs.shape
+        lhs_p = _ptr(lhs)
+    b, l, k = x.shape
+    rows = rhs.shape[0]
+    e, n = scales.shape[0], scales.shape[1]
+    y = np.zeros((rows, l, n), dtype=np.float64)
+    rc = lib().oracle_gather_qmm_lhs_f64(_ptr(x), _dt(x), b, rows, l, k, _ptr(codes), _ptr(scales),
+                                         _ptr(biases), _dt(scales), e, n, group_size, bits, lhs_p,
+                                         _ptr(rhs), _ptr(y))
+    if rc:
+        raise ValueError("oracle_gather_qmm_lhs_f64 rejected its arguments")
     return y

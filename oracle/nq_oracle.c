@@ -328,3 +328,103 @@ int oracle_gather_qmm_f64(const void *x, int x_dt, int64_t rows, int64_t l, int6
     }
     return 0;
 }
+
+/* ---- products with the untransposed weights, and derivatives ------------- */
+
+/* y[r, c] = sum_i x[r, i] * w_hat[i, c]: x times the weights as stored, the
+ * `transpose = false` product ("Quantization" page, "Affine" example's
+ * quantized_matmul flag).  The quantized matrix has rows i (ni of them) and
+ * columns c (nc), grouped along c.  fp64, natural i order.  y: [m, nc]. */
+int oracle_qmm_nt_f64(const void *x, int x_dt, int64_t m, int64_t ni, const uint32_t *codes,
+                      const void *scales, const void *biases, int sb_dt, int64_t nc, int gs,
+                      int bits, double *y)
+{
+    if (!oracle_bits_supported(bits) || !oracle_group_supported(gs) || nc % gs != 0) return -1;
+    const int64_t G = nc / gs;
+    const int64_t P = nc * bits / 32;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t c = 0; c < nc; ++c) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < ni; ++i) {
+                double s = load_f(scales, sb_dt, i * G + c / gs);
+                double b = load_f(biases, sb_dt, i * G + c / gs);
+                double wv = s * (double)get_code(codes + i * P, c, bits) + b;
+                acc += (double)load_f(x, x_dt, r * ni + i) * wv;
+            }
+            y[r * nc + c] = acc;
+        }
+    return 0;
+}
+
+/* Derivatives of L = sum_{r,c} dy[r, c] * y[r, c], y = x times the
+ * transposed weights (w_hat[c, kk] = s[c, g] * q[c, kk] + b[c, g], g = kk / gs),
+ * with respect to the scales and biases ("Quantization" page, "Training
+ * through quantized weights"):
+ *   ds[c, g] = sum_r dy[r, c] * sum_{kk in g} x[r, kk] * q[c, kk]
+ *   db[c, g] = sum_r dy[r, c] * sum_{kk in g} x[r, kk]
+ * fp64, r outer and kk inner in natural order.  x: [m, k]; dy: [m, n];
+ * codes: [n, k*bits/32]; ds, db: [n, k/gs] double.  (The derivative for x is
+ * dy times the weights as stored: oracle_qmm_nt_f64 with ni = n, nc = k.) */
+int oracle_qmm_grad_sb_f64(const void *x, int x_dt, const void *dy, int dy_dt, int64_t m, int64_t k,
+                           const uint32_t *codes, int64_t n, int gs, int bits, double *ds, double *db)
+{
+    if (!oracle_bits_supported(bits) || !oracle_group_supported(gs) || k % gs != 0) return -1;
+    const int64_t G = k / gs;
+    const int64_t P = k * bits / 32;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t g = 0; g < G; ++g) {
+            double as = 0.0, ab = 0.0;
+            for (int64_t r = 0; r < m; ++r) {
+                const double d = load_f(dy, dy_dt, r * n + c);
+                double xq = 0.0, xs = 0.0;
+                for (int64_t kk = g * gs; kk < (g + 1) * gs; ++kk) {
+                    const double xv = load_f(x, x_dt, r * k + kk);
+                    xq += xv * (double)get_code(codes + c * P, kk, bits);
+                    xs += xv;
+                }
+                as += d * xq;
+                ab += d * xs;
+            }
+            ds[c * G + g] = as;
+            db[c * G + g] = ab;
+        }
+    return 0;
+}
+
+/* gather_qmm with both index arrays ("Mixture of experts": the call takes an
+ * optional left index and the expert index).  x: [b, l, k]; lhs [rows]
+ * selects the x item of each output row (null: item r), rhs [rows] the
+ * expert.  y[r, j, :] = x[lhs[r], j, :] times the transposed weights of
+ * expert rhs[r]; zero rows for rhs >= e (lhs >= b is outside the contract of
+ * the callers and also gives a zero row here).  y: [rows, l, n] double. */
+int oracle_gather_qmm_lhs_f64(const void *x, int x_dt, int64_t b, int64_t rows, int64_t l, int64_t k,
+                              const uint32_t *codes, const void *scales, const void *biases,
+                              int sb_dt, int64_t e, int64_t n, int gs, int bits,
+                              const uint32_t *lhs, const uint32_t *rhs, double *y)
+{
+    if (!oracle_bits_supported(bits) || !oracle_group_supported(gs) || k % gs != 0) return -1;
+    const int64_t G = k / gs;
+    const int64_t P = k * bits / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t xi = lhs ? (int64_t)lhs[r] : r;
+        const uint32_t ex = rhs[r];
+        for (int64_t j = 0; j < l; ++j)
+            for (int64_t c = 0; c < n; ++c) {
+                double acc = 0.0;
+                if ((int64_t)ex < e && xi < b) {
+                    const int64_t wr = (int64_t)ex * n + c;
+                    for (int64_t kk = 0; kk < k; ++kk) {
+                        double s = load_f(scales, sb_dt, wr * G + kk / gs);
+                        double bb = load_f(biases, sb_dt, wr * G + kk / gs);
+                        double wv = s * (double)get_code(codes + wr * P, kk, bits) + bb;
+                        acc += (double)load_f(x, x_dt, (xi * l + j) * k + kk) * wv;
+                    }
+                }
+                y[(r * l + j) * n + c] = acc;
+            }
+    }
+    return 0;
+}

@@ -390,3 +390,73 @@ def test_workload_generator_is_seeded():
     assert a["w"].shape == (256, 512) and a["x"].shape == (4, 512)
     rng = np.random.default_rng(0)
     assert np.array_equal(a["w"], rng.standard_normal((256, 512), dtype=np.float32))
+
+
+# ---- the product with the weights as stored, derivatives, left indices
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (3, 32), (8, 128)])
+def test_qmm_nt_is_x_times_dequantized(oracle_mod, bits, gs):
+    """transpose = false: x [m, ni] times the dequantized [ni, nc] matrix,
+    checked against numpy's matmul of the oracle's fp64 dequantization."""
+    w, x = synthetic.random_case(bits + gs, (24, 3 * gs), (5, 24), 1.0, "f32")
+    c, s, b = oracle_mod.quantize(w, gs, bits)
+    y = oracle_mod.qmm_nt_f64(x, c, s, b, gs, bits)
+    ref = x.astype(np.float64) @ oracle_mod.dequantize_f64(c, s, b, gs, bits)
+    assert y.shape == (5, 3 * gs)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (5, 32), (2, 128)])
+def test_adjoint_identity(oracle_mod, bits, gs):
+    """<dy, x . w^T> = <dy . w, x>: the transpose = false product is the
+    adjoint of the product, which is the derivative for the activations."""
+    n, k, m = 40, 2 * gs, 6
+    w, x = synthetic.random_case(7 * bits, (n, k), (m, k), 1.0, "f32")
+    _, dy = synthetic.random_case(8 * bits, (1, 1), (m, n), 1.0, "f32")
+    c, s, b = oracle_mod.quantize(w, gs, bits)
+    lhs = np.sum(dy.astype(np.float64) * oracle_mod.qmm_f64(x, c, s, b, gs, bits))
+    dx = oracle_mod.qmm_nt_f64(dy, c, s, b, gs, bits)
+    rhs = np.sum(dx * x.astype(np.float64))
+    assert dx.shape == (m, k)
+    assert abs(lhs - rhs) <= 1e-11 * (np.abs(dy).sum() * np.abs(x).max() * np.abs(w).max() * k)
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 32), (3, 64), (8, 32)])
+def test_grad_scales_biases_by_linearity(oracle_mod, bits, gs):
+    """The loss sum(dy * y) is linear in every scale and bias: with a one-hot
+    scale matrix and zero biases the forward product gives exactly that
+    scale's derivative, and likewise for a bias."""
+    n, k, m = 3, 2 * gs, 4
+    w, x = synthetic.random_case(11 * bits, (n, k), (m, k), 1.0, "f32")
+    _, dy = synthetic.random_case(12 * bits, (1, 1), (m, n), 1.0, "f32")
+    c, s, b = oracle_mod.quantize(w, gs, bits)
+    ds, db = oracle_mod.qmm_grad_sb_f64(x, dy, c, gs, bits)
+    assert ds.shape == db.shape == (n, k // gs)
+    zero = np.zeros_like(s)
+    for cc in range(n):
+        for g in range(k // gs):
+            one = zero.copy()
+            one[cc, g] = 1.0
+            ls = np.sum(dy.astype(np.float64) * oracle_mod.qmm_f64(x, c, one, zero, gs, bits))
+            lb = np.sum(dy.astype(np.float64) * oracle_mod.qmm_f64(x, c, zero, one, gs, bits))
+            assert abs(ds[cc, g] - ls) <= 1e-12 * max(1.0, abs(ls))
+            assert abs(db[cc, g] - lb) <= 1e-12 * max(1.0, abs(lb))
+
+
+def test_gather_with_left_indices(oracle_mod):
+    """Left indices pick the x item of each output row: none is the plain
+    gather, and with one expert it is the product of the picked rows."""
+    w, x = synthetic.random_case(13, (3, 16, 128), (4, 2, 128), 1.0, "f32")
+    c, s, b = oracle_mod.quantize(w, 64, 4)
+    rhs = np.array([2, 0, 0, 1, 2, 5], np.uint32)
+    lhs = np.array([3, 3, 0, 1, 2, 0], np.uint32)
+    base = oracle_mod.gather_qmm_lhs_f64(x, c, s, b, 64, 4, None, rhs[:4])
+    assert np.array_equal(base, oracle_mod.gather_qmm_f64(x, c, s, b, 64, 4, rhs[:4]))
+    y = oracle_mod.gather_qmm_lhs_f64(x, c, s, b, 64, 4, lhs, rhs)
+    assert y.shape == (6, 2, 16) and np.all(y[5] == 0)
+    for r in range(5):
+        assert np.array_equal(y[r], oracle_mod.qmm_f64(x[lhs[r]], c[rhs[r]], s[rhs[r]], b[rhs[r]], 64, 4))
+    y1 = oracle_mod.gather_qmm_lhs_f64(x, c[:1], s[:1], b[:1], 64, 4, lhs, np.zeros(6, np.uint32))
+    assert np.array_equal(y1.reshape(12, 16),
+                          oracle_mod.qmm_f64(x[lhs].reshape(12, 128), c[0], s[0], b[0], 64, 4))
