@@ -16,6 +16,10 @@ from ._binding import (  # noqa: F401
     nq_gather_qmm_row_exact,
     nq_gather_qmm_workspace_bytes,
     nq_qmm,
+    nq_qmm_grad_scales_biases,
+    nq_qmm_notrans,
+    nq_qmm_notrans_row_exact,
+    nq_qmm_notrans_workspace_bytes,
     nq_qmm_plan,
     nq_qmm_row_exact,
     nq_qmm_with_plan,

@@ -60,11 +60,17 @@ _SIGNATURES = {
                       _I32, _P, _P, _SZ, _P],
     "nq_gather_qmm_row_exact": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32,
                                 _I32, _P, _I32, _P, _P, _SZ, _P],
+    "nq_qmm_notrans_workspace_bytes": [_I64, _I64, _I64, _I32, _I32, _I32, _I32],
+    "nq_qmm_notrans": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P],
+    "nq_qmm_notrans_row_exact": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P,
+                                 _SZ, _P],
+    "nq_qmm_grad_scales_biases": [_P, _P, _I32, _I64, _I64, _P, _I64, _I32, _I32, _P, _P, _I32, _P],
     "nq_status_string": [_I32],
     "nq_last_error": [],
     "nq_version": [],
 }
 _RESTYPES = {"nq_qmm_workspace_bytes": _SZ, "nq_gather_qmm_workspace_bytes": _SZ,
+             "nq_qmm_notrans_workspace_bytes": _SZ,
              "nq_status_string": ctypes.c_char_p, "nq_last_error": ctypes.c_char_p,
              "nq_version": ctypes.c_char_p}
 
@@ -228,6 +234,75 @@ def nq_qmm_with_plan(plan, x, codes, scales, biases, group_size, bits, y=None, w
                      stream=None):
     return _qmm_call(None, x, codes, scales, biases, group_size, bits, y, workspace, stream,
                      plan=plan)
+
+
+def nq_qmm_notrans_workspace_bytes(m, ni, nc, group_size, bits, x_dtype, row_exact=False):
+    torch = _torch()
+    xd = NQ_F32 if x_dtype == torch.float32 else NQ_BF16
+    return load_library().nq_qmm_notrans_workspace_bytes(m, ni, nc, group_size, bits, xd,
+                                                         int(bool(row_exact)))
+
+
+def _notrans_call(entry, x, codes, scales, biases, group_size, bits, y, workspace, stream):
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases)):
+        _contig(name, t)
+    m, ni = x.shape
+    nc = scales.shape[1] * group_size
+    if scales.shape[0] != ni or codes.shape != (ni, words_per_row(nc, bits)):
+        raise ValueError("codes/scales shapes do not match x and the quantization")
+    if y is None:
+        y = torch.empty((m, nc), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        need = lib.nq_qmm_notrans_workspace_bytes(m, ni, nc, group_size, bits, _dt(x),
+                                                  int(entry.endswith("row_exact")))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(getattr(lib, entry)(_ptr(x), _dt(x), m, ni, _ptr(codes), _ptr(scales), _ptr(biases),
+                               _dt(scales), nc, group_size, bits, _ptr(y), _ptr(workspace),
+                               ws_bytes, _stream(stream)))
+    return y
+
+
+def nq_qmm_notrans(x, codes, scales, biases, group_size, bits, y=None, workspace=None, stream=None):
+    """y [m, nc] = x [m, ni] times the dequantized weights as stored ([ni, nc],
+    grouped along nc): the transpose = false product.  With the forward
+    weights and x = dy it is the derivative for the activations."""
+    return _notrans_call("nq_qmm_notrans", x, codes, scales, biases, group_size, bits, y, workspace,
+                         stream)
+
+
+def nq_qmm_notrans_row_exact(x, codes, scales, biases, group_size, bits, y=None, workspace=None,
+                             stream=None):
+    """nq_qmm_notrans whose every row is bit-equal to the one-row product."""
+    return _notrans_call("nq_qmm_notrans_row_exact", x, codes, scales, biases, group_size, bits, y,
+                         workspace, stream)
+
+
+def nq_qmm_grad_scales_biases(x, dy, codes, group_size, bits, out_dtype=None, dscales=None,
+                              dbiases=None, stream=None):
+    """Derivatives of sum(dy * nq_qmm(x, w)) for w's scales and biases:
+    x [m, k], dy [m, n] (same dtype), codes [n, k*bits/32] -> (dscales,
+    dbiases) [n, k/gs] in out_dtype (default: x's dtype)."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("x", x), ("dy", dy), ("codes", codes)):
+        _contig(name, t)
+    m, k = x.shape
+    n = dy.shape[1]
+    if dy.shape[0] != m or dy.dtype != x.dtype or codes.shape != (n, words_per_row(k, bits)):
+        raise ValueError("x, dy and codes do not match")
+    od = out_dtype or x.dtype
+    if dscales is None:
+        dscales = torch.empty((n, k // group_size), dtype=od, device=x.device)
+    if dbiases is None:
+        dbiases = torch.empty((n, k // group_size), dtype=od, device=x.device)
+    _check(lib.nq_qmm_grad_scales_biases(_ptr(x), _ptr(dy), _dt(x), m, k, _ptr(codes), n, group_size,
+                                         bits, _ptr(dscales), _ptr(dbiases), _dt(dscales),
+                                         _stream(stream)))
+    return dscales, dbiases
 
 
 def nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, x_dtype, sb_dtype,

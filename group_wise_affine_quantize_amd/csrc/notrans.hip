@@ -1,0 +1,480 @@
+// Products with the weights as stored (transpose = false), and the
+// derivatives of quantized products for the scales and biases.
+//
+// Method: "Quantization" page of the nuvec documentation -- section "Affine"
+// (the quantized_matmul flag: x times the weights as stored instead of their
+// transpose; the weights' groups then run along the output columns) and
+// section "Training through quantized weights" (derivative rules for the
+// activations, and in affine mode for the scales and biases; the one for the
+// activations is dy times the weights as stored, i.e. this file's product
+// with the forward weights, whose rows are the forward outputs).
+//
+// Notation: the quantized matrix has ni rows of nc columns, grouped along the
+// columns: codes [ni, nc*bits/32], scales and biases [ni, nc/gs];
+// y[m, c] = sum_i x[m, i] * w_hat[i, c], w_hat = fmaf(s, q, b) in fp32.
+#include <algorithm>
+
+#include "nq_device.h"
+#include "nq_internal.h"
+
+namespace nqk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Few activation rows.  Lane L of a workgroup owns the 32 columns
+// [2048 bx + 32 L, +32) -- `bits` consecutive code words of every row, read
+// coalesced; the four waves take the rows i0 + w, i0 + w + 4, ... of the
+// workgroup's row range, each adding x[m, i] * w_hat[i, c] in increasing i;
+// waves 1-3 hand their sums to wave 0 through LDS (added in wave order), and
+// the workgroup's partial sums go to the workspace.  A second kernel adds the
+// row ranges' partials in range order.  The row ranges depend only on ni and
+// nc, and nothing in a row's arithmetic depends on the other rows, so every
+// row is bit-equal to its one-row product.
+
+template <typename XT, typename ST>
+struct NtParams {
+    const XT *x;
+    const uint32_t *codes;
+    const ST *scales;
+    const ST *biases;
+    float *part;   // [nsplit][MR][nc]
+    int64_t m0, ni, nc, words_per_row, groups_per_row, rows_per_split;
+    int mrows, lg_gs;
+};
+
+constexpr int kNtWaves = 4;
+
+template <int BITS, typename XT, typename ST, int MR>
+__global__ void __launch_bounds__(64 * kNtWaves) qmm_nt_partial_kernel(NtParams<XT, ST> p)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t c0 = (int64_t)blockIdx.x * kStepElems + lane * kLaneChunk;
+    const bool cv = c0 < p.nc;   // nc is a multiple of 32: then c0 + 32 <= nc
+    const int64_t cc = cv ? c0 : 0;
+    const int64_t g = cc >> p.lg_gs;
+    const int64_t i0 = (int64_t)blockIdx.y * p.rows_per_split;
+    const int64_t i1 = min(p.ni, i0 + p.rows_per_split);
+    float acc[MR][kLaneChunk];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < kLaneChunk; ++j) acc[m][j] = 0.0f;
+    for (int64_t i = i0 + wave; i < i1; i += kNtWaves) {
+        const uint32_t *src = p.codes + i * p.words_per_row + (cc / kLaneChunk) * BITS;
+        uint32_t w[BITS];
+#pragma unroll
+        for (int u = 0; u < BITS; ++u) w[u] = src[u];
+        const float s = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
+        const float b = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
+        float xv[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) xv[m] = Elt<XT>::load(p.x, (p.m0 + min(m, p.mrows - 1)) * p.ni + i);
+#pragma unroll
+        for (int j = 0; j < kLaneChunk; ++j) {
+            const float wv = fmaf(s, (float)code_at<BITS>(w, j), b);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) acc[m][j] = fmaf(xv[m], wv, acc[m][j]);
+        }
+    }
+    __shared__ float red[kNtWaves - 1][MR][kLaneChunk][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int j = 0; j < kLaneChunk; ++j) red[wave - 1][m][j][lane] = acc[m][j];
+    }
+    __syncthreads();
+    if (wave != 0 || !cv) return;
+#pragma unroll
+    for (int w2 = 0; w2 < kNtWaves - 1; ++w2)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int j = 0; j < kLaneChunk; ++j) acc[m][j] += red[w2][m][j][lane];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m >= p.mrows) break;
+        float4 *dst = reinterpret_cast<float4 *>(p.part + ((int64_t)blockIdx.y * MR + m) * p.nc + c0);
+#pragma unroll
+        for (int j = 0; j < kLaneChunk / 4; ++j)
+            dst[j] = make_float4(acc[m][4 * j], acc[m][4 * j + 1], acc[m][4 * j + 2], acc[m][4 * j + 3]);
+    }
+}
+
+// y[m0 + m, c] = partials of the row ranges, added in range order.
+template <typename XT, int MR>
+__global__ void __launch_bounds__(256) qmm_nt_reduce_kernel(const float *part, XT *y, int64_t m0, int mrows,
+                                                            int64_t nc, int nsplit)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)mrows * nc) return;
+    const int64_t m = idx / nc, c = idx % nc;
+    float s = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) s += part[((int64_t)sp * MR + m) * nc + c];
+    Elt<XT>::store(y, (m0 + m) * nc + c, s);
+}
+
+// ---------------------------------------------------------------------------
+// Many rows (bf16 x): 128 x 128 tiles of y with bf16 MFMA, as the tiled
+// product with the transposed weights, but the weight tile of a K step (32
+// rows i of 128 columns c) is dequantized from the rows as stored and written
+// to LDS transposed, [c][i], so that the B operands read 8 consecutive i of
+// one column.  Each thread dequantizes 16 columns of one row (a bit-offset run
+// of codes, realigned) into round_bf16(fmaf(s, q, b)).
+
+template <typename ST>
+struct NtTiledParams {
+    const bf16_bits *x;   // [m, ni]
+    bf16_bits *y;         // [m, nc]
+    const uint32_t *codes;
+    const ST *scales;
+    const ST *biases;
+    int64_t m, ni, nc, words_per_row, groups_per_row;
+    int lg_gs;
+};
+
+constexpr int kNtTM = 128, kNtTN = 128, kNtBK = 32, kNtLd = kNtBK + 8;
+
+template <int BITS, typename ST>
+__global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
+{
+    __shared__ __attribute__((aligned(16))) bf16_bits xs[kNtTM * kNtLd];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[kNtTN * kNtLd];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kNtTM;
+    const int64_t c0 = (int64_t)blockIdx.x * kNtTN;
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+    const int lrow = tid >> 1, lhalf = tid & 1;          // x loader: one row, 16 elements
+    const int64_t xm = m0 + lrow;
+    const int wrow = tid >> 3, wcol = 16 * (tid & 7);    // weight loader: one row, 16 columns
+    const int64_t cb = c0 + wcol;
+    const bool wv_ok = cb < p.nc;                         // nc % 32 == 0: then cb + 16 <= nc
+    const int64_t g = (wv_ok ? cb : 0) >> p.lg_gs;
+    constexpr int NW = (BITS + 1) / 2;
+
+    for (int64_t i0 = 0; i0 < p.ni; i0 += kNtBK) {       // ni is a multiple of 32
+        uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
+        if (xm < p.m) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(p.x + xm * p.ni + i0 + 16 * lhalf);
+            xa = src[0];
+            xb = src[1];
+        }
+        uint32_t outw[8];
+        if (wv_ok) {
+            const int64_t i = i0 + wrow;
+            const float s = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
+            const float b = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
+            const int64_t bit0 = cb * BITS;
+            const uint32_t *src = p.codes + i * p.words_per_row + (bit0 >> 5);
+            const uint32_t sh = (uint32_t)(bit0 & 31);
+            uint32_t raw[NW], cw[NW];
+#pragma unroll
+            for (int u = 0; u < NW; ++u) raw[u] = src[u];
+#pragma unroll
+            for (int u = 0; u < NW; ++u) cw[u] = __builtin_amdgcn_alignbit(u + 1 < NW ? raw[u + 1] : 0u, raw[u], sh);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float v0 = fmaf(s, (float)code_at<BITS>(cw, 2 * u), b);
+                const float v1 = fmaf(s, (float)code_at<BITS>(cw, 2 * u + 1), b);
+                outw[u] = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) outw[u] = 0u;
+        }
+        __syncthreads();   // the previous step's MFMA reads are done
+        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * kNtLd + 16 * lhalf);
+        xd[0] = xa;
+        xd[1] = xb;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            ws[(wcol + 2 * u) * kNtLd + wrow] = (bf16_bits)(outw[u] & 0xffffu);
+            ws[(wcol + 2 * u + 1) * kNtLd + wrow] = (bf16_bits)(outw[u] >> 16);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kNtBK / 16; ++ks) {
+            const int kk = ks * 16 + 8 * (lane >> 5);
+            bf16x8_t a[2], bo[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8_t *>(xs + (wm * 64 + i * 32 + (lane & 31)) * kNtLd + kk);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bo[j] = *reinterpret_cast<const bf16x8_t *>(ws + (wn * 64 + j * 32 + (lane & 31)) * kNtLd + kk);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bo[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = c0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < p.m && col < p.nc) p.y[row * p.nc + col] = (bf16_bits)f32_to_bf16(acc[i][j][v]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Derivatives for the scales and biases of the product with the transposed
+// weights (codes [n, k*bits/32]):
+//   ds[c, g] = sum_m dy[m, c] * sum_{k in g} x[m, k] q[c, k]
+//   db[c, g] = sum_m dy[m, c] * sum_{k in g} x[m, k]
+// A wave owns RW weight rows c; in K step t lane L owns the 32 columns
+// [2048 t + 32 L, +32) (inside one group).  For every activation row m the
+// lane forms sum x q and sum x over its columns and adds dy[m, c] times them,
+// in increasing m; the gs / 32 lanes of a group are then added by a fixed xor
+// tree, and the group's first lane stores.
+
+template <typename XT, typename GT>
+struct GradParams {
+    const XT *x;    // [m, k]
+    const XT *dy;   // [m, n]
+    const uint32_t *codes;
+    GT *ds;         // [n, k/gs]
+    GT *db;
+    int64_t m, k, n, words_per_row, groups_per_row;
+    int lg_gs, steps;
+};
+
+constexpr int kGradRows = 4;   // weight rows per wave
+
+template <int OFF>
+__device__ __forceinline__ float xor_sum(float v)
+{
+    // v + v from lane (lane ^ OFF), OFF in {1, 2}: DPP quad permutes
+    const int iv = __float_as_int(v);
+    const int r = OFF == 1 ? __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true)
+                           : __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);
+    return v + __int_as_float(r);
+}
+
+template <int BITS, typename XT, typename GT>
+__global__ void __launch_bounds__(256) grad_sb_kernel(GradParams<XT, GT> p)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * kGradRows;
+    const int lpg = 1 << (p.lg_gs - 5);   // lanes per group: 1, 2 or 4
+    for (int t = 0; t < p.steps; ++t) {
+        const int64_t e0 = (int64_t)t * kStepElems + lane * kLaneChunk;
+        const bool on = e0 < p.k;
+        const int64_t ec = on ? e0 : 0;
+        uint32_t w[kGradRows][BITS];
+#pragma unroll
+        for (int r = 0; r < kGradRows; ++r) {
+            const int64_t c = min(r0 + r, p.n - 1);
+            const uint32_t *src = p.codes + c * p.words_per_row + (ec / kLaneChunk) * BITS;
+#pragma unroll
+            for (int u = 0; u < BITS; ++u) w[r][u] = src[u];
+        }
+        float as[kGradRows], ab[kGradRows];
+#pragma unroll
+        for (int r = 0; r < kGradRows; ++r) as[r] = ab[r] = 0.0f;
+        for (int64_t m = 0; m < p.m; ++m) {
+            float xf[kLaneChunk];
+            float X = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kLaneChunk; ++j) {
+                xf[j] = Elt<XT>::load(p.x, m * p.k + ec + j);
+                X += xf[j];
+            }
+#pragma unroll
+            for (int r = 0; r < kGradRows; ++r) {
+                float T = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kLaneChunk; ++j) T = fmaf(xf[j], (float)code_at<BITS>(w[r], j), T);
+                const float d = Elt<XT>::load(p.dy, m * p.n + min(r0 + r, p.n - 1));
+                as[r] = fmaf(d, T, as[r]);
+                ab[r] = fmaf(d, X, ab[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kGradRows; ++r) {
+            if (lpg >= 2) as[r] = xor_sum<1>(as[r]), ab[r] = xor_sum<1>(ab[r]);
+            if (lpg >= 4) as[r] = xor_sum<2>(as[r]), ab[r] = xor_sum<2>(ab[r]);
+            if (on && (lane & (lpg - 1)) == 0 && r0 + r < p.n) {
+                const int64_t o = (r0 + r) * p.groups_per_row + (e0 >> p.lg_gs);
+                Elt<GT>::store(p.ds, o, as[r]);
+                Elt<GT>::store(p.db, o, ab[r]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+
+namespace {
+
+int lg_of(int gs) { return gs == 32 ? 5 : gs == 64 ? 6 : 7; }
+
+template <int BITS, typename XT, typename ST>
+hipError_t qmm_nt_run(const NtLaunch &a, hipStream_t stream)
+{
+    constexpr int MR = kNtRowsPerChunk;
+    NtParams<XT, ST> p;
+    p.x = static_cast<const XT *>(a.x);
+    p.codes = a.codes;
+    p.scales = static_cast<const ST *>(a.scales);
+    p.biases = static_cast<const ST *>(a.biases);
+    p.part = static_cast<float *>(a.workspace);
+    p.ni = a.ni;
+    p.nc = a.nc;
+    p.words_per_row = a.nc * BITS / 32;
+    p.groups_per_row = a.nc / a.gs;
+    p.lg_gs = lg_of(a.gs);
+    const int nsplit = qmm_nt_splits(a.ni, a.nc);
+    p.rows_per_split = (a.ni + nsplit - 1) / nsplit;
+    const unsigned gx = (unsigned)((a.nc + kStepElems - 1) / kStepElems);
+    for (int64_t m0 = 0; m0 < a.m; m0 += MR) {
+        p.m0 = m0;
+        p.mrows = (int)std::min<int64_t>(MR, a.m - m0);
+        qmm_nt_partial_kernel<BITS, XT, ST, MR><<<dim3(gx, (unsigned)nsplit), dim3(64 * kNtWaves), 0, stream>>>(p);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const int64_t outs = (int64_t)p.mrows * a.nc;
+        qmm_nt_reduce_kernel<XT, MR><<<dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, stream>>>(
+            p.part, static_cast<XT *>(a.y), m0, p.mrows, a.nc, nsplit);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+template <int BITS, typename ST>
+hipError_t tiled_nt_run(const NtLaunch &a, hipStream_t stream)
+{
+    NtTiledParams<ST> p;
+    p.x = static_cast<const bf16_bits *>(a.x);
+    p.y = static_cast<bf16_bits *>(a.y);
+    p.codes = a.codes;
+    p.scales = static_cast<const ST *>(a.scales);
+    p.biases = static_cast<const ST *>(a.biases);
+    p.m = a.m;
+    p.ni = a.ni;
+    p.nc = a.nc;
+    p.words_per_row = a.nc * BITS / 32;
+    p.groups_per_row = a.nc / a.gs;
+    p.lg_gs = lg_of(a.gs);
+    if (a.ni % kNtBK != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.nc + kNtTN - 1) / kNtTN), (unsigned)((a.m + kNtTM - 1) / kNtTM));
+    tiled_nt_kernel<BITS, ST><<<grid, dim3(256), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template <int BITS, typename XT, typename ST>
+hipError_t nt_bits(const NtLaunch &a, hipStream_t stream)
+{
+    if (a.tiled) {
+        if constexpr (sizeof(XT) == 2) return tiled_nt_run<BITS, ST>(a, stream);
+        else return hipErrorInvalidValue;
+    }
+    return qmm_nt_run<BITS, XT, ST>(a, stream);
+}
+
+template <typename XT, typename ST>
+hipError_t nt_dt(const NtLaunch &a, hipStream_t stream)
+{
+    switch (a.bits) {
+    case 1: return nt_bits<1, XT, ST>(a, stream);
+    case 2: return nt_bits<2, XT, ST>(a, stream);
+    case 3: return nt_bits<3, XT, ST>(a, stream);
+    case 4: return nt_bits<4, XT, ST>(a, stream);
+    case 5: return nt_bits<5, XT, ST>(a, stream);
+    case 6: return nt_bits<6, XT, ST>(a, stream);
+    case 8: return nt_bits<8, XT, ST>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int BITS, typename XT, typename GT>
+hipError_t grad_run(const GradLaunch &a, hipStream_t stream)
+{
+    GradParams<XT, GT> p;
+    p.x = static_cast<const XT *>(a.x);
+    p.dy = static_cast<const XT *>(a.dy);
+    p.codes = a.codes;
+    p.ds = static_cast<GT *>(a.ds);
+    p.db = static_cast<GT *>(a.db);
+    p.m = a.m;
+    p.k = a.k;
+    p.n = a.n;
+    p.words_per_row = a.k * BITS / 32;
+    p.groups_per_row = a.k / a.gs;
+    p.lg_gs = lg_of(a.gs);
+    p.steps = (int)((a.k + kStepElems - 1) / kStepElems);
+    const unsigned gx = (unsigned)((a.n + 4 * kGradRows - 1) / (4 * kGradRows));
+    grad_sb_kernel<BITS, XT, GT><<<dim3(gx), dim3(256), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template <typename XT, typename GT>
+hipError_t grad_dt(const GradLaunch &a, hipStream_t stream)
+{
+    switch (a.bits) {
+    case 1: return grad_run<1, XT, GT>(a, stream);
+    case 2: return grad_run<2, XT, GT>(a, stream);
+    case 3: return grad_run<3, XT, GT>(a, stream);
+    case 4: return grad_run<4, XT, GT>(a, stream);
+    case 5: return grad_run<5, XT, GT>(a, stream);
+    case 6: return grad_run<6, XT, GT>(a, stream);
+    case 8: return grad_run<8, XT, GT>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int qmm_nt_splits(int64_t ni, int64_t nc)
+{
+    // about 256 workgroups, and at least 16 rows (4 per wave) per range
+    const int64_t col_blocks = (nc + kStepElems - 1) / kStepElems;
+    const int64_t want = std::max<int64_t>(1, (256 + col_blocks - 1) / col_blocks);
+    const int64_t most = std::max<int64_t>(1, (ni + 15) / 16);
+    return (int)std::min<int64_t>(std::min(want, most), 65535);
+}
+
+size_t qmm_nt_ws_bytes(int64_t ni, int64_t nc)
+{
+    return (size_t)qmm_nt_splits(ni, nc) * kNtRowsPerChunk * (size_t)nc * sizeof(float);
+}
+
+hipError_t launch_qmm_nt(const NtLaunch &a, hipStream_t stream)
+{
+    if (a.x_dt == DT_F32) {
+        if (a.sb_dt == DT_F32) return nt_dt<float, float>(a, stream);
+        return nt_dt<float, bf16_bits>(a, stream);
+    }
+    if (a.sb_dt == DT_F32) return nt_dt<bf16_bits, float>(a, stream);
+    return nt_dt<bf16_bits, bf16_bits>(a, stream);
+}
+
+hipError_t launch_grad_sb(const GradLaunch &a, hipStream_t stream)
+{
+    if (a.x_dt == DT_F32) {
+        if (a.g_dt == DT_F32) return grad_dt<float, float>(a, stream);
+        return grad_dt<float, bf16_bits>(a, stream);
+    }
+    if (a.g_dt == DT_F32) return grad_dt<bf16_bits, float>(a, stream);
+    return grad_dt<bf16_bits, bf16_bits>(a, stream);
+}
+
+}  // namespace nqk

@@ -28,7 +28,6 @@ nq_status fail(nq_status st, const char *fmt, ...)
 
 bool dtype_ok(int dt) { return dt == NQ_F32 || dt == NQ_BF16; }
 int64_t dtype_bytes(int dt) { return dt == NQ_F32 ? 4 : 2; }
-const char *dtype_name(int dt) { return dt == NQ_F32 ? "f32" : dt == NQ_BF16 ? "bf16" : "?"; }
 
 // Bit widths of the stand-alone quantize/dequantize kernels and of the
 // product kernels ("an unsupported combination fails in the operation that
@@ -249,9 +248,157 @@ nq_status qmm_common(const char *op, int row_exact, const nq_plan *forced, const
     return run_qmm(op, plan, a, stream);
 }
 
+// ---- product with the weights as stored, derivatives
+
+// Route of the product with the weights as stored: 128 x 128 MFMA tiles for
+// many bf16 rows (the ranges of i a multiple of 32), else the matrix-vector
+// pair, which keeps every row bit-equal to its one-row product.  A pure
+// function of the sizes, dtypes and mode.
+bool nt_tiled(int64_t m, int64_t ni, int x_dt, int row_exact)
+{
+    return !row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && ni % 32 == 0;
+}
+
+nq_status qmm_nt_impl(const char *op, int row_exact, const void *x, nq_dtype x_dt, int64_t m,
+                      int64_t ni, const uint32_t *codes, const void *scales, const void *biases,
+                      nq_dtype sb_dt, int64_t nc, int32_t group_size, int32_t bits, void *y,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!dtype_ok(x_dt) || !dtype_ok(sb_dt))
+        return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, sb_dt=%d)", op, (int)x_dt, (int)sb_dt);
+    nq_status st = check_quant(op, group_size, bits, true);
+    if (st) return st;
+    if (m < 0 || ni < 0) return fail(NQ_ERR_SHAPE, "%s: negative size (m=%lld, ni=%lld)", op,
+                                     (long long)m, (long long)ni);
+    if ((st = check_dims(op, ni, nc, group_size))) return st;
+    if (m >= kMaxDim || (ni > 0 && m > kMaxElems / ni) || (nc > 0 && m > kMaxElems / nc))
+        return fail(NQ_ERR_SHAPE, "%s: m=%lld is too large", op, (long long)m);
+    if (m == 0 || nc == 0) return NQ_OK;
+    if (!y) return fail(NQ_ERR_NULL, "%s: y is null", op);
+    if (ni > 0 && (!x || !codes || !scales || !biases))
+        return fail(NQ_ERR_NULL, "%s: x, codes, scales and biases must be non-null", op);
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(y))
+        return fail(NQ_ERR_ALIGN, "%s: x, codes and y must be 16-byte aligned", op);
+    const int64_t sbb = dtype_bytes(sb_dt);
+    if (!aligned_to(scales, sbb) || !aligned_to(biases, sbb))
+        return fail(NQ_ERR_ALIGN, "%s: scales and biases must be aligned to %lld bytes", op, (long long)sbb);
+    const Span sy{y, m * nc * dtype_bytes(x_dt)};
+    const Span ins[4] = {{x, m * ni * dtype_bytes(x_dt)},
+                         {codes, ni * (nc * bits / 32) * 4},
+                         {scales, ni * (nc / group_size) * sbb},
+                         {biases, ni * (nc / group_size) * sbb}};
+    static const char *names[4] = {"x", "codes", "scales", "biases"};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(sy, ins[i])) return fail(NQ_ERR_ALIAS, "%s: y overlaps %s", op, names[i]);
+    nqk::NtLaunch a;
+    a.x = x;
+    a.y = y;
+    a.codes = codes;
+    a.scales = scales;
+    a.biases = biases;
+    a.workspace = workspace;
+    a.x_dt = x_dt;
+    a.sb_dt = sb_dt;
+    a.m = m;
+    a.ni = ni;
+    a.nc = nc;
+    a.gs = group_size;
+    a.bits = bits;
+    a.tiled = nt_tiled(m, ni, x_dt, row_exact);
+    if (!a.tiled) {
+        const size_t need = nqk::qmm_nt_ws_bytes(ni, nc);
+        if (!workspace || workspace_bytes < need)
+            return fail(NQ_ERR_WORKSPACE, "%s: needs a workspace of %zu bytes (got %zu)", op, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(NQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", op);
+        const Span sw{workspace, (int64_t)need};
+        if (overlap(sw, sy)) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps y", op);
+        for (int i = 0; i < 4; ++i)
+            if (overlap(sw, ins[i])) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps %s", op, names[i]);
+    }
+    return check_launch(op, nqk::launch_qmm_nt(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t nq_qmm_notrans_workspace_bytes(int64_t m, int64_t ni, int64_t nc, int32_t group_size,
+                                      int32_t bits, nq_dtype x_dt, int32_t row_exact)
+{
+    (void)group_size, (void)bits;
+    if (m <= 0 || ni < 0 || nc <= 0 || nt_tiled(m, ni, x_dt, row_exact)) return 0;
+    return nqk::qmm_nt_ws_bytes(ni, nc);
+}
+
+nq_status nq_qmm_notrans(const void *x, nq_dtype x_dt, int64_t m, int64_t ni, const uint32_t *codes,
+                         const void *scales, const void *biases, nq_dtype sb_dt, int64_t nc,
+                         int32_t group_size, int32_t bits, void *y, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    return qmm_nt_impl("nq_qmm_notrans", 0, x, x_dt, m, ni, codes, scales, biases, sb_dt, nc, group_size,
+                       bits, y, workspace, workspace_bytes, stream);
+}
+
+nq_status nq_qmm_notrans_row_exact(const void *x, nq_dtype x_dt, int64_t m, int64_t ni,
+                                   const uint32_t *codes, const void *scales, const void *biases,
+                                   nq_dtype sb_dt, int64_t nc, int32_t group_size, int32_t bits, void *y,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return qmm_nt_impl("nq_qmm_notrans_row_exact", 1, x, x_dt, m, ni, codes, scales, biases, sb_dt, nc,
+                       group_size, bits, y, workspace, workspace_bytes, stream);
+}
+
+nq_status nq_qmm_grad_scales_biases(const void *x, const void *dy, nq_dtype x_dt, int64_t m, int64_t k,
+                                    const uint32_t *codes, int64_t n, int32_t group_size, int32_t bits,
+                                    void *dscales, void *dbiases, nq_dtype g_dt, hipStream_t stream)
+{
+    const char *op = "nq_qmm_grad_scales_biases";
+    g_last_error.clear();
+    if (!dtype_ok(x_dt) || !dtype_ok(g_dt))
+        return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, g_dt=%d)", op, (int)x_dt, (int)g_dt);
+    nq_status st = check_quant(op, group_size, bits, true);
+    if (st) return st;
+    if (m < 0) return fail(NQ_ERR_SHAPE, "%s: negative m=%lld", op, (long long)m);
+    if ((st = check_dims(op, n, k, group_size))) return st;
+    if (m >= kMaxDim || (k > 0 && m > kMaxElems / k) || (n > 0 && m > kMaxElems / n))
+        return fail(NQ_ERR_SHAPE, "%s: m=%lld is too large", op, (long long)m);
+    if (n == 0 || k == 0) return NQ_OK;
+    if (!dscales || !dbiases || !codes)
+        return fail(NQ_ERR_NULL, "%s: codes, dscales and dbiases must be non-null", op);
+    if (m > 0 && (!x || !dy)) return fail(NQ_ERR_NULL, "%s: x and dy must be non-null", op);
+    if (!aligned_to(x, dtype_bytes(x_dt)) || !aligned_to(dy, dtype_bytes(x_dt)) || !aligned_to(codes, 4))
+        return fail(NQ_ERR_ALIGN, "%s: x, dy and codes must be aligned to their element size", op);
+    const int64_t gb = dtype_bytes(g_dt);
+    if (!aligned_to(dscales, gb) || !aligned_to(dbiases, gb))
+        return fail(NQ_ERR_ALIGN, "%s: dscales and dbiases must be aligned to %lld bytes", op, (long long)gb);
+    const int64_t G = k / group_size;
+    const Span outs[2] = {{dscales, n * G * gb}, {dbiases, n * G * gb}};
+    const Span ins[3] = {{x, m * k * dtype_bytes(x_dt)}, {dy, m * n * dtype_bytes(x_dt)},
+                         {codes, n * (k * bits / 32) * 4}};
+    static const char *onames[2] = {"dscales", "dbiases"}, *inames[3] = {"x", "dy", "codes"};
+    if (overlap(outs[0], outs[1])) return fail(NQ_ERR_ALIAS, "%s: dscales overlaps dbiases", op);
+    for (int o = 0; o < 2; ++o)
+        for (int i = 0; i < 3; ++i)
+            if (overlap(outs[o], ins[i]))
+                return fail(NQ_ERR_ALIAS, "%s: %s overlaps %s", op, onames[o], inames[i]);
+    nqk::GradLaunch a;
+    a.x = x;
+    a.dy = dy;
+    a.codes = codes;
+    a.ds = dscales;
+    a.db = dbiases;
+    a.x_dt = x_dt;
+    a.g_dt = g_dt;
+    a.m = m;
+    a.k = k;
+    a.n = n;
+    a.gs = group_size;
+    a.bits = bits;
+    return check_launch(op, nqk::launch_grad_sb(a, stream));
+}
+
 
 nq_status nq_quantize(const void *w, nq_dtype w_dt, int64_t n, int64_t k, int32_t group_size,
                       int32_t bits, uint32_t *codes, void *scales, void *biases, hipStream_t stream)

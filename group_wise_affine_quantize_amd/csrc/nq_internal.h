@@ -102,4 +102,40 @@ bool tiled_supported(int tile_m, int tile_n, int bits);
 // and uses 32-bit offsets).
 bool tiled_fits(int tile_m, int tile_n, int bits, int gs, int sb_dt, int64_t m, int64_t n, int64_t k);
 
+// Product with the weights as stored: y[m, c] = x[m, i] . w_hat[i, c], the
+// quantized matrix [ni, nc] grouped along c.  Few rows: row ranges of the
+// matrix give partial sums in the workspace (qmm_nt_ws_bytes), added by a
+// second kernel, kNtRowsPerChunk activation rows per launch pair.  tiled:
+// 128 x 128 bf16-MFMA tiles (x bf16, ni a multiple of 32), no workspace.
+constexpr int kNtRowsPerChunk = 2;
+struct NtLaunch {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const void *scales;
+    const void *biases;
+    void *workspace;
+    int x_dt, sb_dt;
+    int64_t m, ni, nc;
+    int gs, bits;
+    bool tiled;
+};
+int qmm_nt_splits(int64_t ni, int64_t nc);
+size_t qmm_nt_ws_bytes(int64_t ni, int64_t nc);
+hipError_t launch_qmm_nt(const NtLaunch &a, hipStream_t stream);
+
+// Derivatives of sum(dy * (x . w_hat^T)) for the scales and biases of w:
+// x [m, k], dy [m, n] (same dtype), codes [n, k*bits/32] -> ds, db [n, k/gs].
+struct GradLaunch {
+    const void *x;
+    const void *dy;
+    const uint32_t *codes;
+    void *ds;
+    void *db;
+    int x_dt, g_dt;
+    int64_t m, k, n;
+    int gs, bits;
+};
+hipError_t launch_grad_sb(const GradLaunch &a, hipStream_t stream);
+
 }  // namespace nqk

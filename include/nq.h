@@ -169,6 +169,55 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
                            int32_t bits, void *y, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* ---------------------------------------------------------------- weights as stored, derivatives */
+
+/* Workspace bytes nq_qmm_notrans / nq_qmm_notrans_row_exact need: 0 on the
+ * tiled route (row_exact = 0, m > NQ_ROW_INDEPENDENT_ROWS, bf16 x, ni a
+ * multiple of 32), else room for the partial sums of the matrix's row ranges
+ * (a function of ni and nc only), fully rewritten by every call. */
+size_t nq_qmm_notrans_workspace_bytes(int64_t m, int64_t ni, int64_t nc, int32_t group_size,
+                                      int32_t bits, nq_dtype x_dt, int32_t row_exact);
+
+/* The product with the weights as stored, x times w_hat ("Affine" example:
+ * quantized_matmul with the transpose flag off).  The quantized matrix has
+ * ni rows of nc columns grouped along the columns: codes [ni, nc*bits/32],
+ * scales and biases [ni, nc/group_size] (what nq_quantize makes of an
+ * [ni, nc] matrix).  x [m, ni] (x_dt); y [m, nc] (x_dt):
+ * y[r, c] = sum_i x[r, i] * (s[i, c/gs] * q[i, c] + b[i, c/gs]), fp32
+ * accumulation.  With the forward weights (ni = n, nc = k) and x = dy this is
+ * the derivative for the activations of nq_qmm ("Training through quantized
+ * weights").  Routes: see nq_qmm_notrans_workspace_bytes; the matrix-vector
+ * route splits the rows i into ranges fixed by (ni, nc) and adds their
+ * partial sums in range order, so rows are run-to-run identical and bit-equal
+ * to their one-row calls.  Errors as nq_qmm, nc % group_size != 0 is
+ * NQ_ERR_SHAPE, a missing or short workspace NQ_ERR_WORKSPACE. */
+nq_status nq_qmm_notrans(const void *x, nq_dtype x_dt, int64_t m, int64_t ni, const uint32_t *codes,
+                         const void *scales, const void *biases, nq_dtype sb_dt, int64_t nc,
+                         int32_t group_size, int32_t bits, void *y, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* As nq_qmm_notrans, every row of y bit-equal to the call on that row alone
+ * (always the matrix-vector route). */
+nq_status nq_qmm_notrans_row_exact(const void *x, nq_dtype x_dt, int64_t m, int64_t ni,
+                                   const uint32_t *codes, const void *scales, const void *biases,
+                                   nq_dtype sb_dt, int64_t nc, int32_t group_size, int32_t bits, void *y,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Derivatives of L = sum(dy * nq_qmm(x, w)) for the scales and biases of w
+ * ("Training through quantized weights": affine products have derivative
+ * rules for the activations, scales and biases; the codes have none).
+ * x [m, k] and dy [m, n] in x_dt; codes [n, k*bits/32] (w's, 4-byte
+ * aligned); dscales and dbiases [n, k/group_size] in g_dt:
+ *   dscales[c, g] = sum_r dy[r, c] * sum_{kk in group g} x[r, kk] * q[c, kk]
+ *   dbiases[c, g] = sum_r dy[r, c] * sum_{kk in group g} x[r, kk]
+ * fp32 accumulation in a fixed order (run-to-run identical).  m == 0 writes
+ * zeros.  x, dy and the outputs need only element alignment.  The outputs
+ * must not overlap each other or any input (NQ_ERR_ALIAS).  The derivative
+ * for x is nq_qmm_notrans(dy, w). */
+nq_status nq_qmm_grad_scales_biases(const void *x, const void *dy, nq_dtype x_dt, int64_t m, int64_t k,
+                                    const uint32_t *codes, int64_t n, int32_t group_size, int32_t bits,
+                                    void *dscales, void *dbiases, nq_dtype g_dt, hipStream_t stream);
+
 /* ---------------------------------------------------------------- mixture of experts */
 
 /* Workspace bytes nq_gather_qmm and nq_gather_qmm_row_exact need for these

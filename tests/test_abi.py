@@ -286,3 +286,71 @@ def test_error_string_is_thread_local(lib):
     assert seen["before"] == b""
     assert b"bits=7" in seen["after"]
     assert b"k=100" in lib.nq_last_error()
+
+
+def _nt(lib, entry="nq_qmm_notrans", x=FAKE, x_dt=BF16, m=4, ni=128, codes=FAKE2, scales=FAKE2 + 0x100000,
+        biases=FAKE2 + 0x200000, sb_dt=BF16, nc=256, gs=64, bits=4, y=FAKE2 + 0x300000,
+        ws=FAKE2 + 0x1000000, ws_bytes=1 << 24):
+    fn = getattr(lib, entry)
+    return fn(x, x_dt, m, ni, codes, scales, biases, sb_dt, nc, gs, bits, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("entry", ["nq_qmm_notrans", "nq_qmm_notrans_row_exact"])
+def test_notrans_argument_errors(lib, entry):
+    """The product with the weights as stored validates like nq_qmm; its
+    groups run along the columns (nc), and its matrix-vector route needs a
+    workspace fixed by (ni, nc)."""
+    need = lib.nq_qmm_notrans_workspace_bytes(4, 128, 256, 64, 4, BF16, 0)
+    assert need > 0 and need == lib.nq_qmm_notrans_workspace_bytes(1, 128, 256, 64, 4, BF16, 0)
+    assert lib.nq_qmm_notrans_workspace_bytes(64, 128, 256, 64, 4, BF16, 0) == 0      # tiled
+    assert lib.nq_qmm_notrans_workspace_bytes(64, 128, 256, 64, 4, BF16, 1) == need   # row-exact
+    assert lib.nq_qmm_notrans_workspace_bytes(64, 100, 256, 64, 4, BF16, 0) > 0       # ni % 32
+    cases = [
+        (dict(x_dt=7), NQ_ERR_DTYPE, "dtype"),
+        (dict(bits=7), NQ_ERR_QUANT, "bits=7"),
+        (dict(nc=100), NQ_ERR_SHAPE, "not a multiple of group_size=64"),
+        (dict(m=-1), NQ_ERR_SHAPE, "negative"),
+        (dict(y=0), NQ_ERR_NULL, "y is null"),
+        (dict(codes=0), NQ_ERR_NULL, "non-null"),
+        (dict(x=FAKE + 8), NQ_ERR_ALIGN, "aligned"),
+        (dict(y=FAKE), NQ_ERR_ALIAS, "y overlaps x"),
+        (dict(ws=0), NQ_ERR_WORKSPACE, "workspace"),
+        (dict(ws_bytes=need - 1), NQ_ERR_WORKSPACE, "workspace"),
+        (dict(ws=FAKE2 + 0x1000008), NQ_ERR_ALIGN, "workspace"),
+        (dict(ws=FAKE2 + 0x300000), NQ_ERR_ALIAS, "workspace overlaps"),
+    ]
+    for kw, want, msg in cases:
+        st = _nt(lib, entry, **kw)
+        assert st == want, (kw, st, lib.nq_last_error())
+        err = lib.nq_last_error().decode()
+        assert err.startswith(entry + ":") and msg in err, (kw, err)
+    assert _nt(lib, entry, m=0, x=0, codes=0, scales=0, biases=0, y=0, ws=0, ws_bytes=0) == NQ_OK
+
+
+def _grad(lib, x=FAKE, dy=FAKE + 0x100000, x_dt=BF16, m=4, k=256, codes=FAKE2, n=64, gs=64, bits=4,
+          ds=FAKE2 + 0x200000, db=FAKE2 + 0x300000, g_dt=F32):
+    return lib.nq_qmm_grad_scales_biases(x, dy, x_dt, m, k, codes, n, gs, bits, ds, db, g_dt, None)
+
+
+def test_grad_scales_biases_argument_errors(lib):
+    op = "nq_qmm_grad_scales_biases"
+    cases = [
+        (dict(g_dt=3), NQ_ERR_DTYPE, "dtype"),
+        (dict(bits=0), NQ_ERR_QUANT, "bits=0"),
+        (dict(k=100), NQ_ERR_SHAPE, "multiple of group_size"),
+        (dict(m=-3), NQ_ERR_SHAPE, "negative"),
+        (dict(ds=0), NQ_ERR_NULL, "non-null"),
+        (dict(codes=0), NQ_ERR_NULL, "non-null"),
+        (dict(dy=0), NQ_ERR_NULL, "x and dy"),
+        (dict(codes=FAKE2 + 2), NQ_ERR_ALIGN, "aligned"),
+        (dict(ds=FAKE2 + 0x200002), NQ_ERR_ALIGN, "aligned"),
+        (dict(db=FAKE2 + 0x200000), NQ_ERR_ALIAS, "dscales overlaps dbiases"),
+        (dict(ds=FAKE), NQ_ERR_ALIAS, "dscales overlaps x"),
+        (dict(db=FAKE2 + 0x10), NQ_ERR_ALIAS, "dbiases overlaps codes"),
+    ]
+    for kw, want, msg in cases:
+        st = _grad(lib, **kw)
+        assert st == want, (kw, st, lib.nq_last_error())
+        err = lib.nq_last_error().decode()
+        assert err.startswith(op + ":") and msg in err, (kw, err)
+    assert _grad(lib, n=0, x=0, dy=0, codes=0, ds=0, db=0) == NQ_OK

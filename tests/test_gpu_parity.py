@@ -399,6 +399,81 @@ def test_other_widths_gather(bits, rows):
             assert bits_equal(yr, y[r]), r
 
 
+# ------------------------------------------------------------------ weights as stored, derivatives
+
+
+@pytest.mark.parametrize("m,ni,nc,gs,bits,x_dtype,w_dtype", [
+    (1, 700, 4096, 64, 4, "bf16", "bf16"),     # decode-sized activation derivative
+    (2, 333, 192, 32, 3, "f32", "f32"),        # ragged row ranges, straddling codes
+    (5, 1024, 2560, 128, 8, "bf16", "f32"),    # three row chunks, two column blocks
+    (40, 100, 256, 64, 4, "bf16", "bf16"),     # many rows, ni not a multiple of 32
+    (200, 512, 384, 64, 4, "bf16", "bf16"),    # 128-row tiles
+    (150, 320, 4160, 64, 5, "bf16", "bf16"),   # tiles, odd width, ragged m and nc
+])
+def test_qmm_notrans(m, ni, nc, gs, bits, x_dtype, w_dtype):
+    """x times the weights as stored against the oracle; row-exact rows (and
+    matrix-vector rows) bit-equal to their one-row calls."""
+    w, x = synthetic.random_case(m + ni, (ni, nc), (m, ni), 0.02, w_dtype, x_dtype)
+    c, s, b = O.quantize(w, gs, bits)
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y_ref = O.qmm_nt_f64(x, c, s, b, gs, bits)
+    y = B.nq_qmm_notrans(xs, *q, gs, bits)
+    assert y.shape == (m, nc)
+    assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "notrans")
+    yr = B.nq_qmm_notrans_row_exact(xs, *q, gs, bits)
+    assert_rows_close(values(host(yr)), y_ref, tolerance(yr.dtype), "notrans row-exact")
+    tiled = m > 8 and x_dtype == "bf16" and ni % 32 == 0
+    for r in range(0, m, max(1, m // 5)):
+        y1 = B.nq_qmm_notrans(xs[r:r + 1].clone(), *q, gs, bits)   # a fresh, aligned row
+        assert bits_equal(y1, yr[r:r + 1]), r
+        if not tiled:
+            assert bits_equal(y1, y[r:r + 1]), r
+    assert bits_equal(y, B.nq_qmm_notrans(xs, *q, gs, bits))   # run to run
+
+
+def test_activation_derivative_is_notrans_of_forward_weights():
+    """dx = dy times the forward weights as stored ("Training through
+    quantized weights"): the oracle's transpose = false product with n rows."""
+    n, k, m, gs, bits = 1408, 2048, 4, 64, 4
+    w, x = synthetic.random_case(31, (n, k), (m, k), 0.02, "bf16")
+    _, dy = synthetic.random_case(32, (1, 1), (m, n), 1.0, "f32", "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    dx = B.nq_qmm_notrans(dev(dy), *gpu_quantized(c, s, b), gs, bits)
+    assert dx.shape == (m, k)
+    assert_rows_close(values(host(dx)), O.qmm_nt_f64(dy, c, s, b, gs, bits), 1e-2, "dx")
+
+
+@pytest.mark.parametrize("m,n,k,gs,bits,x_dtype,g_dtype", [
+    (3, 100, 4096, 64, 4, "f32", "f32"),
+    (8, 64, 2112, 32, 3, "bf16", "f32"),
+    (17, 50, 512, 128, 8, "bf16", "bf16"),
+    (1, 33, 6144, 64, 6, "f32", "f32"),
+])
+def test_grad_scales_biases(m, n, k, gs, bits, x_dtype, g_dtype):
+    """Derivatives for the scales and biases against the oracle, row by row
+    of the [n, k/gs] outputs; run-to-run identical."""
+    w, x = synthetic.random_case(m * n, (n, k), (m, k), 0.02, "f32", x_dtype)
+    _, dy = synthetic.random_case(m + n, (1, 1), (m, n), 1.0, "f32", x_dtype)
+    c, _, _ = O.quantize(w, gs, bits)
+    od = torch.float32 if g_dtype == "f32" else torch.bfloat16
+    ds, db = B.nq_qmm_grad_scales_biases(dev(x), dev(dy), dev(c), gs, bits, out_dtype=od)
+    ds_ref, db_ref = O.qmm_grad_sb_f64(x, dy, c, gs, bits)
+    tol = tolerance(od)
+    assert_rows_close(values(host(ds)), ds_ref, tol, "dscales")
+    assert_rows_close(values(host(db)), db_ref, tol, "dbiases")
+    ds2, db2 = B.nq_qmm_grad_scales_biases(dev(x), dev(dy), dev(c), gs, bits, out_dtype=od)
+    assert bits_equal(ds, ds2) and bits_equal(db, db2)
+
+
+def test_grad_scales_biases_no_rows():
+    """m == 0: the sums are empty, the derivatives zero."""
+    c, _, _ = O.quantize(synthetic.random_case(1, (10, 256), (1, 256))[0], 64, 4)
+    x = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    dy = torch.empty((0, 10), dtype=torch.float32, device="cuda")
+    ds, db = B.nq_qmm_grad_scales_biases(x, dy, dev(c), 64, 4)
+    assert torch.count_nonzero(ds).item() == 0 and torch.count_nonzero(db).item() == 0
+
+
 # ------------------------------------------------------------------ determinism and edges
 
 
