@@ -307,6 +307,42 @@ def main():
                                            torch.bfloat16, tag == "row_exact").as_dict()})
             del cps
 
+        # the decode shape at the other code widths (3 and 6 straddle words)
+        for bits in (2, 3, 6):
+            qb = B.nq_quantize(w2, 64, bits)
+            cps = rotated(qb)
+            t = timer.run(lambda i: B.nq_qmm(x2, *cps[i % len(cps)], 64, bits, y=y2), steps, 10)
+            put(f"decode_{bits}bit", t, steps, nbytes(*qb), "GB/s",
+                {"workload": f"x bf16 [1,4096] . W[14336,4096]^T {bits}-bit g64"})
+            del cps, qb
+
+        # derivatives through the decode weights: dx = dy times the weights as
+        # stored (1 row, and 2048 rows on the tiles), and the scale/bias
+        # derivatives for one row
+        cps = rotated(q2)
+        dy1 = dev(synthetic.random_case(5, (1, 1), (1, 14336), 1.0, "f32", "bf16")[1])
+        dx1 = torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda")
+        wsn = torch.empty(B.nq_qmm_notrans_workspace_bytes(1, 14336, 4096, 64, 4, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        t = timer.run(lambda i: B.nq_qmm_notrans(dy1, *cps[i % len(cps)], 64, 4, y=dx1, workspace=wsn),
+                      steps, 10)
+        put("dx_decode", t, steps, weight_bytes, "GB/s",
+            {"workload": "dx bf16 [1,4096] = dy [1,14336] . W[14336,4096] (weights as stored), 4-bit g64"})
+        dsg = torch.empty((14336, 64), dtype=torch.float32, device="cuda")
+        dbg = torch.empty_like(dsg)
+        x1 = x2
+        t = timer.run(lambda i: B.nq_qmm_grad_scales_biases(x1, dy1, cps[i % len(cps)][0], 64, 4,
+                                                            dscales=dsg, dbiases=dbg), steps, 10)
+        put("dscales_dbiases_decode", t, steps, nbytes(q2[0]) + 2 * nbytes(dsg), "GB/s",
+            {"workload": "x [1,4096], dy [1,14336], codes of W[14336,4096] 4-bit g64 -> f32 [14336,64] x2"})
+        del cps
+        dyp = dev(synthetic.random_case(6, (1, 1), (2048, 14336), 1.0, "f32", "bf16")[1])
+        dxp = torch.empty((2048, 4096), dtype=torch.bfloat16, device="cuda")
+        tp = timer.run(lambda i: B.nq_qmm_notrans(dyp, *q2, 64, 4, y=dxp), max(2, steps // 20), 2)
+        put("dx_prefill", tp, max(2, steps // 20), 2 * 2048 * 14336 * 4096, "TFLOP/s",
+            {"workload": "dx bf16 [2048,4096] = dy [2048,14336] . W[14336,4096] (128-row tiles)"})
+        del dyp, dxp
+
         wl = synthetic.WORKLOADS["moe_gather"]
         d = synthetic.generate("moe_gather")
         q = B.nq_quantize(dev(d["w"]), wl.group_size, wl.bits)

@@ -25,8 +25,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 // Few activation rows.  Lane L of a workgroup owns the 32 columns
 // [2048 bx + 32 L, +32) -- `bits` consecutive code words of every row, read
-// coalesced; the four waves take the rows i0 + w, i0 + w + 4, ... of the
-// workgroup's row range, each adding x[m, i] * w_hat[i, c] in increasing i;
+// coalesced, all in one group; the four waves take the rows i0 + w,
+// i0 + w + 4, ... of the workgroup's row range.  Per row, with the row's
+// scale s and bias b of that group, the lane adds (x s) q to each column's
+// sum and x b to one sum shared by its 32 columns (sum_i x (s q + b) split
+// in two), in increasing i;
 // waves 1-3 hand their sums to wave 0 through LDS (added in wave order), and
 // the workgroup's partial sums go to the workspace.  A second kernel adds the
 // row ranges' partials in range order.  The row ranges depend only on ni and
@@ -46,6 +49,32 @@ struct NtParams {
 
 constexpr int kNtWaves = 4;
 
+// A lane's 32 codes of a row: `bits` words, 16-, 8- or 4-byte aligned as the
+// width allows (every row starts on such a boundary: nc is a multiple of 32).
+template <int BITS>
+__device__ __forceinline__ void load_run(const uint32_t *src, uint32_t *w)
+{
+    if constexpr (BITS % 4 == 0) {
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u) {
+            const uint4 d = reinterpret_cast<const uint4 *>(src)[u];
+            w[4 * u] = d.x, w[4 * u + 1] = d.y, w[4 * u + 2] = d.z, w[4 * u + 3] = d.w;
+        }
+    } else if constexpr (BITS % 2 == 0) {
+#pragma unroll
+        for (int u = 0; u < BITS / 2; ++u) {
+            const uint2 d = reinterpret_cast<const uint2 *>(src)[u];
+            w[2 * u] = d.x, w[2 * u + 1] = d.y;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < BITS; ++u) w[u] = src[u];
+    }
+}
+
+// Rows a wave loads before it computes any of them (its rows i, i + 4, ...).
+constexpr int kNtUnroll = 4;
+
 template <int BITS, typename XT, typename ST, int MR>
 __global__ void __launch_bounds__(64 * kNtWaves) qmm_nt_partial_kernel(NtParams<XT, ST> p)
 {
@@ -57,28 +86,50 @@ __global__ void __launch_bounds__(64 * kNtWaves) qmm_nt_partial_kernel(NtParams<
     const int64_t g = cc >> p.lg_gs;
     const int64_t i0 = (int64_t)blockIdx.y * p.rows_per_split;
     const int64_t i1 = min(p.ni, i0 + p.rows_per_split);
-    float acc[MR][kLaneChunk];
+    float acc[MR][kLaneChunk], bsum[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        bsum[m] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kLaneChunk; ++j) acc[m][j] = 0.0f;
+    }
+    // kNtUnroll rows per pass, all their loads first; rows past i1 read row
+    // i1 - 1 and take x = 0 (adding exactly nothing)
+    for (int64_t ib = i0 + wave; ib < i1; ib += kNtUnroll * kNtWaves) {
+        uint32_t w[kNtUnroll][BITS];
+        float s[kNtUnroll], b[kNtUnroll], xv[kNtUnroll][MR];
+#pragma unroll
+        for (int u = 0; u < kNtUnroll; ++u) {
+            const int64_t iu = ib + (int64_t)u * kNtWaves;
+            const bool ok = iu < i1;
+            const int64_t i = ok ? iu : i1 - 1;
+            load_run<BITS>(p.codes + i * p.words_per_row + (cc / kLaneChunk) * BITS, w[u]);
+            s[u] = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
+            b[u] = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                xv[u][m] = ok ? Elt<XT>::load(p.x, (p.m0 + min(m, p.mrows - 1)) * p.ni + i) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kNtUnroll; ++u) {
+            float xs[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                xs[m] = xv[u][m] * s[u];
+                bsum[m] = fmaf(xv[u][m], b[u], bsum[m]);
+            }
+#pragma unroll
+            for (int j = 0; j < kLaneChunk; ++j) {
+                const float qf = (float)code_at<BITS>(w[u], j);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) acc[m][j] = fmaf(xs[m], qf, acc[m][j]);
+            }
+        }
+    }
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int j = 0; j < kLaneChunk; ++j) acc[m][j] = 0.0f;
-    for (int64_t i = i0 + wave; i < i1; i += kNtWaves) {
-        const uint32_t *src = p.codes + i * p.words_per_row + (cc / kLaneChunk) * BITS;
-        uint32_t w[BITS];
-#pragma unroll
-        for (int u = 0; u < BITS; ++u) w[u] = src[u];
-        const float s = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
-        const float b = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
-        float xv[MR];
-#pragma unroll
-        for (int m = 0; m < MR; ++m) xv[m] = Elt<XT>::load(p.x, (p.m0 + min(m, p.mrows - 1)) * p.ni + i);
-#pragma unroll
-        for (int j = 0; j < kLaneChunk; ++j) {
-            const float wv = fmaf(s, (float)code_at<BITS>(w, j), b);
-#pragma unroll
-            for (int m = 0; m < MR; ++m) acc[m][j] = fmaf(xv[m], wv, acc[m][j]);
-        }
-    }
+        for (int j = 0; j < kLaneChunk; ++j) acc[m][j] += bsum[m];
     __shared__ float red[kNtWaves - 1][MR][kLaneChunk][64];
     if (wave > 0) {
 #pragma unroll
@@ -104,17 +155,36 @@ __global__ void __launch_bounds__(64 * kNtWaves) qmm_nt_partial_kernel(NtParams<
     }
 }
 
-// y[m0 + m, c] = partials of the row ranges, added in range order.
+// y[m0 + m, c] = the row ranges' partials, added in a fixed order: a
+// workgroup takes 64 outputs, and its thread q * 64 + t adds the ranges of
+// quarter q of output t in increasing order; the four quarter sums are then
+// added in quarter order.
+constexpr int kNtRedCols = 64;
+
 template <typename XT, int MR>
 __global__ void __launch_bounds__(256) qmm_nt_reduce_kernel(const float *part, XT *y, int64_t m0, int mrows,
                                                             int64_t nc, int nsplit)
 {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)mrows * nc) return;
-    const int64_t m = idx / nc, c = idx % nc;
-    float s = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) s += part[((int64_t)sp * MR + m) * nc + c];
-    Elt<XT>::store(y, (m0 + m) * nc + c, s);
+    const int t = threadIdx.x & (kNtRedCols - 1), qt = threadIdx.x / kNtRedCols;
+    const int64_t idx = (int64_t)blockIdx.x * kNtRedCols + t;
+    const bool ok = idx < (int64_t)mrows * nc;
+    const int64_t m = ok ? idx / nc : 0, c = ok ? idx % nc : 0;
+    const int per = (nsplit + 3) / 4;
+    const int s0 = min(nsplit, qt * per), s1 = min(nsplit, s0 + per);
+    float sum = 0.0f;
+    int sp = s0;
+    for (; sp + 8 <= s1; sp += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[((int64_t)(sp + u) * MR + m) * nc + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; sp < s1; ++sp) sum += part[((int64_t)sp * MR + m) * nc + c];
+    __shared__ float qs[3][kNtRedCols];
+    if (qt > 0) qs[qt - 1][t] = sum;
+    __syncthreads();
+    if (qt == 0 && ok) Elt<XT>::store(y, (m0 + m) * nc + c, ((sum + qs[0][t]) + qs[1][t]) + qs[2][t]);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,10 +397,9 @@ namespace {
 
 int lg_of(int gs) { return gs == 32 ? 5 : gs == 64 ? 6 : 7; }
 
-template <int BITS, typename XT, typename ST>
+template <int BITS, typename XT, typename ST, int MR>
 hipError_t qmm_nt_run(const NtLaunch &a, hipStream_t stream)
 {
-    constexpr int MR = kNtRowsPerChunk;
     NtParams<XT, ST> p;
     p.x = static_cast<const XT *>(a.x);
     p.codes = a.codes;
@@ -352,7 +421,7 @@ hipError_t qmm_nt_run(const NtLaunch &a, hipStream_t stream)
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         const int64_t outs = (int64_t)p.mrows * a.nc;
-        qmm_nt_reduce_kernel<XT, MR><<<dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, stream>>>(
+        qmm_nt_reduce_kernel<XT, MR><<<dim3((unsigned)((outs + kNtRedCols - 1) / kNtRedCols)), dim3(256), 0, stream>>>(
             p.part, static_cast<XT *>(a.y), m0, p.mrows, a.nc, nsplit);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -387,7 +456,9 @@ hipError_t nt_bits(const NtLaunch &a, hipStream_t stream)
         if constexpr (sizeof(XT) == 2) return tiled_nt_run<BITS, ST>(a, stream);
         else return hipErrorInvalidValue;
     }
-    return qmm_nt_run<BITS, XT, ST>(a, stream);
+    // one activation row per pass for single-row calls (the same arithmetic per row)
+    if (a.m == 1) return qmm_nt_run<BITS, XT, ST, 1>(a, stream);
+    return qmm_nt_run<BITS, XT, ST, kNtRowsPerChunk>(a, stream);
 }
 
 template <typename XT, typename ST>
@@ -445,9 +516,9 @@ hipError_t grad_dt(const GradLaunch &a, hipStream_t stream)
 
 int qmm_nt_splits(int64_t ni, int64_t nc)
 {
-    // about 256 workgroups, and at least 16 rows (4 per wave) per range
+    // about 512 workgroups, and at least 16 rows (4 per wave) per range
     const int64_t col_blocks = (nc + kStepElems - 1) / kStepElems;
-    const int64_t want = std::max<int64_t>(1, (256 + col_blocks - 1) / col_blocks);
+    const int64_t want = std::max<int64_t>(1, (512 + col_blocks - 1) / col_blocks);
     const int64_t most = std::max<int64_t>(1, (ni + 15) / 16);
     return (int)std::min<int64_t>(std::min(want, most), 65535);
 }
