@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     nq_dequantize,
     nq_gather_qmm,
     nq_gather_qmm_row_exact,
+    nq_gather_qmm_lhs,
     nq_gather_qmm_workspace_bytes,
     nq_qmm,
     nq_qmm_grad_scales_biases,

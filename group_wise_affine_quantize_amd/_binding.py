@@ -60,6 +60,8 @@ _SIGNATURES = {
                       _I32, _P, _P, _SZ, _P],
     "nq_gather_qmm_row_exact": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32,
                                 _I32, _P, _I32, _P, _P, _SZ, _P],
+    "nq_gather_qmm_lhs": [_P, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32,
+                          _P, _P, _I32, _I32, _P, _P, _SZ, _P],
     "nq_qmm_notrans_workspace_bytes": [_I64, _I64, _I64, _I32, _I32, _I32, _I32],
     "nq_qmm_notrans": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ, _P],
     "nq_qmm_notrans_row_exact": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P,
@@ -356,3 +358,35 @@ def nq_gather_qmm_row_exact(x, codes, scales, biases, group_size, bits, rhs_idx,
     """As nq_gather_qmm, every row bit-equal to its one-row product."""
     return _gather_call("nq_gather_qmm_row_exact", x, codes, scales, biases, group_size, bits,
                         rhs_idx, sorted_hint, y, workspace, stream)
+
+
+def nq_gather_qmm_lhs(x, codes, scales, biases, group_size, bits, lhs_idx, rhs_idx,
+                      sorted_hint=False, row_exact=False, y=None, workspace=None, stream=None):
+    """x [x_items, l, k]; lhs_idx and rhs_idx [rows] (32-bit ids): row r of
+    y [rows, l, n] is x[lhs_idx[r]] times expert rhs_idx[r]'s weights; an id
+    past x_items or e gives a zero row."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases),
+                    ("lhs_idx", lhs_idx), ("rhs_idx", rhs_idx)):
+        _contig(name, t)
+    if lhs_idx.element_size() != 4 or rhs_idx.element_size() != 4:
+        raise ValueError("lhs_idx and rhs_idx must hold 32-bit ids")
+    x_items, l, k = x.shape
+    e, n = scales.shape[0], scales.shape[1]
+    rows = rhs_idx.numel()
+    if lhs_idx.numel() != rows:
+        raise ValueError("lhs_idx and rhs_idx must have one id per output row")
+    if y is None:
+        y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        need = lib.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, _dt(x),
+                                                 _dt(scales), int(bool(sorted_hint)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.nq_gather_qmm_lhs(_ptr(x), _dt(x), x_items, rows, l, k, _ptr(codes), _ptr(scales),
+                                 _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(lhs_idx),
+                                 _ptr(rhs_idx), int(bool(sorted_hint)), int(bool(row_exact)),
+                                 _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y

@@ -61,6 +61,9 @@ struct GemvParams {
     const uint4 *chunks;
     const uint32_t *perm;
     const uint32_t *nchunks;
+    // left indices: vector r * lhs_l + j reads x row lhs[r] * lhs_l + j
+    const uint32_t *lhs;
+    int64_t x_items, lhs_l;
     int gs, ksplit, steps, chunks_per_item, qrows;   // qrows: row groups per workgroup
 };
 
@@ -267,7 +270,12 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
         const int64_t item = p.item0 + blockIdx.y / p.chunks_per_item;
         const int64_t r0 = (int64_t)(blockIdx.y % p.chunks_per_item) * MR;
         mrows = (int)min((int64_t)MR, p.rows_per_item - r0);
-        xb = p.x + (item * p.rows_per_item + r0) * p.k;
+        int64_t xi = item;
+        if (p.lhs) {
+            xi = p.lhs[item];
+            if (xi >= p.x_items) live = false, xi = 0;   // a zero row; x is never read
+        }
+        xb = p.x + (xi * p.rows_per_item + r0) * p.k;
         yb = p.y + (item * p.rows_per_item + r0) * p.n;
         if (p.idx) {
             const uint32_t ex = p.idx[item];
@@ -282,7 +290,17 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const int mm = min(m, mrows - 1);
-        const XT *r = p.chunks ? p.x + (int64_t)p.perm[first + mm] * p.k : xb + (int64_t)mm * p.k;
+        int64_t v = 0;
+        if (p.chunks) {
+            v = p.perm[first + mm];
+            if (p.lhs) {
+                // rows with lhs >= x_items are in the zero bucket and never
+                // read x; they point at item 0 all the same
+                const int64_t xi = p.lhs[v / p.lhs_l];
+                v = (xi < p.x_items ? xi : 0) * p.lhs_l + v % p.lhs_l;
+            }
+        }
+        const XT *r = p.chunks ? p.x + v * p.k : xb + (int64_t)mm * p.k;
         const uint64_t u = reinterpret_cast<uint64_t>(r);
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
@@ -551,8 +569,8 @@ __device__ void block_exclusive_scan(uint32_t *a, int n, uint32_t *part, uint32_
 }
 
 __global__ void __launch_bounds__(kGroupThreads)
-gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_t *ws, int64_t v_total,
-                    uint32_t chunk)
+gather_group_kernel(const uint32_t *ids, const uint32_t *lhs, int64_t x_items, int64_t rows, int64_t l, int e,
+                    uint32_t *ws, int64_t v_total, uint32_t chunk)
 {
     extern __shared__ uint4 sh4[];   // bucket[1024], part[1024], count[e+1], chunk offset[e+1], totals[2]
     uint32_t *sh = reinterpret_cast<uint32_t *>(sh4);
@@ -562,7 +580,10 @@ gather_group_kernel(const uint32_t *ids, int64_t rows, int64_t l, int e, uint32_
     uint32_t *perm = ws, *nchunks = ws + v_total;
     uint4 *table = reinterpret_cast<uint4 *>(ws + ((v_total + 1 + 3) & ~(int64_t)3));
     const int t = threadIdx.x;
-    auto bucket = [&](int64_t v) -> uint32_t { return min(ids[v / l], (uint32_t)e); };
+    auto bucket = [&](int64_t v) -> uint32_t {
+        const int64_t r = v / l;
+        return lhs && (int64_t)lhs[r] >= x_items ? (uint32_t)e : min(ids[r], (uint32_t)e);
+    };
 
     for (int b = t; b < nb; b += kGroupThreads) cnt[b] = 0;
     __syncthreads();
@@ -617,7 +638,8 @@ constexpr int kGroupSmallBuckets = 256;
 constexpr int kGroupWaves = kGroupThreads / 64;
 
 __global__ void __launch_bounds__(kGroupThreads)
-gather_group_small_kernel(const uint32_t *ids, int64_t l, int e, uint32_t *ws, int64_t v_total, uint32_t chunk)
+gather_group_small_kernel(const uint32_t *ids, const uint32_t *lhs, int64_t x_items, int64_t l, int e, uint32_t *ws,
+                          int64_t v_total, uint32_t chunk)
 {
     __shared__ uint32_t wc[kGroupWaves][kGroupSmallBuckets];   // per-wave counts, then positions
     __shared__ uint32_t hist[kGroupSmallBuckets];
@@ -629,7 +651,9 @@ gather_group_small_kernel(const uint32_t *ids, int64_t l, int e, uint32_t *ws, i
     uint4 *table = reinterpret_cast<uint4 *>(ws + ((v_total + 1 + 3) & ~(int64_t)3));
     const uint64_t lanes_below = (lane ? ~0ull >> (64 - lane) : 0ull);
     auto bucket = [&](int64_t v) -> uint32_t {
-        return v < v_total ? min(ids[v / l], (uint32_t)e) : 0xffffffffu;
+        if (v >= v_total) return 0xffffffffu;
+        const int64_t r = v / l;
+        return lhs && (int64_t)lhs[r] >= x_items ? (uint32_t)e : min(ids[r], (uint32_t)e);
     };
     // For every distinct bucket among this wave's valid lanes (in lane
     // order of first appearance): fn(bucket, lanes holding it).
@@ -733,16 +757,18 @@ size_t gather_group_ws_bytes(int64_t vectors, int64_t e, int chunk)
     return (size_t)(((vectors + 1 + 3) & ~(int64_t)3) + 4 * gather_group_max_chunks(vectors, e, chunk)) * 4;
 }
 
-hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, int chunk,
+hipError_t launch_gather_groups(const uint32_t *ids, const uint32_t *lhs, int64_t x_items, int64_t rows,
+                                int64_t l, int64_t e, int chunk,
                                 void *ws, hipStream_t stream)
 {
     if (e + 1 <= kGroupSmallBuckets) {
-        gather_group_small_kernel<<<1, kGroupThreads, 0, stream>>>(ids, l, (int)e, static_cast<uint32_t *>(ws),
+        gather_group_small_kernel<<<1, kGroupThreads, 0, stream>>>(ids, lhs, x_items, l, (int)e,
+                                                                   static_cast<uint32_t *>(ws),
                                                                    rows * l, (uint32_t)chunk);
         return hipGetLastError();
     }
     const size_t lds = (size_t)(2 * (e + 1) + 2 * kGroupThreads + 2) * 4;
-    gather_group_kernel<<<1, kGroupThreads, lds, stream>>>(ids, rows, l, (int)e,
+    gather_group_kernel<<<1, kGroupThreads, lds, stream>>>(ids, lhs, x_items, rows, l, (int)e,
                                                            static_cast<uint32_t *>(ws), rows * l,
                                                            (uint32_t)chunk);
     return hipGetLastError();
@@ -766,6 +792,9 @@ hipError_t gemv_run(const GemvLaunch &a, hipStream_t stream)
     p.chunks = reinterpret_cast<const uint4 *>(a.chunks);
     p.perm = a.perm;
     p.nchunks = a.nchunks;
+    p.lhs = a.lhs;
+    p.x_items = a.x_items;
+    p.lhs_l = a.lhs_l;
     p.rows_per_item = a.rows_per_item;
     p.k = a.k;
     p.n = a.n;

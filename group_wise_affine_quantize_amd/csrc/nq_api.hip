@@ -541,9 +541,10 @@ bool gather_mfma(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n, int x
 nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_dt, int64_t rows,
                       int64_t l, int64_t k, const uint32_t *codes, const void *scales,
                       const void *biases, nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size,
-                      int32_t bits, const uint32_t *rhs_idx, void *y, void *workspace,
-                      size_t workspace_bytes, hipStream_t stream)
+                      int32_t bits, const uint32_t *lhs_idx, int64_t x_items, const uint32_t *rhs_idx,
+                      void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
+    // lhs_idx null: output row r reads x item r (x has rows items)
     g_last_error.clear();
     if (!dtype_ok(x_dt) || !dtype_ok(sb_dt))
         return fail(NQ_ERR_DTYPE, "%s: unknown dtype (x_dt=%d, sb_dt=%d)", op, (int)x_dt, (int)sb_dt);
@@ -558,6 +559,11 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     if (rows >= kMaxDim || l >= kMaxDim || (rows > 0 && l > kMaxElems / rows) ||
         (rows * l > 0 && std::max<int64_t>(k, n) > kMaxElems / (rows * l)))
         return fail(NQ_ERR_SHAPE, "%s: rows*l is too large", op);
+    if (lhs_idx && (x_items < 1 || x_items >= kMaxDim ||
+                    (k > 0 && x_items > kMaxElems / std::max<int64_t>(l, 1) / k)))
+        return fail(NQ_ERR_SHAPE, "%s: x_items=%lld must be positive and not too large", op,
+                    (long long)x_items);
+    if (!lhs_idx) x_items = rows;
     if (rows == 0 || l == 0 || n == 0) return NQ_OK;
     if (!y || !rhs_idx) return fail(NQ_ERR_NULL, "%s: y and rhs_idx must be non-null", op);
     if (k > 0 && (!x || (e > 0 && (!codes || !scales || !biases))))
@@ -565,16 +571,18 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     if (!aligned16(x) || !aligned16(codes) || !aligned16(y))
         return fail(NQ_ERR_ALIGN, "%s: x, codes and y must be 16-byte aligned", op);
     const int64_t sbb = dtype_bytes(sb_dt);
-    if (!aligned_to(scales, sbb) || !aligned_to(biases, sbb) || !aligned_to(rhs_idx, 4))
-        return fail(NQ_ERR_ALIGN, "%s: scales, biases or rhs_idx misaligned", op);
+    if (!aligned_to(scales, sbb) || !aligned_to(biases, sbb) || !aligned_to(rhs_idx, 4) ||
+        !aligned_to(lhs_idx, 4))
+        return fail(NQ_ERR_ALIGN, "%s: scales, biases, rhs_idx or lhs_idx misaligned", op);
     const Span sy{y, rows * l * n * dtype_bytes(x_dt)};
-    const Span ins[5] = {{x, rows * l * k * dtype_bytes(x_dt)},
+    const Span ins[6] = {{x, x_items * l * k * dtype_bytes(x_dt)},
                          {codes, e * n * (k * bits / 32) * 4},
                          {scales, e * n * (k / group_size) * sbb},
                          {biases, e * n * (k / group_size) * sbb},
-                         {rhs_idx, rows * 4}};
-    static const char *names[5] = {"x", "codes", "scales", "biases", "rhs_idx"};
-    for (int i = 0; i < 5; ++i)
+                         {rhs_idx, rows * 4},
+                         {lhs_idx, lhs_idx ? rows * 4 : 0}};
+    static const char *names[6] = {"x", "codes", "scales", "biases", "rhs_idx", "lhs_idx"};
+    for (int i = 0; i < 6; ++i)
         if (overlap(sy, ins[i])) return fail(NQ_ERR_ALIAS, "%s: y overlaps %s", op, names[i]);
 
     const bool shared = gather_shared(rows, l, k, e, n);
@@ -588,7 +596,7 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
         if (!aligned16(workspace)) return fail(NQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", op);
         const Span sw{workspace, (int64_t)need};
         if (overlap(sw, sy)) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps y", op);
-        for (int i = 0; i < 5; ++i)
+        for (int i = 0; i < 6; ++i)
             if (overlap(sw, ins[i])) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps %s", op, names[i]);
     }
     uint32_t *ws = static_cast<uint32_t *>(workspace);
@@ -596,7 +604,8 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     // the matrix-core route groups small id sets inside its own workgroups
     const bool self_group = mfma && nqk::gather_self_group_fits(v, e);
     if (shared && !self_group) {
-        if (hipError_t err = nqk::launch_gather_groups(rhs_idx, rows, l, e, chunk, workspace, stream))
+        if (hipError_t err = nqk::launch_gather_groups(rhs_idx, lhs_idx, x_items, rows, l, e, chunk, workspace,
+                                                       stream))
             return check_launch(op, err);
     }
     if (mfma) {
@@ -610,6 +619,8 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
         g.nchunks = ws + v;
         g.chunks = ws + ((v + 1 + 3) & ~(int64_t)3);
         g.ids = rhs_idx;
+        g.lhs = lhs_idx;
+        g.x_items = x_items;
         g.sb_dt = sb_dt;
         g.n = n;
         g.k = k;
@@ -641,6 +652,9 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     g.bits = bits;
     g.ksplit = gemv_ksplit(n, k);   // the plan nq_qmm_row_exact takes
     g.rows_per_wave = 0;
+    g.lhs = lhs_idx;
+    g.x_items = x_items;
+    g.lhs_l = l;
     if (shared) {
         g.idx = nullptr;
         g.perm = ws;
@@ -673,7 +687,7 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
 {
     (void)sorted_hint;
     return gather_impl("nq_gather_qmm", 0, x, x_dt, rows, l, k, codes, scales, biases, sb_dt, e, n,
-                       group_size, bits, rhs_idx, y, workspace, workspace_bytes, stream);
+                       group_size, bits, nullptr, rows, rhs_idx, y, workspace, workspace_bytes, stream);
 }
 
 nq_status nq_gather_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
@@ -685,7 +699,25 @@ nq_status nq_gather_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t rows, in
 {
     (void)sorted_hint;
     return gather_impl("nq_gather_qmm_row_exact", 1, x, x_dt, rows, l, k, codes, scales, biases,
-                       sb_dt, e, n, group_size, bits, rhs_idx, y, workspace, workspace_bytes, stream);
+                       sb_dt, e, n, group_size, bits, nullptr, rows, rhs_idx, y, workspace, workspace_bytes,
+                       stream);
+}
+
+nq_status nq_gather_qmm_lhs(const void *x, nq_dtype x_dt, int64_t x_items, int64_t rows, int64_t l,
+                            int64_t k, const uint32_t *codes, const void *scales, const void *biases,
+                            nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                            const uint32_t *lhs_idx, const uint32_t *rhs_idx, int32_t sorted_hint,
+                            int32_t row_exact, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    (void)sorted_hint;
+    const char *op = "nq_gather_qmm_lhs";
+    if (!lhs_idx && rows > 0 && l > 0 && n > 0) {
+        g_last_error.clear();
+        return fail(NQ_ERR_NULL, "%s: lhs_idx must be non-null (nq_gather_qmm takes none)", op);
+    }
+    return gather_impl(op, row_exact ? 1 : 0, x, x_dt, rows, l, k, codes, scales, biases, sb_dt, e, n,
+                       group_size, bits, lhs_idx, x_items, rhs_idx, y, workspace, workspace_bytes, stream);
 }
 
 const char *nq_status_string(nq_status s)

@@ -46,6 +46,10 @@ struct GemvLaunch {
     int ksplit, rows_per_wave;
     const uint32_t *perm = nullptr, *chunks = nullptr, *nchunks = nullptr;
     int64_t max_chunks = 0;
+    // gather with left indices: vector r * l + j reads x row lhs[r] * l + j
+    // (lhs[r] >= x_items gives a zero row)
+    const uint32_t *lhs = nullptr;
+    int64_t x_items = 0, lhs_l = 1;
 };
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 
@@ -59,7 +63,8 @@ size_t gather_group_ws_bytes(int64_t vectors, int64_t e, int chunk);
 int64_t gather_group_max_chunks(int64_t vectors, int64_t e, int chunk);
 // Groups the vectors r * l + j by expert ids[r] (one workgroup): perm,
 // chunk count and chunk table into ws (layout in gemv.hip).
-hipError_t launch_gather_groups(const uint32_t *ids, int64_t rows, int64_t l, int64_t e, int chunk,
+hipError_t launch_gather_groups(const uint32_t *ids, const uint32_t *lhs, int64_t x_items, int64_t rows,
+                                int64_t l, int64_t e, int chunk,
                                 void *ws, hipStream_t stream);
 
 // Grouped matrix-core gather: chunk c of the table multiplies its (up to 32)
@@ -73,6 +78,8 @@ struct GatherMfmaLaunch {
     const void *biases;
     const uint32_t *perm, *chunks, *nchunks;   // grouping tables (unless self_group)
     const uint32_t *ids;                       // expert ids (self_group)
+    const uint32_t *lhs;                       // left indices, or null
+    int64_t x_items;
     int sb_dt;
     int64_t n, k, e, max_chunks, l, v_total;
     int gs, bits;

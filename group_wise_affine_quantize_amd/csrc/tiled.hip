@@ -607,7 +607,8 @@ struct GatherParams {
     const uint4 *chunks;
     const uint32_t *nchunks;
     const uint32_t *ids;
-    int64_t n, k, e, words_per_row, groups_per_row, l, v_total;
+    const uint32_t *lhs;   // left indices or null: vector r * l + j reads x row lhs[r] * l + j
+    int64_t n, k, e, words_per_row, groups_per_row, l, v_total, x_items;
     int lg_gs;
 };
 
@@ -642,8 +643,8 @@ __device__ __forceinline__ void wait_vmcnt()
 constexpr int kSelfGroupRounds = 16;
 
 template <int NT>
-__device__ bool gather_self_group(const uint32_t *ids, int64_t l, int64_t v_total, int e, uint4 &ch,
-                                  uint32_t *list)
+__device__ bool gather_self_group(const uint32_t *ids, const uint32_t *lhs, int64_t x_items, int64_t l,
+                                  int64_t v_total, int e, uint4 &ch, uint32_t *list)
 {
     constexpr int NWV = NT / 64;
     __shared__ uint32_t gh[256], gst[256], gcoff[257], gw[NWV];
@@ -659,7 +660,10 @@ __device__ bool gather_self_group(const uint32_t *ids, int64_t l, int64_t v_tota
         bk[r] = 0xffffffffu;
         if (r < rounds) {   // uniform
             const int64_t v = (int64_t)r * NT + t;
-            if (v < v_total) bk[r] = min(ids[v / l], (uint32_t)e);
+            if (v < v_total) {
+                const int64_t rr = v / l;   // rows with lhs past the x items: the zero bucket
+                bk[r] = lhs && (int64_t)lhs[rr] >= x_items ? (uint32_t)e : min(ids[rr], (uint32_t)e);
+            }
             // one atomic per distinct bucket of the wave
             uint64_t active = __ballot(bk[r] != 0xffffffffu);
             while (active) {
@@ -751,7 +755,8 @@ __global__ void __launch_bounds__(64 * CB * KS) gather_mfma_kernel(GatherParams<
     __shared__ uint32_t vec_list[kGatherRows];
     uint4 ch;
     if constexpr (SELF) {
-        if (!gather_self_group<64 * CB * KS>(p.ids, p.l, p.v_total, (int)p.e, ch, vec_list)) return;
+        if (!gather_self_group<64 * CB * KS>(p.ids, p.lhs, p.x_items, p.l, p.v_total, (int)p.e, ch, vec_list))
+            return;
     } else {
         if (blockIdx.y >= *p.nchunks) return;   // uniform over the workgroup
         ch = p.chunks[blockIdx.y];
@@ -780,7 +785,11 @@ __global__ void __launch_bounds__(64 * CB * KS) gather_mfma_kernel(GatherParams<
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
             const int xr = r0 + 8 * i + (lane >> 3);
-            const int64_t xvec = vec_at(min(xr, count - 1));
+            int64_t xvec = vec_at(min(xr, count - 1));
+            if (p.lhs) {   // the x row of vector xvec (zero-bucket rows never get here)
+                const int64_t xi = p.lhs[xvec / p.l];
+                xvec = (xi < p.x_items ? xi : 0) * p.l + xvec % p.l;
+            }
             xsrc[i] = p.x + xvec * p.k + (int64_t)kb0 * kBK2 + 8 * ((lane & 7) ^ ((xr >> 1) & 7));
         }
         // this lane's codes: weight row c, k = 32 h .. 32 h + 31 of each block
@@ -988,6 +997,8 @@ hipError_t gather_mfma_run(const GatherMfmaLaunch &a, hipStream_t stream)
     p.chunks = reinterpret_cast<const uint4 *>(a.chunks);
     p.nchunks = a.nchunks;
     p.ids = a.ids;
+    p.lhs = a.lhs;
+    p.x_items = a.x_items;
     p.n = a.n;
     p.k = a.k;
     p.e = a.e;

@@ -262,6 +262,27 @@ nq_status nq_gather_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t rows, in
                                   void *y, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/* gather_qmm with indices on both sides ("Mixture of experts" section: the
+ * gathered product picks the activation batch and the expert per output
+ * row).  x [x_items, l, k]; lhs_idx [rows] and rhs_idx [rows] uint32:
+ *   y[r, j, :] = x[lhs_idx[r], j, :] times expert rhs_idx[r]'s transposed weights.
+ * lhs_idx[r] >= x_items, like rhs_idx[r] >= e, gives an all-zero row of y
+ * and is never used to address memory.  x_items >= 1 (NQ_ERR_SHAPE
+ * otherwise); lhs_idx must be non-null (NQ_ERR_NULL), 4-byte aligned and
+ * must not overlap y or the workspace.  row_exact != 0 takes the row-exact
+ * mode of nq_gather_qmm_row_exact (each row bit-equal to nq_qmm_row_exact of
+ * its x row with its expert's weights); otherwise the routes, the
+ * workspace (nq_gather_qmm_workspace_bytes with these rows, l, k, e, n) and
+ * the tolerance are those of nq_gather_qmm.  With lhs_idx[r] = r and
+ * x_items = rows the results equal nq_gather_qmm's / _row_exact's bit for
+ * bit. */
+nq_status nq_gather_qmm_lhs(const void *x, nq_dtype x_dt, int64_t x_items, int64_t rows, int64_t l,
+                            int64_t k, const uint32_t *codes, const void *scales, const void *biases,
+                            nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                            const uint32_t *lhs_idx, const uint32_t *rhs_idx, int32_t sorted_hint,
+                            int32_t row_exact, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* ---------------------------------------------------------------- errors */
 
 /* A static description of a status code. */

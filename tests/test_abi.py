@@ -241,6 +241,35 @@ def test_gather_argument_errors(lib):
     assert b"nq_gather_qmm:" in lib.nq_last_error()
 
 
+def test_gather_lhs_argument_errors(lib):
+    def g(**kw):
+        a = dict(x=FAKE, x_dt=BF16, x_items=2, rows=4, l=1, k=128, codes=FAKE2,
+                 scales=FAKE2 + 0x100000, biases=FAKE2 + 0x200000, sb_dt=BF16, e=8, n=64, gs=64,
+                 bits=4, lhs=FAKE2 + 0x500000, idx=FAKE2 + 0x300000, sorted_hint=0, row_exact=0,
+                 y=FAKE2 + 0x400000)
+        a.update(kw)
+        return lib.nq_gather_qmm_lhs(a["x"], a["x_dt"], a["x_items"], a["rows"], a["l"], a["k"],
+                                     a["codes"], a["scales"], a["biases"], a["sb_dt"], a["e"],
+                                     a["n"], a["gs"], a["bits"], a["lhs"], a["idx"],
+                                     a["sorted_hint"], a["row_exact"], a["y"], 0, 0, None)
+    assert g(lhs=0) == NQ_ERR_NULL
+    assert b"lhs_idx" in lib.nq_last_error()
+    assert g(x_items=0) == NQ_ERR_SHAPE
+    assert g(x_items=-3) == NQ_ERR_SHAPE
+    assert b"x_items" in lib.nq_last_error()
+    assert g(lhs=FAKE2 + 0x500002) == NQ_ERR_ALIGN
+    assert g(y=FAKE2 + 0x500000) == NQ_ERR_ALIAS          # y overlaps lhs_idx
+    assert b"lhs_idx" in lib.nq_last_error()
+    # x spans x_items items of l * k elements
+    assert g(y=FAKE + 2 * 128 * 2 - 16, x_items=2) == NQ_ERR_ALIAS
+    assert b"y overlaps x" in lib.nq_last_error()
+    assert g(idx=0, row_exact=1) == NQ_ERR_NULL
+    assert g(bits=7) == NQ_ERR_QUANT
+    assert b"nq_gather_qmm_lhs:" in lib.nq_last_error()
+    # nothing to do: no rows
+    assert g(rows=0, lhs=0) == NQ_OK
+
+
 def test_gather_grouped_route_workspace(lib):
     """Many rows per expert take the grouped route, which needs a workspace;
     few rows per expert (or few rows) do not."""

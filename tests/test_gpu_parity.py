@@ -349,6 +349,56 @@ def test_gather_sorted_hint_same_bits():
     assert_rows_close(host(y0), O.gather_qmm_f64(x, c, s, b, gs, bits, ids), 1e-3, "page example")
 
 
+@pytest.mark.parametrize("case", ["per_row_f32", "per_row_bf16", "grouped_f32", "mfma_self", "mfma_table",
+                                  "many_experts"])
+def test_gather_lhs(case):
+    """Left and right indices ("Mixture of experts" section): row r of y is
+    x[lhs[r]] times expert rhs[r]'s weights; ids past x_items or e give zero
+    rows.  Every route (per row, grouped matrix-vector, matrix cores grouped
+    in-kernel or by the grouping pass, the general grouping pass) against the
+    oracle; row-exact rows bit-equal to the one-row product of their x row;
+    the identity lhs gives nq_gather_qmm's bits."""
+    gs, bits = 64, 4
+    x_dt, w_dt, e, rows, l, x_items, n, k = {
+        "per_row_f32": ("f32", "f32", 8, 10, 3, 4, 100, 640),
+        "per_row_bf16": ("bf16", "bf16", 8, 10, 2, 3, 72, 512),
+        "grouped_f32": ("f32", "bf16", 3, 100, 1, 7, 96, 1024),
+        "mfma_self": ("bf16", "bf16", 4, 200, 1, 9, 96, 512),
+        "mfma_table": ("bf16", "f32", 16, 700, 3, 5, 72, 512),
+        "many_experts": ("bf16", "bf16", 300, 1300, 1, 40, 64, 256)}[case]
+    rng = np.random.default_rng(rows + x_items)
+    rhs = rng.integers(0, e, size=rows, dtype=np.uint32)
+    lhs = rng.integers(0, x_items, size=rows, dtype=np.uint32)
+    rhs[:3] = e                                            # zero rows by either index
+    lhs[3:6] = [x_items, x_items + 5, 0xFFFFFFFF]
+    w, _ = synthetic.random_case(e + rows, (e, n, k), (1, k), 0.02, w_dt)
+    _, x = synthetic.random_case(x_items, (1, 1), (x_items, l, k), 1.0, "f32", x_dt)
+    c, s, b = O.quantize(w, gs, bits)
+    xs, cs, ss, bs, dl, dr = dev(x), dev(c), dev(s), dev(b), dev(lhs), dev(rhs)
+    y_ref = O.gather_qmm_lhs_f64(x, c, s, b, gs, bits, lhs, rhs).reshape(rows * l, n)
+    zero = (lhs >= x_items) | (rhs >= e)
+    tol = tolerance(torch.float32 if x_dt == "f32" else torch.bfloat16)
+    yd = B.nq_gather_qmm_lhs(xs, cs, ss, bs, gs, bits, dl, dr)
+    assert yd.shape == (rows, l, n)
+    assert_rows_close(values(host(yd)).reshape(rows * l, n), y_ref, tol, "gather lhs")
+    y = B.nq_gather_qmm_lhs(xs, cs, ss, bs, gs, bits, dl, dr, row_exact=True)
+    assert_rows_close(values(host(y)).reshape(rows * l, n), y_ref, tol, "gather lhs row-exact")
+    assert np.all(values(host(yd))[zero] == 0) and np.all(values(host(y))[zero] == 0)
+    for r in range(0, rows, max(1, rows // 12)):
+        if zero[r]:
+            continue
+        yr = B.nq_qmm_row_exact(xs[lhs[r]].contiguous(), cs[rhs[r]], ss[rhs[r]], bs[rhs[r]], gs, bits)
+        assert bits_equal(yr, y[r]), r
+    assert bits_equal(yd, B.nq_gather_qmm_lhs(xs, cs, ss, bs, gs, bits, dl, dr))
+    # the identity lhs over x's own items is nq_gather_qmm
+    xr = dev(x[np.minimum(lhs, x_items - 1)])
+    ident = dev(np.arange(rows, dtype=np.uint32))
+    assert bits_equal(B.nq_gather_qmm_lhs(xr, cs, ss, bs, gs, bits, ident, dr),
+                      B.nq_gather_qmm(xr, cs, ss, bs, gs, bits, dr))
+    assert bits_equal(B.nq_gather_qmm_lhs(xr, cs, ss, bs, gs, bits, ident, dr, row_exact=True),
+                      B.nq_gather_qmm_row_exact(xr, cs, ss, bs, gs, bits, dr))
+
+
 # ------------------------------------------------------------------ other widths
 
 
