@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     nq_gather_qmm_lhs,
     nq_gather_qmm_workspace_bytes,
     nq_qmm,
+    nq_qmm_batched,
     nq_qmm_grad_scales_biases,
     nq_qmm_notrans,
     nq_qmm_notrans_row_exact,

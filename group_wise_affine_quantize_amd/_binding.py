@@ -54,6 +54,8 @@ _SIGNATURES = {
                          _P],
     "nq_qmm_with_plan": [ctypes.POINTER(Plan), _P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64,
                          _I32, _I32, _P, _P, _SZ, _P],
+    "nq_qmm_batched": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _SZ,
+                       _P],
     "nq_gather_qmm_workspace_bytes": [_I64, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                       _I32],
     "nq_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P,
@@ -236,6 +238,26 @@ def nq_qmm_with_plan(plan, x, codes, scales, biases, group_size, bits, y=None, w
                      stream=None):
     return _qmm_call(None, x, codes, scales, biases, group_size, bits, y, workspace, stream,
                      plan=plan)
+
+
+def nq_qmm_batched(x, codes, scales, biases, group_size, bits, y=None, workspace=None,
+                   stream=None):
+    """x [batch, l, k] -> y [batch, l, n]: item i bit-equal to nq_qmm(x[i])."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases)):
+        _contig(name, t)
+    batch, l, k = x.shape
+    n = scales.shape[0]
+    if scales.shape[1] * group_size != k or codes.shape != (n, words_per_row(k, bits)):
+        raise ValueError("codes/scales shapes do not match x and the quantization")
+    if y is None:
+        y = torch.empty((batch, l, n), dtype=x.dtype, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.nq_qmm_batched(_ptr(x), _dt(x), batch, l, k, _ptr(codes), _ptr(scales),
+                              _ptr(biases), _dt(scales), n, group_size, bits, _ptr(y),
+                              _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
 
 
 def nq_qmm_notrans_workspace_bytes(m, ni, nc, group_size, bits, x_dtype, row_exact=False):

@@ -515,6 +515,55 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
     return qmm_common("nq_qmm_with_plan", 0, plan, a, stream);
 }
 
+// Batch items keep their solo bits ("Products on the GPU" section: batch
+// items of quantized products).  The route is the plan of one item; every
+// kernel's arithmetic for an output element depends only on its own row of
+// x and its weight row, so running that plan over all items at once gives
+// each item the bits of the call on it alone.  Only the launch is cut where
+// the 256-row tiles' 32-bit offsets would overflow.
+nq_status nq_qmm_batched(const void *x, nq_dtype x_dt, int64_t batch, int64_t l, int64_t k,
+                         const uint32_t *codes, const void *scales, const void *biases,
+                         nq_dtype sb_dt, int64_t n, int32_t group_size, int32_t bits, void *y,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *op = "nq_qmm_batched";
+    g_last_error.clear();
+    if (batch < 0 || l < 0)
+        return fail(NQ_ERR_SHAPE, "%s: negative size (batch=%lld, l=%lld)", op, (long long)batch,
+                    (long long)l);
+    if (batch >= kMaxDim || l >= kMaxDim || (batch > 0 && l > kMaxDim / batch))
+        return fail(NQ_ERR_SHAPE, "%s: batch*l is too large", op);
+    const QmmArgs a{x, x_dt, batch * l, k, codes, scales, biases, sb_dt, n, group_size, bits, y,
+                    workspace, workspace_bytes};
+    bool empty = false;
+    nq_status st = check_qmm(op, a, &empty);
+    if (st || empty) return st;
+    nq_plan plan;
+    make_plan(op, l, n, k, group_size, bits, x_dt, sb_dt, 0, &plan);
+    int64_t per_launch = batch;   // items per launch
+    const int64_t xb = dtype_bytes(x_dt);
+    if (plan.route == NQ_ROUTE_TILED &&
+        !nqk::tiled_fits(plan.tile_m, plan.tile_n, bits, group_size, sb_dt, batch * l, n, k)) {
+        while (per_launch > 1 && !nqk::tiled_fits(plan.tile_m, plan.tile_n, bits, group_size, sb_dt,
+                                                   per_launch * l, n, k))
+            per_launch = (per_launch + 1) / 2;
+        // every launch's y starts 16-byte aligned
+        int64_t unit = 1;
+        while ((unit * l * n * xb) % 16) unit *= 2;
+        if (per_launch < unit)
+            return fail(NQ_ERR_SHAPE, "%s: items of l=%lld rows are too large to batch", op, (long long)l);
+        per_launch -= per_launch % unit;
+    }
+    for (int64_t i0 = 0; i0 < batch; i0 += per_launch) {
+        QmmArgs part = a;
+        part.m = std::min(per_launch, batch - i0) * l;
+        part.x = static_cast<const char *>(x) + i0 * l * k * xb;
+        part.y = static_cast<char *>(y) + i0 * l * n * xb;
+        if ((st = run_qmm(op, plan, part, stream))) return st;
+    }
+    return NQ_OK;
+}
+
 namespace {
 // Gather routes ("Mixture of experts" section).  Once experts are shared by
 // several vectors (at least 16 vectors, 4 per expert on average) the

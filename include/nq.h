@@ -169,6 +169,20 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
                            int32_t bits, void *y, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* A product over batch items that keeps each item's solo bits ("Products on
+ * the GPU" section: batch items of a quantized product each get the bits of
+ * their product alone, the split of K counted per item).  x [batch, l, k]
+ * (x_dt), y [batch, l, n] (x_dt), weights as for nq_qmm; item i of y is
+ * bit-equal to nq_qmm(x[i]) with m = l, whatever batch is, because the
+ * route is nq_qmm_plan(l, ...) (not of batch * l rows) and no kernel's
+ * result for an element depends on the other rows of its launch.  Errors
+ * and conventions as for nq_qmm, with m = batch * l; NQ_ERR_SHAPE if
+ * batch * l overflows. */
+nq_status nq_qmm_batched(const void *x, nq_dtype x_dt, int64_t batch, int64_t l, int64_t k,
+                         const uint32_t *codes, const void *scales, const void *biases,
+                         nq_dtype sb_dt, int64_t n, int32_t group_size, int32_t bits, void *y,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- weights as stored, derivatives */
 
 /* Workspace bytes nq_qmm_notrans / nq_qmm_notrans_row_exact need: 0 on the

@@ -146,6 +146,27 @@ def test_qmm_argument_errors(lib, entry):
         assert err.startswith(entry + ":") and msg in err, (kw, err)
 
 
+def test_batched_argument_errors(lib):
+    def q(**kw):
+        a = dict(x=FAKE, x_dt=BF16, batch=3, l=4, k=128, codes=FAKE2, scales=FAKE2 + 0x100000,
+                 biases=FAKE2 + 0x200000, sb_dt=BF16, n=64, gs=64, bits=4, y=FAKE2 + 0x300000)
+        a.update(kw)
+        return lib.nq_qmm_batched(a["x"], a["x_dt"], a["batch"], a["l"], a["k"], a["codes"],
+                                  a["scales"], a["biases"], a["sb_dt"], a["n"], a["gs"], a["bits"],
+                                  a["y"], 0, 0, None)
+    assert q(batch=-1) == NQ_ERR_SHAPE
+    assert q(l=-1) == NQ_ERR_SHAPE
+    assert q(batch=1 << 20, l=1 << 20) == NQ_ERR_SHAPE
+    assert q(k=100) == NQ_ERR_SHAPE
+    assert q(bits=7) == NQ_ERR_QUANT
+    assert q(y=0) == NQ_ERR_NULL
+    # x spans batch * l rows of k
+    assert q(y=FAKE + 3 * 4 * 128 * 2 - 16) == NQ_ERR_ALIAS
+    assert b"nq_qmm_batched: y overlaps x" in lib.nq_last_error()
+    assert q(batch=0, x=0, y=0) == NQ_OK
+    assert q(l=0, x=0, y=0) == NQ_OK
+
+
 def test_empty_products_enqueue_nothing(lib):
     # m == 0 or n == 0: OK without touching any pointer (all null here)
     assert _qmm(lib, m=0, x=0, codes=0, scales=0, biases=0, y=0) == NQ_OK

@@ -399,6 +399,30 @@ def test_gather_lhs(case):
                       B.nq_gather_qmm_row_exact(xr, cs, ss, bs, gs, bits, dr))
 
 
+@pytest.mark.parametrize("batch,l,n,k,bits,x_dtype", [
+    (3, 5, 200, 1024, 4, "bf16"),     # items on the matrix-vector route, 15 rows on the tiles
+    (3, 100, 300, 1024, 4, "bf16"),   # items on 128-row tiles, all rows on 256-row tiles
+    (2, 300, 512, 2048, 8, "bf16"),   # items on 256-row tiles
+    (4, 40, 130, 640, 3, "bf16"),     # another width, ragged n
+    (2, 20, 96, 512, 4, "f32"),       # fp32 x: matrix-vector route at any size
+])
+def test_qmm_batched_items_keep_solo_bits(batch, l, n, k, bits, x_dtype):
+    """Batch items of a quantized product ("Products on the GPU" section):
+    item i of nq_qmm_batched over [batch, l, k] is bit-equal to nq_qmm on
+    x[i] alone, and within the product tolerance of the oracle."""
+    gs = 64
+    w, x, c, s, b = quantized_case(batch * l + bits, n, k, gs, bits, "bf16", m=batch * l, x_dtype=x_dtype)
+    x3 = x.reshape(batch, l, k)
+    xs, cs, ss, bs = dev(x3), dev(c), dev(s), dev(b)
+    y = B.nq_qmm_batched(xs, cs, ss, bs, gs, bits)
+    assert y.shape == (batch, l, n)
+    for i in range(batch):
+        assert bits_equal(y[i], B.nq_qmm(xs[i], cs, ss, bs, gs, bits)), i
+    y_ref = O.qmm_f64(x, c, s, b, gs, bits)
+    assert_rows_close(values(host(y)).reshape(batch * l, n), y_ref, tolerance(y.dtype), "batched")
+    assert bits_equal(y, B.nq_qmm_batched(xs, cs, ss, bs, gs, bits))
+
+
 # ------------------------------------------------------------------ other widths
 
 
