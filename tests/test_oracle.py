@@ -460,3 +460,8 @@ def test_gather_with_left_indices(oracle_mod):
     y1 = oracle_mod.gather_qmm_lhs_f64(x, c[:1], s[:1], b[:1], 64, 4, lhs, np.zeros(6, np.uint32))
     assert np.array_equal(y1.reshape(12, 16),
                           oracle_mod.qmm_f64(x[lhs].reshape(12, 128), c[0], s[0], b[0], 64, 4))
+    # a left index past the x items gives a zero row, as an expert id past e does
+    yz = oracle_mod.gather_qmm_lhs_f64(x, c, s, b, 64, 4, np.array([4, 1, 0xFFFFFFFF], np.uint32),
+                                       np.array([0, 1, 2], np.uint32))
+    assert np.all(yz[0] == 0) and np.all(yz[2] == 0)
+    assert np.array_equal(yz[1], oracle_mod.qmm_f64(x[1], c[1], s[1], b[1], 64, 4))
