@@ -232,7 +232,7 @@ def main():
     traffic = measured_traffic("decode_gemv")
     out["roofline"] = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                       "traffic": traffic, "kernel": "gemv_kernel<4,bf16,bf16,1,2,1>",
+                       "traffic": traffic, "kernel": "gemv_stream_kernel<bf16,2,14>",
                        "launch_us": round(dec_launch_s * 1e6, 3)}
     del copies2
 

@@ -531,6 +531,130 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 }
 
 // ---------------------------------------------------------------------------
+// One activation row with 4-bit codes and bf16 activations, K in at most
+// kStreamMaxSteps steps and not split: a streaming form of the kernel above.
+// Every wave keeps the activation pairs and chunk sums of all its steps in
+// registers and walks NR weight rows spaced by the wave count W (rows
+// w, w + W, w + 2W, ...: at any moment the waves read one contiguous band of
+// the weights), loading rows kStreamDepth ahead of the one it computes.  The
+// row loop is straight-line code (lanes past k compute on clamped data and a
+// select drops the result), so the only waits are the counted ones for the
+// row about to be used.  Per lane and row the arithmetic is that of
+// gemv_kernel (same lane chunks, same operation order) and the lane sums take
+// the same xor tree, so every row has the bits gemv_kernel gives it.  Rows
+// past n read row n - 1 and are not stored.
+constexpr int kStreamMaxSteps = 4;
+constexpr int kStreamDepth = 3;
+constexpr int kStreamWaves = 4;   // waves per workgroup
+
+template <int STEPS>
+struct StreamStage {
+    uint32_t s[STEPS], b[STEPS];
+    uint4 c[STEPS];
+};
+
+template <typename ST, int STEPS, int NR>
+__global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvParams<bf16_bits, ST> p)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * kStreamWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
+    constexpr uint32_t kMag = 0x43434343u;
+
+    // activation pairs and chunk sums of every step
+    uint32_t xp[STEPS][16];
+    float X[STEPS];
+    bool on[STEPS];
+    int64_t e0[STEPS], g0[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+        const int64_t e = (int64_t)t * kStepElems + lane * kLaneChunk;
+        on[t] = e < p.k;
+        e0[t] = on[t] ? e : 0;
+        g0[t] = e0[t] / p.gs;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.x + e0[t]);
+        X[t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 d = src[j];
+            x_pairs_word(d, xp[t] + 4 * j);
+            X[t] = x_sum_word(d, X[t]);
+        }
+    }
+
+    auto row_of = [&](int i) -> int64_t { return min(w + (int64_t)i * nw, p.n - 1); };
+    auto load = [&](int i, StreamStage<STEPS> &st) {
+        const int64_t r = row_of(i);
+        const uint32_t *crow = p.codes + r * p.words_per_row;
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            st.s[t] = load_raw(p.scales, r * p.groups_per_row + g0[t]);
+            st.b[t] = load_raw(p.biases, r * p.groups_per_row + g0[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+            const u32x4_t d = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(crow + e0[t] / 8));
+            st.c[t] = make_uint4(d.x, d.y, d.z, d.w);
+        }
+    };
+    auto compute = [&](const StreamStage<STEPS> &st) -> float {
+        float a = 0.0f;
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            const uint32_t cw[4] = {st.c[t].x, st.c[t].y, st.c[t].z, st.c[t].w};
+            float D = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) D = word_dot_magic(cw[j], xp[t] + 4 * j, kMag, D);
+            const float T = fmaf(-128.0f, X[t], D);
+            float an = fmaf(raw_to_f32<ST>(st.s[t]), T, a);
+            an = fmaf(raw_to_f32<ST>(st.b[t]), X[t], an);
+            a = pick(on[t], an, a);
+        }
+        return a;
+    };
+
+    constexpr int V = NR <= 8 ? 8 : 16;
+    float acc[V];
+    StreamStage<STEPS> st[kStreamDepth + 1];
+#pragma unroll
+    for (int i = 0; i < kStreamDepth && i < NR; ++i) load(i, st[i]);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        if (i + kStreamDepth < NR) load(i + kStreamDepth, st[(i + kStreamDepth) % (kStreamDepth + 1)]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the arithmetic
+        acc[i] = compute(st[i % (kStreamDepth + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = NR; i < V; ++i) acc[i] = 0.0f;
+    const float mine = wave_reduce_transposed<V>(acc, lane);
+    constexpr int kShift = 6 - ilog2<V>();
+    const int vi = lane >> kShift;
+    const int64_t row = w + (int64_t)vi * nw;
+    if ((lane & ((1 << kShift) - 1)) == 0 && vi < NR && row < p.n) Elt<bf16_bits>::store(p.y, row, mine);
+}
+
+// Launch shape of the streaming kernel for n rows on `cus` compute units:
+// a whole number of workgroups per compute unit (an uneven count leaves some
+// units with twice the rows), and rows per wave the smallest of 8, 10, ..., 16
+// that covers n.
+struct StreamShape {
+    int64_t groups;
+    int nr;
+};
+
+StreamShape stream_shape(int64_t n, int cus)
+{
+    const int64_t per_cu = (n + (int64_t)cus * kStreamWaves * 16 - 1) / ((int64_t)cus * kStreamWaves * 16);
+    StreamShape sh;
+    sh.groups = std::max<int64_t>(1, per_cu) * cus;
+    const int64_t need = (n + sh.groups * kStreamWaves - 1) / (sh.groups * kStreamWaves);
+    sh.nr = need <= 8 ? 8 : (int)((need + 1) / 2 * 2);
+    return sh;
+}
+
+// ---------------------------------------------------------------------------
 // Grouping pass of the grouped gather ("Mixture of experts" section: a
 // grouped kernel reads each expert's weights once for the rows that chose
 // it).  One workgroup sorts the activation vectors v = r * l + j by expert
@@ -832,10 +956,68 @@ hipError_t gemv_run(const GemvLaunch &a, hipStream_t stream)
 // Rows per wave: 2 for one or two activation rows (more waves, shorter
 // per-wave work), else 4 (more reuse of the activations).  It does not
 // change any row's arithmetic.
+template <typename ST, int STEPS, int NR>
+hipError_t gemv_stream_run(const GemvLaunch &a, int64_t groups, hipStream_t stream)
+{
+    GemvParams<bf16_bits, ST> p{};
+    p.x = static_cast<const bf16_bits *>(a.x);
+    p.y = static_cast<bf16_bits *>(a.y);
+    p.codes = a.codes;
+    p.scales = static_cast<const ST *>(a.scales);
+    p.biases = static_cast<const ST *>(a.biases);
+    p.k = a.k;
+    p.n = a.n;
+    p.words_per_row = a.k * 4 / 32;
+    p.groups_per_row = a.k / a.gs;
+    p.gs = a.gs;
+    gemv_stream_kernel<ST, STEPS, NR><<<dim3((unsigned)groups), dim3(64 * kStreamWaves), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+template <typename ST, int STEPS>
+hipError_t gemv_stream_nr(const GemvLaunch &a, hipStream_t stream)
+{
+    int dev = 0, cus = 0;
+    if (hipError_t err = hipGetDevice(&dev)) return err;
+    if (hipError_t err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return err;
+    const StreamShape sh = stream_shape(a.n, std::max(cus, 1));
+    switch (sh.nr) {
+    case 16: return gemv_stream_run<ST, STEPS, 16>(a, sh.groups, stream);
+    case 14: return gemv_stream_run<ST, STEPS, 14>(a, sh.groups, stream);
+    case 12: return gemv_stream_run<ST, STEPS, 12>(a, sh.groups, stream);
+    case 10: return gemv_stream_run<ST, STEPS, 10>(a, sh.groups, stream);
+    default: return gemv_stream_run<ST, STEPS, 8>(a, sh.groups, stream);
+    }
+}
+
+// The streaming kernel serves a plain one-row product (no gather) with
+// enough weight rows to give every wave 8 or more, K unsplit.
+bool gemv_stream_fits(const GemvLaunch &a)
+{
+    const int64_t steps = (a.k + kStepElems - 1) / kStepElems;
+    return a.bits == 4 && a.x_dt == DT_BF16 && a.items == 1 && a.rows_per_item == 1 && !a.idx &&
+           !a.chunks && !a.lhs && a.ksplit == 1 && a.rows_per_wave == 0 && steps >= 1 &&
+           steps <= kStreamMaxSteps && a.n >= 8 * 1024;
+}
+
+template <typename ST>
+hipError_t gemv_stream(const GemvLaunch &a, hipStream_t stream)
+{
+    switch ((a.k + kStepElems - 1) / kStepElems) {
+    case 1: return gemv_stream_nr<ST, 1>(a, stream);
+    case 2: return gemv_stream_nr<ST, 2>(a, stream);
+    case 3: return gemv_stream_nr<ST, 3>(a, stream);
+    default: return gemv_stream_nr<ST, 4>(a, stream);
+    }
+}
+
 template <int BITS, typename XT, typename ST, int MR>
 hipError_t gemv_mr(const GemvLaunch &a, hipStream_t stream)
 {
     constexpr int RW = MR <= 2 ? 2 : 4;
+    if constexpr (BITS == 4 && MR == 1 && sizeof(XT) == 2) {
+        if (gemv_stream_fits(a)) return gemv_stream<ST>(a, stream);
+    }
     if (a.rows_per_wave != 0 && a.rows_per_wave != RW) return hipErrorInvalidValue;
     if constexpr (BITS == 4 && sizeof(XT) == 2 && MR <= 2) {
         const int steps = (int)((a.k + kStepElems - 1) / kStepElems);

@@ -116,6 +116,29 @@ def test_splitk_parity(ksplit, x_dtype):
         assert bits_equal(yi[0], y[i])
 
 
+@pytest.mark.parametrize("n,k,w_dtype", [(14336, 4096, "bf16"), (8192, 2048, "f32"),
+                                         (16500, 6144, "bf16"), (9000, 7936, "bf16")])
+def test_decode_streaming_rows_keep_bits(n, k, w_dtype):
+    """Long one-row products (many weight rows, K unsplit) run a streaming
+    form of the matrix-vector kernel; its rows have the bits the kernel with
+    2 rows per wave gives them (a forced plan), and the bits of the same row
+    in a 2-row call."""
+    gs, bits = 64, 4
+    w, x, c, s, b = quantized_case(n + k, n, k, gs, bits, w_dtype, 2, "bf16", 0.02)
+    plan = B.nq_qmm_plan(1, n, k, gs, bits, torch.bfloat16,
+                         torch.float32 if w_dtype == "f32" else torch.bfloat16)
+    assert plan.route == B.NQ_ROUTE_GEMV and plan.ksplit == 1
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y1 = B.nq_qmm(xs[:1].contiguous(), *q, gs, bits)
+    forced = B.Plan()
+    forced.route, forced.ksplit, forced.rows_per_wave = B.NQ_ROUTE_GEMV, 1, 2
+    assert bits_equal(y1, B.nq_qmm_with_plan(forced, xs[:1].contiguous(), *q, gs, bits))
+    y2 = B.nq_qmm(xs, *q, gs, bits)
+    assert bits_equal(y1[0], y2[0])
+    assert_rows_close(values(host(y1)), O.qmm_f64(x[:1], c, s, b, gs, bits), 1e-2, "streaming decode")
+    assert bits_equal(y1, B.nq_qmm(xs[:1].contiguous(), *q, gs, bits))
+
+
 def test_splitk_is_chosen_for_long_k():
     p = B.nq_qmm_plan(4, 1024, 14336, 64, 4, torch.bfloat16, torch.bfloat16)
     assert p.route == B.NQ_ROUTE_GEMV and p.ksplit > 1
