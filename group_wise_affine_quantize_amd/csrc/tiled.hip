@@ -664,15 +664,8 @@ __device__ bool gather_self_group(const uint32_t *ids, const uint32_t *lhs, int6
                 const int64_t rr = v / l;   // rows with lhs past the x items: the zero bucket
                 bk[r] = lhs && (int64_t)lhs[rr] >= x_items ? (uint32_t)e : min(ids[rr], (uint32_t)e);
             }
-            // one atomic per distinct bucket of the wave
-            uint64_t active = __ballot(bk[r] != 0xffffffffu);
-            while (active) {
-                const int leader = __ffsll((long long)active) - 1;
-                const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bk[r], leader);
-                const uint64_t m = __ballot(bk[r] == lb) & active;
-                if (lane == leader) atomicAdd(&gh[lb], (uint32_t)__popcll(m));
-                active &= ~m;
-            }
+            // counts by LDS atomics (the sums do not depend on their order)
+            if (bk[r] != 0xffffffffu) atomicAdd(&gh[bk[r]], 1u);
         }
     }
     __syncthreads();
