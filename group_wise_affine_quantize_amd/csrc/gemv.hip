@@ -35,7 +35,10 @@
 // same order ((x0,x2) (x4,x6) (x1,x3) (x5,x7) per word) and the
 // 128 * sum(x) offset is removed once per lane chunk.  For one or two
 // activation rows the pairs and chunk sums are prepared once per workgroup in
-// LDS.  Other cases convert codes to fp32 and use fp32 FMAs.
+// LDS.  8-bit codes with bf16 activations are exact in bf16 too: each code
+// word becomes two bf16 pairs (v_cvt_f32_ubyte and the high halves), made
+// once per weight row and dotted with the activations' own bf16 pairs by
+// every activation row.  Other cases convert codes to fp32 and use fp32 FMAs.
 #include <algorithm>
 
 #include "nq_device.h"
@@ -238,6 +241,7 @@ template <int BITS, typename XT, typename ST, int MR, int RW, int STX>
 __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 {
     constexpr bool kMagic = (BITS == 4) && (sizeof(XT) == 2);
+    constexpr bool kBytePairs = (BITS == 8) && (sizeof(XT) == 2);
     static_assert(STX == 0 || kMagic, "staged activations hold bf16 pairs for 4-bit codes");
     // without staging, activations travel with the codes when they are few
     constexpr int kXW = (STX == 0 && MR <= 2) ? MR * (kLaneChunk * (int)sizeof(XT) / 16) : 0;
@@ -410,6 +414,41 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) D = word_dot_magic(st.cw[r][j], xp + 4 * j, kMag, D);
                     T[m][r] = fmaf(-128.0f, X[m], D);
+                }
+            }
+        } else if constexpr (kBytePairs) {
+            // 8-bit codes are exact in bf16: each weight row's 32 codes become
+            // 16 bf16 pairs once (v_cvt_f32_ubyte, then the high halves), and
+            // every activation row takes 16 dot2 against its own bf16 pairs
+            uint32_t qp[RW][16];
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t w = st.cw[r][j];
+                    const float f0 = (float)(w & 0xffu), f1 = (float)((w >> 8) & 0xffu);
+                    const float f2 = (float)((w >> 16) & 0xffu), f3 = (float)(w >> 24);
+                    qp[r][2 * j] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+                    qp[r][2 * j + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+                }
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                uint32_t xd[16];
+                X[m] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint4 d;
+                    if constexpr (kXW > 0) d = st.xr[m * kXWR + j];
+                    else d = reinterpret_cast<const uint4 *>(x_row(m) + e0)[j];
+                    xd[4 * j] = d.x, xd[4 * j + 1] = d.y, xd[4 * j + 2] = d.z, xd[4 * j + 3] = d.w;
+                    X[m] = x_sum_word(d, X[m]);
+                }
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    float D = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) D = dot2_bf16(xd[u], qp[r][u], D);
+                    T[m][r] = D;
                 }
             }
         } else {
