@@ -570,7 +570,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 }
 
 // ---------------------------------------------------------------------------
-// One activation row with 4-bit codes and bf16 activations, K in at most
+// One activation row of bf16 activations (any code width), K in at most
 // kStreamMaxSteps steps and not split: a streaming form of the kernel above.
 // Every wave keeps the activation pairs and chunk sums of all its steps in
 // registers and walks NR weight rows spaced by the wave count W (rows
@@ -586,13 +586,21 @@ constexpr int kStreamMaxSteps = 4;
 constexpr int kStreamDepth = 3;
 constexpr int kStreamWaves = 4;   // waves per workgroup
 
-template <int STEPS>
+template <int BITS, int STEPS>
 struct StreamStage {
     uint32_t s[STEPS], b[STEPS];
-    uint4 c[STEPS];
+    uint32_t c[STEPS][BITS];
 };
 
-template <typename ST, int STEPS, int NR>
+// Per-step activations held by a wave: 4-bit codes, the pairs in code-pair
+// order; 8-bit codes, the bf16 pairs as stored; other widths, fp32 values.
+template <int BITS>
+struct StreamX {
+    static constexpr int kWords = BITS == 4 || BITS == 8 ? 16 : 32;
+    uint32_t v[kWords];
+};
+
+template <int BITS, typename ST, int STEPS, int NR>
 __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvParams<bf16_bits, ST> p)
 {
     const int lane = threadIdx.x & 63;
@@ -600,8 +608,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
     const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
     constexpr uint32_t kMag = 0x43434343u;
 
-    // activation pairs and chunk sums of every step
-    uint32_t xp[STEPS][16];
+    // activations and chunk sums of every step, in gemv_kernel's order
+    StreamX<BITS> xs[STEPS];
     float X[STEPS];
     bool on[STEPS];
     int64_t e0[STEPS], g0[STEPS];
@@ -616,13 +624,26 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint4 d = src[j];
-            x_pairs_word(d, xp[t] + 4 * j);
-            X[t] = x_sum_word(d, X[t]);
+            if constexpr (BITS == 4) {
+                x_pairs_word(d, xs[t].v + 4 * j);
+                X[t] = x_sum_word(d, X[t]);
+            } else if constexpr (BITS == 8) {
+                xs[t].v[4 * j] = d.x, xs[t].v[4 * j + 1] = d.y, xs[t].v[4 * j + 2] = d.z, xs[t].v[4 * j + 3] = d.w;
+                X[t] = x_sum_word(d, X[t]);
+            } else {
+                float xf[8];
+                x_f32_word<bf16_bits>(src, j, xf);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    xs[t].v[8 * j + i] = __float_as_uint(xf[i]);
+                    X[t] += xf[i];
+                }
+            }
         }
     }
 
     auto row_of = [&](int i) -> int64_t { return min(w + (int64_t)i * nw, p.n - 1); };
-    auto load = [&](int i, StreamStage<STEPS> &st) {
+    auto load = [&](int i, StreamStage<BITS, STEPS> &st) {
         const int64_t r = row_of(i);
         const uint32_t *crow = p.codes + r * p.words_per_row;
 #pragma unroll
@@ -631,21 +652,35 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
             st.b[t] = load_raw(p.biases, r * p.groups_per_row + g0[t]);
         }
 #pragma unroll
-        for (int t = 0; t < STEPS; ++t) {
-            typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-            const u32x4_t d = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(crow + e0[t] / 8));
-            st.c[t] = make_uint4(d.x, d.y, d.z, d.w);
-        }
+        for (int t = 0; t < STEPS; ++t) load_chunk_words<BITS>(crow + e0[t] * BITS / 32, st.c[t]);
     };
-    auto compute = [&](const StreamStage<STEPS> &st) -> float {
+    auto compute = [&](const StreamStage<BITS, STEPS> &st) -> float {
         float a = 0.0f;
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
-            const uint32_t cw[4] = {st.c[t].x, st.c[t].y, st.c[t].z, st.c[t].w};
-            float D = 0.0f;
+            float T;
+            if constexpr (BITS == 4) {
+                float D = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) D = word_dot_magic(cw[j], xp[t] + 4 * j, kMag, D);
-            const float T = fmaf(-128.0f, X[t], D);
+                for (int j = 0; j < 4; ++j) D = word_dot_magic(st.c[t][j], xs[t].v + 4 * j, kMag, D);
+                T = fmaf(-128.0f, X[t], D);
+            } else if constexpr (BITS == 8) {
+                float D = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t cw = st.c[t][j];
+                    const float f0 = (float)(cw & 0xffu), f1 = (float)((cw >> 8) & 0xffu);
+                    const float f2 = (float)((cw >> 16) & 0xffu), f3 = (float)(cw >> 24);
+                    D = dot2_bf16(xs[t].v[2 * j], __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u), D);
+                    D = dot2_bf16(xs[t].v[2 * j + 1], __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u), D);
+                }
+                T = D;
+            } else {
+                T = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kLaneChunk; ++i)
+                    T = fmaf(__uint_as_float(xs[t].v[i]), (float)code_at<BITS>(st.c[t], i), T);
+            }
             float an = fmaf(raw_to_f32<ST>(st.s[t]), T, a);
             an = fmaf(raw_to_f32<ST>(st.b[t]), X[t], an);
             a = pick(on[t], an, a);
@@ -655,7 +690,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
 
     constexpr int V = NR <= 8 ? 8 : 16;
     float acc[V];
-    StreamStage<STEPS> st[kStreamDepth + 1];
+    StreamStage<BITS, STEPS> st[kStreamDepth + 1];
 #pragma unroll
     for (int i = 0; i < kStreamDepth && i < NR; ++i) load(i, st[i]);
 #pragma unroll
@@ -992,10 +1027,7 @@ hipError_t gemv_run(const GemvLaunch &a, hipStream_t stream)
     return hipSuccess;
 }
 
-// Rows per wave: 2 for one or two activation rows (more waves, shorter
-// per-wave work), else 4 (more reuse of the activations).  It does not
-// change any row's arithmetic.
-template <typename ST, int STEPS, int NR>
+template <int BITS, typename ST, int STEPS, int NR>
 hipError_t gemv_stream_run(const GemvLaunch &a, int64_t groups, hipStream_t stream)
 {
     GemvParams<bf16_bits, ST> p{};
@@ -1006,14 +1038,14 @@ hipError_t gemv_stream_run(const GemvLaunch &a, int64_t groups, hipStream_t stre
     p.biases = static_cast<const ST *>(a.biases);
     p.k = a.k;
     p.n = a.n;
-    p.words_per_row = a.k * 4 / 32;
+    p.words_per_row = a.k * BITS / 32;
     p.groups_per_row = a.k / a.gs;
     p.gs = a.gs;
-    gemv_stream_kernel<ST, STEPS, NR><<<dim3((unsigned)groups), dim3(64 * kStreamWaves), 0, stream>>>(p);
+    gemv_stream_kernel<BITS, ST, STEPS, NR><<<dim3((unsigned)groups), dim3(64 * kStreamWaves), 0, stream>>>(p);
     return hipGetLastError();
 }
 
-template <typename ST, int STEPS>
+template <int BITS, typename ST, int STEPS>
 hipError_t gemv_stream_nr(const GemvLaunch &a, hipStream_t stream)
 {
     int dev = 0, cus = 0;
@@ -1021,11 +1053,11 @@ hipError_t gemv_stream_nr(const GemvLaunch &a, hipStream_t stream)
     if (hipError_t err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return err;
     const StreamShape sh = stream_shape(a.n, std::max(cus, 1));
     switch (sh.nr) {
-    case 16: return gemv_stream_run<ST, STEPS, 16>(a, sh.groups, stream);
-    case 14: return gemv_stream_run<ST, STEPS, 14>(a, sh.groups, stream);
-    case 12: return gemv_stream_run<ST, STEPS, 12>(a, sh.groups, stream);
-    case 10: return gemv_stream_run<ST, STEPS, 10>(a, sh.groups, stream);
-    default: return gemv_stream_run<ST, STEPS, 8>(a, sh.groups, stream);
+    case 16: return gemv_stream_run<BITS, ST, STEPS, 16>(a, sh.groups, stream);
+    case 14: return gemv_stream_run<BITS, ST, STEPS, 14>(a, sh.groups, stream);
+    case 12: return gemv_stream_run<BITS, ST, STEPS, 12>(a, sh.groups, stream);
+    case 10: return gemv_stream_run<BITS, ST, STEPS, 10>(a, sh.groups, stream);
+    default: return gemv_stream_run<BITS, ST, STEPS, 8>(a, sh.groups, stream);
     }
 }
 
@@ -1034,28 +1066,31 @@ hipError_t gemv_stream_nr(const GemvLaunch &a, hipStream_t stream)
 bool gemv_stream_fits(const GemvLaunch &a)
 {
     const int64_t steps = (a.k + kStepElems - 1) / kStepElems;
-    return a.bits == 4 && a.x_dt == DT_BF16 && a.items == 1 && a.rows_per_item == 1 && !a.idx &&
+    return a.x_dt == DT_BF16 && a.items == 1 && a.rows_per_item == 1 && !a.idx &&
            !a.chunks && !a.lhs && a.ksplit == 1 && a.rows_per_wave == 0 && steps >= 1 &&
            steps <= kStreamMaxSteps && a.n >= 8 * 1024;
 }
 
-template <typename ST>
+template <int BITS, typename ST>
 hipError_t gemv_stream(const GemvLaunch &a, hipStream_t stream)
 {
     switch ((a.k + kStepElems - 1) / kStepElems) {
-    case 1: return gemv_stream_nr<ST, 1>(a, stream);
-    case 2: return gemv_stream_nr<ST, 2>(a, stream);
-    case 3: return gemv_stream_nr<ST, 3>(a, stream);
-    default: return gemv_stream_nr<ST, 4>(a, stream);
+    case 1: return gemv_stream_nr<BITS, ST, 1>(a, stream);
+    case 2: return gemv_stream_nr<BITS, ST, 2>(a, stream);
+    case 3: return gemv_stream_nr<BITS, ST, 3>(a, stream);
+    default: return gemv_stream_nr<BITS, ST, 4>(a, stream);
     }
 }
 
+// Rows per wave: 2 for one or two activation rows (more waves, shorter
+// per-wave work), else 4 (more reuse of the activations).  It does not
+// change any row's arithmetic.
 template <int BITS, typename XT, typename ST, int MR>
 hipError_t gemv_mr(const GemvLaunch &a, hipStream_t stream)
 {
     constexpr int RW = MR <= 2 ? 2 : 4;
-    if constexpr (BITS == 4 && MR == 1 && sizeof(XT) == 2) {
-        if (gemv_stream_fits(a)) return gemv_stream<ST>(a, stream);
+    if constexpr (MR == 1 && sizeof(XT) == 2) {
+        if (gemv_stream_fits(a)) return gemv_stream<BITS, ST>(a, stream);
     }
     if (a.rows_per_wave != 0 && a.rows_per_wave != RW) return hipErrorInvalidValue;
     if constexpr (BITS == 4 && sizeof(XT) == 2 && MR <= 2) {

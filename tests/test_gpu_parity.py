@@ -116,14 +116,16 @@ def test_splitk_parity(ksplit, x_dtype):
         assert bits_equal(yi[0], y[i])
 
 
-@pytest.mark.parametrize("n,k,w_dtype", [(14336, 4096, "bf16"), (8192, 2048, "f32"),
-                                         (16500, 6144, "bf16"), (9000, 7936, "bf16")])
-def test_decode_streaming_rows_keep_bits(n, k, w_dtype):
+@pytest.mark.parametrize("n,k,w_dtype,bits", [
+    (14336, 4096, "bf16", 4), (8192, 2048, "f32", 4), (16500, 6144, "bf16", 4), (9000, 7936, "bf16", 4),
+    (9000, 4096, "bf16", 8), (8200, 6080, "f32", 8), (8192, 4096, "bf16", 1), (8300, 2048, "bf16", 2),
+    (9000, 6144, "bf16", 3), (8192, 7936, "f32", 5), (10000, 4096, "bf16", 6)])
+def test_decode_streaming_rows_keep_bits(n, k, w_dtype, bits):
     """Long one-row products (many weight rows, K unsplit) run a streaming
-    form of the matrix-vector kernel; its rows have the bits the kernel with
-    2 rows per wave gives them (a forced plan), and the bits of the same row
-    in a 2-row call."""
-    gs, bits = 64, 4
+    form of the matrix-vector kernel at every width; its rows have the bits
+    the kernel with 2 rows per wave gives them (a forced plan), and the bits
+    of the same row in a 2-row call."""
+    gs = 64
     w, x, c, s, b = quantized_case(n + k, n, k, gs, bits, w_dtype, 2, "bf16", 0.02)
     plan = B.nq_qmm_plan(1, n, k, gs, bits, torch.bfloat16,
                          torch.float32 if w_dtype == "f32" else torch.bfloat16)
