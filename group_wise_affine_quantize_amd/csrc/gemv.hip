@@ -211,6 +211,63 @@ __device__ __forceinline__ float word_dot_magic(uint32_t w, const uint32_t *xp, 
     return dot2_bf16(xp[3], __builtin_amdgcn_perm(mag, hi, 0x04030402u), D); // (q5, q7)
 }
 
+// 1- and 2-bit codes with bf16 activations use the same (128 + q) pairs:
+// shifting a code word right by `bits` * i and masking every byte down to its
+// low `bits` bits leaves one code per byte, codes i, i + 32 / (4 bits), ...
+// (a stride of 8 at 1 bit, 4 at 2 bits), and two v_perm_b32 turn the four
+// bytes into two bf16 pairs.  The activation pairs follow that order.
+
+// Activation pairs of a lane chunk (32 bf16 in d[0..3]) in the order of the
+// code pairs of chunk_dot_magic<BITS>.
+template <int BITS>
+__device__ __forceinline__ void x_pairs_chunk(const uint4 *d, uint32_t *xp)
+{
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x_pairs_word(d[j], xp + 4 * j);
+    } else {
+        uint32_t v[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * j] = d[j].x, v[4 * j + 1] = d[j].y, v[4 * j + 2] = d[j].z, v[4 * j + 3] = d[j].w;
+        // element e of the chunk is half e % 2 of dword e / 2
+        auto pair = [&](int a, int b) -> uint32_t {   // (x_a, x_b), a % 2 == b % 2
+            return __builtin_amdgcn_perm(v[b >> 1], v[a >> 1], (a & 1) ? 0x07060302u : 0x05040100u);
+        };
+        constexpr int kWordCodes = 32 / BITS;      // codes per word: 16 or 32
+        constexpr int kStride = kWordCodes / 4;    // code stride inside a byte lane: 4 or 8
+#pragma unroll
+        for (int h = 0; h < BITS; ++h)             // word h of the chunk
+#pragma unroll
+            for (int i = 0; i < kStride; ++i) {
+                const int c0 = h * kWordCodes + i;
+                xp[2 * (h * kStride + i)] = pair(c0, c0 + kStride);
+                xp[2 * (h * kStride + i) + 1] = pair(c0 + 2 * kStride, c0 + 3 * kStride);
+            }
+    }
+}
+
+// D += sum over the lane chunk's 32 codes (words cw[0 .. BITS)) of x * (128 + q).
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_magic(const uint32_t *cw, const uint32_t *xp, uint32_t mag, float D)
+{
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) D = word_dot_magic(cw[j], xp + 4 * j, mag, D);
+    } else {
+        constexpr uint32_t kMask = BITS == 1 ? 0x01010101u : 0x03030303u;
+        constexpr int kStride = 8 / BITS;
+#pragma unroll
+        for (int h = 0; h < BITS; ++h)
+#pragma unroll
+            for (int i = 0; i < kStride; ++i) {
+                const uint32_t b = (cw[h] >> (BITS * i)) & kMask;   // codes i, i + s, i + 2 s, i + 3 s
+                D = dot2_bf16(xp[2 * (h * kStride + i)], __builtin_amdgcn_perm(mag, b, 0x04010400u), D);
+                D = dot2_bf16(xp[2 * (h * kStride + i) + 1], __builtin_amdgcn_perm(mag, b, 0x04030402u), D);
+            }
+    }
+    return D;
+}
+
 // The fp32 activations of a lane chunk's word j (8 values).
 template <typename XT>
 __device__ __forceinline__ void x_f32_word(const uint4 *xw, int j, float *xf)
@@ -240,9 +297,9 @@ constexpr int kStageBytesPerStep = 4 * 64 * 16 + 64 * 4;
 template <int BITS, typename XT, typename ST, int MR, int RW, int STX>
 __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
 {
-    constexpr bool kMagic = (BITS == 4) && (sizeof(XT) == 2);
+    constexpr bool kMagic = (BITS == 1 || BITS == 2 || BITS == 4) && (sizeof(XT) == 2);
     constexpr bool kBytePairs = (BITS == 8) && (sizeof(XT) == 2);
-    static_assert(STX == 0 || kMagic, "staged activations hold bf16 pairs for 4-bit codes");
+    static_assert(STX == 0 || (kMagic && BITS == 4), "staged activations hold bf16 pairs for 4-bit codes");
     // without staging, activations travel with the codes when they are few
     constexpr int kXW = (STX == 0 && MR <= 2) ? MR * (kLaneChunk * (int)sizeof(XT) / 16) : 0;
     constexpr int kXWR = kLaneChunk * (int)sizeof(XT) / 16;   // 16-byte pieces per row chunk
@@ -399,20 +456,18 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams<XT, ST> p)
                     X[m] = sums[(m * p.steps + t) * 64 + lane];
                 } else {
                     X[m] = 0.0f;
+                    uint4 d[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        uint4 d;
-                        if constexpr (kXW > 0) d = st.xr[m * kXWR + j];
-                        else d = reinterpret_cast<const uint4 *>(x_row(m) + e0)[j];
-                        x_pairs_word(d, xp + 4 * j);
-                        X[m] = x_sum_word(d, X[m]);
+                        if constexpr (kXW > 0) d[j] = st.xr[m * kXWR + j];
+                        else d[j] = reinterpret_cast<const uint4 *>(x_row(m) + e0)[j];
+                        X[m] = x_sum_word(d[j], X[m]);
                     }
+                    x_pairs_chunk<BITS>(d, xp);
                 }
 #pragma unroll
                 for (int r = 0; r < RW; ++r) {
-                    float D = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) D = word_dot_magic(st.cw[r][j], xp + 4 * j, kMag, D);
+                    const float D = chunk_dot_magic<BITS>(st.cw[r], xp, kMag, 0.0f);
                     T[m][r] = fmaf(-128.0f, X[m], D);
                 }
             }
@@ -592,11 +647,12 @@ struct StreamStage {
     uint32_t c[STEPS][BITS];
 };
 
-// Per-step activations held by a wave: 4-bit codes, the pairs in code-pair
-// order; 8-bit codes, the bf16 pairs as stored; other widths, fp32 values.
+// Per-step activations held by a wave: 1-, 2- and 4-bit codes, the pairs in
+// code-pair order; 8-bit codes, the bf16 pairs as stored; other widths, fp32
+// values.
 template <int BITS>
 struct StreamX {
-    static constexpr int kWords = BITS == 4 || BITS == 8 ? 16 : 32;
+    static constexpr int kWords = BITS == 1 || BITS == 2 || BITS == 4 || BITS == 8 ? 16 : 32;
     uint32_t v[kWords];
 };
 
@@ -621,16 +677,24 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
         g0[t] = e0[t] / p.gs;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.x + e0[t]);
         X[t] = 0.0f;
+        if constexpr (BITS == 1 || BITS == 2 || BITS == 4) {
+            uint4 d[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 d = src[j];
-            if constexpr (BITS == 4) {
-                x_pairs_word(d, xs[t].v + 4 * j);
-                X[t] = x_sum_word(d, X[t]);
-            } else if constexpr (BITS == 8) {
+            for (int j = 0; j < 4; ++j) {
+                d[j] = src[j];
+                X[t] = x_sum_word(d[j], X[t]);
+            }
+            x_pairs_chunk<BITS>(d, xs[t].v);
+        } else if constexpr (BITS == 8) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 d = src[j];
                 xs[t].v[4 * j] = d.x, xs[t].v[4 * j + 1] = d.y, xs[t].v[4 * j + 2] = d.z, xs[t].v[4 * j + 3] = d.w;
                 X[t] = x_sum_word(d, X[t]);
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
                 float xf[8];
                 x_f32_word<bf16_bits>(src, j, xf);
 #pragma unroll
@@ -659,10 +723,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(GemvPara
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
             float T;
-            if constexpr (BITS == 4) {
-                float D = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) D = word_dot_magic(st.c[t][j], xs[t].v + 4 * j, kMag, D);
+            if constexpr (BITS == 1 || BITS == 2 || BITS == 4) {
+                const float D = chunk_dot_magic<BITS>(st.c[t], xs[t].v, kMag, 0.0f);
                 T = fmaf(-128.0f, X[t], D);
             } else if constexpr (BITS == 8) {
                 float D = 0.0f;
