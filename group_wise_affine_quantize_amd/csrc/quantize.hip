@@ -133,8 +133,16 @@ dequantize_kernel(const uint32_t *__restrict__ codes, const ST *__restrict__ sca
                   const ST *__restrict__ biases, int64_t chunks, int64_t k, int gs,
                   OT *__restrict__ out)
 {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= chunks) return;
+    // A lane's 32 outputs are 16-byte pieces; a wave's 64 chunks are one
+    // contiguous run of the output.  The pieces go through LDS so that store
+    // instruction i writes pieces 64 i .. 64 i + 63 of the run: 1 KB
+    // contiguous per instruction instead of 16 bytes every 64 or 128.
+    constexpr int kPieces = kLaneChunk * (int)sizeof(OT) / 16;   // 4 (bf16) or 8 (f32)
+    constexpr int kStride = kPieces + 1;                         // padded LDS row, in pieces
+    __shared__ uint4 stage[4][64 * kStride];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * blockDim.x + wave * 64;   // the wave's first chunk
+    const int64_t c = min(c0 + lane, chunks - 1);                       // past the end: a valid chunk, not stored
     const int64_t chunks_per_row = k / kLaneChunk;
     const int64_t row = c / chunks_per_row;
     const int64_t cir = c - row * chunks_per_row;
@@ -146,22 +154,37 @@ dequantize_kernel(const uint32_t *__restrict__ codes, const ST *__restrict__ sca
     float v[kLaneChunk];
 #pragma unroll
     for (int j = 0; j < kLaneChunk; ++j) v[j] = fmaf(s, (float)code_at<BITS>(wd, j), b);
-    OT *dst = out + c * kLaneChunk;
+    uint4 *st = stage[wave] + lane * kStride;
     if constexpr (sizeof(OT) == 4) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            reinterpret_cast<uint4 *>(dst)[i] =
-                make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
-                           __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3]));
+            st[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                               __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3]));
     } else {
+        // v_cvt_pk_bf16_f32: round to nearest even, the rounding of f32_to_bf16
+        // for every finite value (the values here are finite)
+        typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+        typedef float f32x2_v __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t p[4];
+            uint32_t pk[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                p[j] = f32_to_bf16(v[8 * i + 2 * j]) | (f32_to_bf16(v[8 * i + 2 * j + 1]) << 16);
-            reinterpret_cast<uint4 *>(dst)[i] = make_uint4(p[0], p[1], p[2], p[3]);
+            for (int j = 0; j < 4; ++j) {
+                const f32x2_v f = {v[8 * i + 2 * j], v[8 * i + 2 * j + 1]};
+                pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+            }
+            st[i] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
+    }
+    __builtin_amdgcn_wave_barrier();   // the wave's LDS writes before its reads (one wave, no workgroup barrier)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint4 *dst = reinterpret_cast<uint4 *>(out + c0 * kLaneChunk);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+        const int q = i * 64 + lane;          // piece q of the run: chunk q / kPieces, piece q % kPieces
+        const int ch = q / kPieces, pc = q % kPieces;
+        if (c0 + ch < chunks) dst[q] = stage[wave][ch * kStride + pc];
     }
 }
 

@@ -76,6 +76,17 @@ def test_quantize_bit_exact(bits, gs, w_dtype):
 def test_dequantize_bit_exact(bits, gs, sb_dtype, out_dtype):
     n, k = 93, 5 * gs
     w, _, c, s, b = quantized_case(7 * bits + gs, n, k, gs, bits, sb_dtype)
+    # special groups: denormal and huge scales and biases, values that round
+    # to the largest finite bf16 and just past bf16's denormal range
+    s, b = s.copy(), b.copy()
+    specials = [(1e-39, -3e-39), (3e-40, 0.0), (1e37, -1e38), (2e36, 3.3e38 - 2e36 * ((1 << bits) - 1)),
+                (1.1754944e-38, -1.1754944e-38 * 7)]
+    for r, (sv, bv) in enumerate(specials):
+        if sb_dtype == "f32":
+            s[r, :], b[r, :] = np.float32(sv), np.float32(bv)
+        else:
+            s[r, :] = synthetic.to_bf16_bits(np.full(s.shape[1], sv, np.float32))
+            b[r, :] = synthetic.to_bf16_bits(np.full(b.shape[1], bv, np.float32))
     want = O.dequantize(c, s, b, gs, bits, out_dtype=np.float32 if out_dtype == "f32" else np.uint16)
     got = B.nq_dequantize(*gpu_quantized(c, s, b), gs, bits,
                           out_dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
