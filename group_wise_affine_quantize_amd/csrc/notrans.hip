@@ -72,6 +72,36 @@ __device__ __forceinline__ void load_run(const uint32_t *src, uint32_t *w)
     }
 }
 
+// The 32 codes of a lane's run as fp32 values.  4-bit words are split into
+// their even and odd nibbles (kept opaque to the compiler) so that each code
+// is one v_cvt_f32_ubyte; 8-bit codes are bytes already.  The values are the
+// codes exactly, whichever way they are converted.
+template <int BITS>
+__device__ __forceinline__ void codes_f32(const uint32_t *w, float *q)
+{
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t lo, hi;
+            asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w[u]));
+            asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w[u] >> 4));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                q[8 * u + 2 * b] = (float)((lo >> (8 * b)) & 0xffu);
+                q[8 * u + 2 * b + 1] = (float)((hi >> (8 * b)) & 0xffu);
+            }
+        }
+    } else if constexpr (BITS == 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) q[4 * u + b] = (float)((w[u] >> (8 * b)) & 0xffu);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLaneChunk; ++j) q[j] = (float)code_at<BITS>(w, j);
+    }
+}
+
 // Rows a wave loads before it computes any of them (its rows i, i + 4, ...).
 constexpr int kNtUnroll = 4;
 
@@ -118,12 +148,12 @@ __global__ void __launch_bounds__(64 * kNtWaves) qmm_nt_partial_kernel(NtParams<
                 xs[m] = xv[u][m] * s[u];
                 bsum[m] = fmaf(xv[u][m], b[u], bsum[m]);
             }
+            float qf[kLaneChunk];
+            codes_f32<BITS>(w[u], qf);
 #pragma unroll
-            for (int j = 0; j < kLaneChunk; ++j) {
-                const float qf = (float)code_at<BITS>(w[u], j);
+            for (int j = 0; j < kLaneChunk; ++j)
 #pragma unroll
-                for (int m = 0; m < MR; ++m) acc[m][j] = fmaf(xs[m], qf, acc[m][j]);
-            }
+                for (int m = 0; m < MR; ++m) acc[m][j] = fmaf(xs[m], qf[j], acc[m][j]);
         }
     }
 #pragma unroll
@@ -157,19 +187,20 @@ __global__ void __launch_bounds__(64 * kNtWaves) qmm_nt_partial_kernel(NtParams<
 
 // y[m0 + m, c] = the row ranges' partials, added in a fixed order: a
 // workgroup takes 64 outputs, and its thread q * 64 + t adds the ranges of
-// quarter q of output t in increasing order; the four quarter sums are then
-// added in quarter order.
+// part q (of kNtRedParts equal parts) of output t in increasing order; the
+// part sums are then added in part order.
 constexpr int kNtRedCols = 64;
+constexpr int kNtRedParts = 16;
 
 template <typename XT, int MR>
-__global__ void __launch_bounds__(256) qmm_nt_reduce_kernel(const float *part, XT *y, int64_t m0, int mrows,
-                                                            int64_t nc, int nsplit)
+__global__ void __launch_bounds__(kNtRedCols * kNtRedParts)
+qmm_nt_reduce_kernel(const float *part, XT *y, int64_t m0, int mrows, int64_t nc, int nsplit)
 {
     const int t = threadIdx.x & (kNtRedCols - 1), qt = threadIdx.x / kNtRedCols;
     const int64_t idx = (int64_t)blockIdx.x * kNtRedCols + t;
     const bool ok = idx < (int64_t)mrows * nc;
     const int64_t m = ok ? idx / nc : 0, c = ok ? idx % nc : 0;
-    const int per = (nsplit + 3) / 4;
+    const int per = (nsplit + kNtRedParts - 1) / kNtRedParts;
     const int s0 = min(nsplit, qt * per), s1 = min(nsplit, s0 + per);
     float sum = 0.0f;
     int sp = s0;
@@ -181,10 +212,14 @@ __global__ void __launch_bounds__(256) qmm_nt_reduce_kernel(const float *part, X
         for (int u = 0; u < 8; ++u) sum += v[u];
     }
     for (; sp < s1; ++sp) sum += part[((int64_t)sp * MR + m) * nc + c];
-    __shared__ float qs[3][kNtRedCols];
+    __shared__ float qs[kNtRedParts - 1][kNtRedCols];
     if (qt > 0) qs[qt - 1][t] = sum;
     __syncthreads();
-    if (qt == 0 && ok) Elt<XT>::store(y, (m0 + m) * nc + c, ((sum + qs[0][t]) + qs[1][t]) + qs[2][t]);
+    if (qt == 0 && ok) {
+#pragma unroll
+        for (int q = 0; q < kNtRedParts - 1; ++q) sum += qs[q][t];
+        Elt<XT>::store(y, (m0 + m) * nc + c, sum);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -337,9 +372,11 @@ __device__ __forceinline__ float xor_sum(float v)
     return v + __int_as_float(r);
 }
 
-template <int BITS, typename XT, typename GT>
+template <int BITS, typename XT, typename GT, bool VEC>
 __global__ void __launch_bounds__(256) grad_sb_kernel(GradParams<XT, GT> p)
 {
+    // VEC: x and the codes are 16-byte aligned, so a lane's 32 activations
+    // and its run of codes are read with 16-byte loads (same values)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * kGradRows;
@@ -348,13 +385,20 @@ __global__ void __launch_bounds__(256) grad_sb_kernel(GradParams<XT, GT> p)
         const int64_t e0 = (int64_t)t * kStepElems + lane * kLaneChunk;
         const bool on = e0 < p.k;
         const int64_t ec = on ? e0 : 0;
-        uint32_t w[kGradRows][BITS];
+        // the codes of this step, as fp32 values, for all activation rows
+        float qf[kGradRows][kLaneChunk];
 #pragma unroll
         for (int r = 0; r < kGradRows; ++r) {
             const int64_t c = min(r0 + r, p.n - 1);
             const uint32_t *src = p.codes + c * p.words_per_row + (ec / kLaneChunk) * BITS;
+            uint32_t w[BITS];
+            if constexpr (VEC) {
+                load_run<BITS>(src, w);
+            } else {
 #pragma unroll
-            for (int u = 0; u < BITS; ++u) w[r][u] = src[u];
+                for (int u = 0; u < BITS; ++u) w[u] = src[u];
+            }
+            codes_f32<BITS>(w, qf[r]);
         }
         float as[kGradRows], ab[kGradRows];
 #pragma unroll
@@ -362,16 +406,19 @@ __global__ void __launch_bounds__(256) grad_sb_kernel(GradParams<XT, GT> p)
         for (int64_t m = 0; m < p.m; ++m) {
             float xf[kLaneChunk];
             float X = 0.0f;
+            if constexpr (VEC) {
+                load32_f32<XT>(p.x + m * p.k + ec, xf);
+            } else {
 #pragma unroll
-            for (int j = 0; j < kLaneChunk; ++j) {
-                xf[j] = Elt<XT>::load(p.x, m * p.k + ec + j);
-                X += xf[j];
+                for (int j = 0; j < kLaneChunk; ++j) xf[j] = Elt<XT>::load(p.x, m * p.k + ec + j);
             }
+#pragma unroll
+            for (int j = 0; j < kLaneChunk; ++j) X += xf[j];
 #pragma unroll
             for (int r = 0; r < kGradRows; ++r) {
                 float T = 0.0f;
 #pragma unroll
-                for (int j = 0; j < kLaneChunk; ++j) T = fmaf(xf[j], (float)code_at<BITS>(w[r], j), T);
+                for (int j = 0; j < kLaneChunk; ++j) T = fmaf(xf[j], qf[r][j], T);
                 const float d = Elt<XT>::load(p.dy, m * p.n + min(r0 + r, p.n - 1));
                 as[r] = fmaf(d, T, as[r]);
                 ab[r] = fmaf(d, X, ab[r]);
@@ -421,7 +468,8 @@ hipError_t qmm_nt_run(const NtLaunch &a, hipStream_t stream)
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         const int64_t outs = (int64_t)p.mrows * a.nc;
-        qmm_nt_reduce_kernel<XT, MR><<<dim3((unsigned)((outs + kNtRedCols - 1) / kNtRedCols)), dim3(256), 0, stream>>>(
+        qmm_nt_reduce_kernel<XT, MR><<<dim3((unsigned)((outs + kNtRedCols - 1) / kNtRedCols)),
+                                      dim3(kNtRedCols * kNtRedParts), 0, stream>>>(
             p.part, static_cast<XT *>(a.y), m0, p.mrows, a.nc, nsplit);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -493,7 +541,10 @@ hipError_t grad_run(const GradLaunch &a, hipStream_t stream)
     p.lg_gs = lg_of(a.gs);
     p.steps = (int)((a.k + kStepElems - 1) / kStepElems);
     const unsigned gx = (unsigned)((a.n + 4 * kGradRows - 1) / (4 * kGradRows));
-    grad_sb_kernel<BITS, XT, GT><<<dim3(gx), dim3(256), 0, stream>>>(p);
+    if ((((uintptr_t)a.x | (uintptr_t)a.codes) & 15) == 0)
+        grad_sb_kernel<BITS, XT, GT, true><<<dim3(gx), dim3(256), 0, stream>>>(p);
+    else
+        grad_sb_kernel<BITS, XT, GT, false><<<dim3(gx), dim3(256), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -573,6 +573,16 @@ def test_grad_scales_biases(m, n, k, gs, bits, x_dtype, g_dtype):
     assert_rows_close(values(host(db)), db_ref, tol, "dbiases")
     ds2, db2 = B.nq_qmm_grad_scales_biases(dev(x), dev(dy), dev(c), gs, bits, out_dtype=od)
     assert bits_equal(ds, ds2) and bits_equal(db, db2)
+    # x and codes only element-aligned (one element past a 16-byte boundary):
+    # scalar loads instead of 16-byte ones, the same bits
+    def offset_copy(t):
+        flat = torch.zeros(t.numel() + 16, dtype=t.dtype, device=t.device)
+        v = flat[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 != 0
+        return v
+    ds3, db3 = B.nq_qmm_grad_scales_biases(offset_copy(dev(x)), dev(dy), offset_copy(dev(c)), gs, bits, out_dtype=od)
+    assert bits_equal(ds, ds3) and bits_equal(db, db3)
 
 
 def test_grad_scales_biases_no_rows():
