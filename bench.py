@@ -374,23 +374,31 @@ def main():
 
     # ---------------------------------------------------------------- measured ceilings
     # Context only (no product code): what this GPU's library paths reach on
-    # the same data sizes -- a 1 GiB device copy (HBM read + write) and a
-    # dense bf16 matmul (hipBLASLt through torch) of the prefill shape with
-    # the weights already dequantized.
+    # the same data sizes -- a 1 GiB device copy (HBM read + write), a read
+    # of 1 GiB (torch's max over int64 elements: one read stream, a few
+    # bytes written) and a dense bf16 matmul (hipBLASLt through torch) of the
+    # prefill shape with the weights already dequantized.
     if not args.no_rows:
         log("timing the context ceilings")
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         t = timer.run(lambda i: dst.copy_(src), 20, 3, chunk=10)
         copy_gbs = 2 * src.numel() / (t / 20) / 1e9
-        del src, dst
+        del dst
+        # eager launches: a multi-block reduction records memsets, kept out of
+        # graphs; max over int64 is the fastest of torch's reductions here
+        src64 = src.view(torch.int64)
+        t = Timer(torch, eager=True).run(lambda i: src64.max(), 20, 3, chunk=10)
+        read_gbs = src.numel() / (t / 20) / 1e9
+        del src, src64
         w_hat = B.nq_dequantize(*q2, 64, 4)
         yd = torch.empty((2048, 14336), dtype=torch.bfloat16, device="cuda")
         t = timer.run(lambda i: torch.matmul(x4, w_hat.t(), out=yd), 20, 3, chunk=10)
         out["context"] = {
             "hbm_copy_1GiB_GBs": round(copy_gbs, 1),
+            "hbm_read_1GiB_GBs": round(read_gbs, 1),
             "dense_bf16_matmul_prefill_shape_TFLOPs": round(flops / (t / 20) / 1e12, 1),
-            "note": "torch copy_ and torch.matmul (hipBLASLt) on the same GPU; not the product path",
+            "note": "torch copy_, max and matmul (hipBLASLt) on the same GPU; not the product path",
         }
         del w_hat, yd
 
