@@ -23,12 +23,37 @@ def test_graph_replays_match_eager():
     cg, sg, bg = (dev(a) for a in O.quantize(wg, gs, bits))
     xgs = dev(xg)
 
+    # a long decode (the streaming kernel), a grouped gather with left
+    # indices, the product with the weights as stored and the derivatives
+    wl, xl = synthetic.random_case(13, (8192, 2048), (2, 2048), 0.02, "bf16")
+    cl, sl, bl = (dev(a) for a in O.quantize(wl, gs, bits))
+    xls = dev(xl)
+    we, xe = synthetic.random_case(14, (3, 128, 1024), (64, 1, 1024), 0.02, "bf16")
+    ce, se, be = (dev(a) for a in O.quantize(we, gs, bits))
+    xes = dev(xe)
+    rng = np.random.default_rng(5)
+    ide = dev(rng.integers(0, 3, size=80, dtype=np.uint32))
+    lhe = dev(rng.integers(0, 64, size=80, dtype=np.uint32))
+    ws_g = torch.empty(B.nq_gather_qmm_workspace_bytes(80, 1, 1024, 3, 128, gs, bits, torch.bfloat16,
+                                                       torch.bfloat16), dtype=torch.uint8, device="cuda")
+    ws_nt = torch.empty(max(1, B.nq_qmm_notrans_workspace_bytes(1, 512, 2048 * 3, gs, bits, torch.bfloat16)),
+                        dtype=torch.uint8, device="cuda")
+    dy = xs[:1, :512].contiguous()
+    dy3 = xs[:3, :512].contiguous()
+
     outs = {
         "decode": torch.empty((1, 512), dtype=torch.bfloat16, device="cuda"),
         "few": torch.empty((5, 512), dtype=torch.bfloat16, device="cuda"),
         "exact": torch.empty((20, 512), dtype=torch.bfloat16, device="cuda"),
         "tiled": torch.empty((20, 512), dtype=torch.bfloat16, device="cuda"),
         "gather": torch.empty((4, 1, 256), dtype=torch.bfloat16, device="cuda"),
+        "stream": torch.empty((1, 8192), dtype=torch.bfloat16, device="cuda"),
+        "batched": torch.empty((2, 10, 512), dtype=torch.bfloat16, device="cuda"),
+        "gather_lhs": torch.empty((80, 1, 128), dtype=torch.bfloat16, device="cuda"),
+        "notrans": torch.empty((1, 2048 * 3), dtype=torch.bfloat16, device="cuda"),
+        "dscales": torch.empty((512, 2048 * 3 // gs), dtype=torch.float32, device="cuda"),
+        "dbiases": torch.empty((512, 2048 * 3 // gs), dtype=torch.float32, device="cuda"),
+        "dequant": torch.empty((512, 2048 * 3), dtype=torch.bfloat16, device="cuda"),
     }
 
     def launch():
@@ -37,6 +62,12 @@ def test_graph_replays_match_eager():
         B.nq_qmm_row_exact(xs, c, s, b, gs, bits, y=outs["exact"])
         B.nq_qmm(xs, c, s, b, gs, bits, y=outs["tiled"])
         B.nq_gather_qmm(xgs, cg, sg, bg, gs, bits, ids, y=outs["gather"])
+        B.nq_qmm(xls[:1], cl, sl, bl, gs, bits, y=outs["stream"])
+        B.nq_qmm_batched(xs.view(2, 10, -1), c, s, b, gs, bits, y=outs["batched"])
+        B.nq_gather_qmm_lhs(xes, ce, se, be, gs, bits, lhe, ide, y=outs["gather_lhs"], workspace=ws_g)
+        B.nq_qmm_notrans(dy, c, s, b, gs, bits, y=outs["notrans"], workspace=ws_nt)
+        B.nq_qmm_grad_scales_biases(xs[:3], dy3, c, gs, bits, dscales=outs["dscales"], dbiases=outs["dbiases"])
+        B.nq_dequantize(c, s, b, gs, bits, out=outs["dequant"])
 
     launch()
     torch.cuda.synchronize()
