@@ -8,6 +8,8 @@ CPU oracle on the same seeded inputs.
   splitk              W [1024,14336] 4-bit g64, x bf16 [4,14336]
   prefill             W as decode_gemv, x bf16 [2048,4096] (sampled outputs)
   moe_gather          W [32,1408,2048] 4-bit g64, x bf16 [512,1,2048], ids in [0,32)
+and the derivative rows of the benchmark at the decode weights (dx for 1 and
+2048 rows, the scale and bias derivatives for 1 row).
 """
 import numpy as np
 import pytest
@@ -145,3 +147,30 @@ def test_moe_gather():
     torch.cuda.synchronize()
     for r in range(512):
         assert bits_equal(outs[r], y[r]), r
+
+
+def test_derivatives_at_the_decode_weights():
+    """The derivative rows of the benchmark at full size ("Training through
+    quantized weights"): dx = dy times the decode weights as stored, for one
+    row (partial sums and their ordered reduction) and for 2048 rows (tiles,
+    sampled rows), and the scale and bias derivatives for one row."""
+    d = workload("decode_gemv")
+    wl = d["wl"]
+    cr, sr, br = d["q"]
+    c, s, b = dev(cr), dev(sr), dev(br)
+    gs, bits = wl.group_size, wl.bits
+    dy1 = synthetic.random_case(5, (1, 1), (1, 14336), 1.0, "f32", "bf16")[1]
+    dx = B.nq_qmm_notrans(dev(dy1), c, s, b, gs, bits)
+    assert dx.shape == (1, 4096) and dx.dtype == torch.bfloat16
+    assert_rows_close(values(host(dx)), O.qmm_nt_f64(dy1, cr, sr, br, gs, bits), 1e-2, "dx decode")
+    assert bits_equal(dx, B.nq_qmm_notrans_row_exact(dev(dy1), c, s, b, gs, bits))
+    ds, db = B.nq_qmm_grad_scales_biases(dev(d["x"]), dev(dy1), c, gs, bits, out_dtype=torch.float32)
+    ds_ref, db_ref = O.qmm_grad_sb_f64(d["x"], dy1, cr, gs, bits)
+    assert ds.shape == (14336, 64)
+    assert_rows_close(values(host(ds)), ds_ref, 1e-3, "dscales")
+    assert_rows_close(values(host(db)), db_ref, 1e-3, "dbiases")
+    dyp = synthetic.random_case(6, (1, 1), (2048, 14336), 1.0, "f32", "bf16")[1]
+    dxp = values(host(B.nq_qmm_notrans(dev(dyp), c, s, b, gs, bits)))
+    assert dxp.shape == (2048, 4096) and np.all(np.isfinite(dxp))
+    rows = np.array([0, 127, 128, 1023, 2047])
+    assert_rows_close(dxp[rows], O.qmm_nt_f64(dyp[rows], cr, sr, br, gs, bits), 1e-2, "dx prefill rows")
