@@ -224,11 +224,13 @@ qmm_nt_reduce_kernel(const float *part, XT *y, int64_t m0, int mrows, int64_t nc
 
 // ---------------------------------------------------------------------------
 // Many rows (bf16 x): 128 x 128 tiles of y with bf16 MFMA, as the tiled
-// product with the transposed weights, but the weight tile of a K step (32
+// product with the transposed weights, but the weight tile of a K step (64
 // rows i of 128 columns c) is dequantized from the rows as stored and written
 // to LDS transposed, [c][i], so that the B operands read 8 consecutive i of
-// one column.  Each thread dequantizes 16 columns of one row (a bit-offset run
-// of codes, realigned) into round_bf16(fmaf(s, q, b)).
+// one column.  Each thread dequantizes 32 columns of one row (a run of
+// codes that starts on a word) into round_bf16(fmaf(s, q, b)).  The next K step's
+// loads are issued before this step's MFMAs, so they are in flight while the
+// matrix cores run.
 
 template <typename ST>
 struct NtTiledParams {
@@ -241,13 +243,20 @@ struct NtTiledParams {
     int lg_gs;
 };
 
-constexpr int kNtTM = 128, kNtTN = 128, kNtBK = 32, kNtLd = kNtBK + 8;
+constexpr int kNtTM = 128, kNtTN = 128, kNtBK = 64, kNtLd = kNtBK + 8;
+// Column c of the transposed weight tile starts at c * kNtLd + 16 * ((c / 32) % 4)
+// elements: with the plain stride, the 2-byte writes of a wave (16 rows x 4
+// groups of 32 columns) all fall in the same few LDS banks; the shift spreads
+// the groups over distinct banks, and the 16 columns one B-operand read
+// touches share a shift, so the reads stay conflict-free.
+__device__ __forceinline__ int nt_wcol(int c) { return c * kNtLd + 16 * ((c >> 5) & 3); }
+constexpr int kNtWsElems = kNtTN * kNtLd + 64;
 
 template <int BITS, typename ST>
 __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
 {
     __shared__ __attribute__((aligned(16))) bf16_bits xs[kNtTM * kNtLd];
-    __shared__ __attribute__((aligned(16))) bf16_bits ws[kNtTN * kNtLd];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[kNtWsElems];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -259,53 +268,57 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-    const int lrow = tid >> 1, lhalf = tid & 1;          // x loader: one row, 16 elements
+    const int lrow = tid >> 1, lhalf = tid & 1;          // x loader: one row, 32 elements
     const int64_t xm = m0 + lrow;
-    const int wrow = tid >> 3, wcol = 16 * (tid & 7);    // weight loader: one row, 16 columns
+    const int wrow = tid >> 2, wcol = 32 * (tid & 3);    // weight loader: one row, 32 columns
     const int64_t cb = c0 + wcol;
-    const bool wv_ok = cb < p.nc;                         // nc % 32 == 0: then cb + 16 <= nc
+    const bool wv_ok = cb < p.nc;                         // nc % 32 == 0: then cb + 32 <= nc
     const int64_t g = (wv_ok ? cb : 0) >> p.lg_gs;
-    constexpr int NW = (BITS + 1) / 2;
+    constexpr int NW = BITS;   // 32 codes from a word boundary (32 columns x bits)
 
-    for (int64_t i0 = 0; i0 < p.ni; i0 += kNtBK) {       // ni is a multiple of 32
-        uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
-        if (xm < p.m) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(p.x + xm * p.ni + i0 + 16 * lhalf);
-            xa = src[0];
-            xb = src[1];
-        }
-        uint32_t outw[8];
-        if (wv_ok) {
-            const int64_t i = i0 + wrow;
-            const float s = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
-            const float b = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
-            const int64_t bit0 = cb * BITS;
-            const uint32_t *src = p.codes + i * p.words_per_row + (bit0 >> 5);
-            const uint32_t sh = (uint32_t)(bit0 & 31);
-            uint32_t raw[NW], cw[NW];
+    struct Ld {
+        uint4 x[4];
+        uint32_t raw[NW];
+        float s, b;
+    };
+    const int64_t xmc = min(xm, p.m - 1);   // rows past m read row m - 1 (not stored)
+    const int64_t cbc = wv_ok ? cb : 0;     // columns past nc read column 0 (dropped)
+    auto load = [&](int64_t i0, Ld &l) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.x + xmc * p.ni + i0 + 32 * lhalf);
 #pragma unroll
-            for (int u = 0; u < NW; ++u) raw[u] = src[u];
+        for (int u = 0; u < 4; ++u) l.x[u] = src[u];
+        const int64_t i = i0 + wrow;
+        l.s = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
+        l.b = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
+        load_run<BITS>(p.codes + i * p.words_per_row + ((cbc * BITS) >> 5), l.raw);
+    };
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    typedef float f32x2_v __attribute__((ext_vector_type(2)));
+    Ld cur, nxt;
+    if (p.ni > 0) load(0, cur);
+    for (int64_t i0 = 0; i0 < p.ni; i0 += kNtBK) {       // ni is a multiple of 64
+        uint32_t outw[16];
+        {
+            float qf[kLaneChunk];
+            codes_f32<BITS>(cur.raw, qf);
 #pragma unroll
-            for (int u = 0; u < NW; ++u) cw[u] = __builtin_amdgcn_alignbit(u + 1 < NW ? raw[u + 1] : 0u, raw[u], sh);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float v0 = fmaf(s, (float)code_at<BITS>(cw, 2 * u), b);
-                const float v1 = fmaf(s, (float)code_at<BITS>(cw, 2 * u + 1), b);
-                outw[u] = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+            for (int u = 0; u < 16; ++u) {
+                // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16 for finite values
+                const f32x2_v f = {wv_ok ? fmaf(cur.s, qf[2 * u], cur.b) : 0.0f,
+                                   wv_ok ? fmaf(cur.s, qf[2 * u + 1], cur.b) : 0.0f};
+                outw[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) outw[u] = 0u;
         }
         __syncthreads();   // the previous step's MFMA reads are done
-        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * kNtLd + 16 * lhalf);
-        xd[0] = xa;
-        xd[1] = xb;
+        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * kNtLd + 32 * lhalf);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            ws[(wcol + 2 * u) * kNtLd + wrow] = (bf16_bits)(outw[u] & 0xffffu);
-            ws[(wcol + 2 * u + 1) * kNtLd + wrow] = (bf16_bits)(outw[u] >> 16);
+        for (int u = 0; u < 4; ++u) xd[u] = xm < p.m ? cur.x[u] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            ws[nt_wcol(wcol + 2 * u) + wrow] = (bf16_bits)(outw[u] & 0xffffu);
+            ws[nt_wcol(wcol + 2 * u + 1) + wrow] = (bf16_bits)(outw[u] >> 16);
         }
+        if (i0 + kNtBK < p.ni) load(i0 + kNtBK, nxt);   // in flight during this step's MFMAs
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < kNtBK / 16; ++ks) {
@@ -316,13 +329,14 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
                 a[i] = *reinterpret_cast<const bf16x8_t *>(xs + (wm * 64 + i * 32 + (lane & 31)) * kNtLd + kk);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bo[j] = *reinterpret_cast<const bf16x8_t *>(ws + (wn * 64 + j * 32 + (lane & 31)) * kNtLd + kk);
+                bo[j] = *reinterpret_cast<const bf16x8_t *>(ws + nt_wcol(wn * 64 + j * 32 + (lane & 31)) + kk);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bo[j], acc[i][j], 0, 0, 0);
         }
+        cur = nxt;
     }
     // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
 #pragma unroll

@@ -251,12 +251,12 @@ nq_status qmm_common(const char *op, int row_exact, const nq_plan *forced, const
 // ---- product with the weights as stored, derivatives
 
 // Route of the product with the weights as stored: 128 x 128 MFMA tiles for
-// many bf16 rows (the ranges of i a multiple of 32), else the matrix-vector
+// many bf16 rows (the ranges of i a multiple of 64), else the matrix-vector
 // pair, which keeps every row bit-equal to its one-row product.  A pure
 // function of the sizes, dtypes and mode.
 bool nt_tiled(int64_t m, int64_t ni, int x_dt, int row_exact)
 {
-    return !row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && ni % 32 == 0;
+    return !row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && ni % 64 == 0;
 }
 
 nq_status qmm_nt_impl(const char *op, int row_exact, const void *x, nq_dtype x_dt, int64_t m,

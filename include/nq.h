@@ -187,7 +187,7 @@ nq_status nq_qmm_batched(const void *x, nq_dtype x_dt, int64_t batch, int64_t l,
 
 /* Workspace bytes nq_qmm_notrans / nq_qmm_notrans_row_exact need: 0 on the
  * tiled route (row_exact = 0, m > NQ_ROW_INDEPENDENT_ROWS, bf16 x, ni a
- * multiple of 32), else room for the partial sums of the matrix's row ranges
+ * multiple of 64), else room for the partial sums of the matrix's row ranges
  * (a function of ni and nc only), fully rewritten by every call. */
 size_t nq_qmm_notrans_workspace_bytes(int64_t m, int64_t ni, int64_t nc, int32_t group_size,
                                       int32_t bits, nq_dtype x_dt, int32_t row_exact);

@@ -354,7 +354,8 @@ def test_notrans_argument_errors(lib, entry):
     assert need > 0 and need == lib.nq_qmm_notrans_workspace_bytes(1, 128, 256, 64, 4, BF16, 0)
     assert lib.nq_qmm_notrans_workspace_bytes(64, 128, 256, 64, 4, BF16, 0) == 0      # tiled
     assert lib.nq_qmm_notrans_workspace_bytes(64, 128, 256, 64, 4, BF16, 1) == need   # row-exact
-    assert lib.nq_qmm_notrans_workspace_bytes(64, 100, 256, 64, 4, BF16, 0) > 0       # ni % 32
+    assert lib.nq_qmm_notrans_workspace_bytes(64, 100, 256, 64, 4, BF16, 0) > 0       # ni % 64
+    assert lib.nq_qmm_notrans_workspace_bytes(64, 96, 256, 64, 4, BF16, 0) > 0        # ni % 64
     cases = [
         (dict(x_dt=7), NQ_ERR_DTYPE, "dtype"),
         (dict(bits=7), NQ_ERR_QUANT, "bits=7"),

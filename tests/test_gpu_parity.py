@@ -516,7 +516,9 @@ def test_other_widths_gather(bits, rows):
     (1, 700, 4096, 64, 4, "bf16", "bf16"),     # decode-sized activation derivative
     (2, 333, 192, 32, 3, "f32", "f32"),        # ragged row ranges, straddling codes
     (5, 1024, 2560, 128, 8, "bf16", "f32"),    # three row chunks, two column blocks
-    (40, 100, 256, 64, 4, "bf16", "bf16"),     # many rows, ni not a multiple of 32
+    (40, 100, 256, 64, 4, "bf16", "bf16"),     # many rows, ni not a multiple of 64
+    (30, 96, 256, 64, 4, "bf16", "bf16"),      # many rows, ni a multiple of 32 only
+    (30, 192, 320, 64, 6, "bf16", "bf16"),     # tiles, three K steps, ragged m and nc
     (200, 512, 384, 64, 4, "bf16", "bf16"),    # 128-row tiles
     (150, 320, 4160, 64, 5, "bf16", "bf16"),   # tiles, odd width, ragged m and nc
 ])
@@ -532,13 +534,25 @@ def test_qmm_notrans(m, ni, nc, gs, bits, x_dtype, w_dtype):
     assert_rows_close(values(host(y)), y_ref, tolerance(y.dtype), "notrans")
     yr = B.nq_qmm_notrans_row_exact(xs, *q, gs, bits)
     assert_rows_close(values(host(yr)), y_ref, tolerance(yr.dtype), "notrans row-exact")
-    tiled = m > 8 and x_dtype == "bf16" and ni % 32 == 0
+    tiled = m > 8 and x_dtype == "bf16" and ni % 64 == 0
     for r in range(0, m, max(1, m // 5)):
         y1 = B.nq_qmm_notrans(xs[r:r + 1].clone(), *q, gs, bits)   # a fresh, aligned row
         assert bits_equal(y1, yr[r:r + 1]), r
         if not tiled:
             assert bits_equal(y1, y[r:r + 1]), r
     assert bits_equal(y, B.nq_qmm_notrans(xs, *q, gs, bits))   # run to run
+
+
+@pytest.mark.parametrize("m", [1, 20])
+def test_qmm_notrans_empty_inner_dimension(m):
+    """ni == 0: an empty sum, all-zero rows, on the matrix-vector route (one
+    row) and on the tiles (20 bf16 rows)."""
+    x = torch.empty((m, 0), dtype=torch.bfloat16, device="cuda")
+    codes = torch.empty((0, 256 * 4 // 32), dtype=torch.int32, device="cuda")
+    sc = torch.empty((0, 4), dtype=torch.bfloat16, device="cuda")
+    y = B.nq_qmm_notrans(x, codes, sc, sc.clone(), 64, 4)
+    assert y.shape == (m, 256)
+    assert torch.count_nonzero(y.float()).item() == 0
 
 
 def test_activation_derivative_is_notrans_of_forward_weights():
