@@ -4,7 +4,8 @@ Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The GPU library does not depend on it in any way.
 
 Thin numpy wrappers around nq_oracle.c (see that file for the readings of the
-"Quantization" page of the nuvec documentation that it follows).  bf16 arrays
+"Quantization" page of the nuvec documentation that it follows).  The
+floating-point modes (MXFP4, MXFP8, NVFP4) are in the numpy module fp.py.  bf16 arrays
 are passed as numpy uint16 bit patterns.
 """
 import ctypes
