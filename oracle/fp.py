@@ -39,7 +39,8 @@ Every rounding decision is taken on fp32 numbers, as the GPU takes it.
 Dequantize and the products are exact definitions: w_hat = g * S * E with
 S the decoded scale, E the decoded element and g the global scale (1 when
 absent); dequantize rounds w_hat (exact in fp64) to bfloat16 (round to
-nearest even; NaN comes out as the canonical quiet NaN 0x7fc0) or to fp32;
+nearest even) or to fp32, and a NaN comes out as the canonical quiet NaN of
+the output type (0x7fc0, 0x7fc00000) whatever the sign of the NaN element;
 products are y = x . w_hat^T accumulated in fp64.
 """
 import numpy as np
@@ -210,7 +211,8 @@ def dequantize(codes, scales, mode, k, out_dtype="bf16"):
     if out_dtype == "bf16":
         return _round_bf16(w)
     with np.errstate(over="ignore"):
-        return w.astype(np.float32)
+        f = w.astype(np.float32)
+    return np.where(np.isnan(f), np.uint32(0x7FC00000).view(np.float32), f)
 
 
 def qmm_f64(x, codes, scales, mode, global_scale=None):

@@ -268,3 +268,16 @@ def test_gather_rows_pick_their_expert():
         else:
             want = F.qmm_f64(x[r], cq[idx[r]], sq[idx[r]], "nvfp4") * float(gsc[idx[r]])
             assert np.allclose(y[r], want, rtol=1e-14, atol=0)
+
+
+def test_dequantize_nan_is_canonical_in_both_outputs():
+    # a negative NaN element (E4M3 0xff) and a NaN scale give the quiet NaN
+    # of the output type, sign cleared
+    cq = F.pack(np.array([[0xFF] + [0xB8] * 31]), 8)
+    for s in (127, 255):
+        f = F.dequantize(cq, np.array([[s]], np.uint8), "mxfp8", 32, "f32").view(np.uint32)
+        assert f[0, 0] == 0x7FC00000
+        b = F.dequantize(cq, np.array([[s]], np.uint8), "mxfp8", 32, "bf16")
+        assert b[0, 0] == 0x7FC0
+    f = F.dequantize(cq, np.array([[127]], np.uint8), "mxfp8", 32, "f32")
+    assert f[0, 1] == -1.0
