@@ -370,6 +370,48 @@ def main():
         t = timer.run(lambda i: B.nq_qmm(xs, *q, 64, 4, y=y1), steps, 10)
         put("affine_f32_256x512", t, steps, nbytes(*q), "GB/s",
             {"workload": "x f32 [4,512] . W[256,512]^T 4-bit g64 f32 scales (launch-bound)"})
+
+        # floating-point modes (uniformly random codes; moderate scale codes)
+        fp_scales = {"mxfp4": (120, 134), "mxfp8": (120, 134), "nvfp4": (0x20, 0x50)}
+
+        def fp_weights(mode, lead, k, seed):
+            _, bits, gs = B.FP_MODES[mode]
+            wds, scs = synthetic.random_fp_matrix(seed, lead, k, bits, gs, fp_scales[mode],
+                                                  finite_bytes=True)
+            return dev(wds), torch.from_numpy(scs).cuda()
+
+        qf = tuple(torch.empty_like(t) for t in B.nq_fp_quantize(w2, "mxfp4"))
+        w_copies = [w2] + [w2.clone() for _ in range(math.ceil(ROTATE_BYTES / nbytes(w2)) - 1)]
+        t = timer.run(lambda i: B.nq_fp_quantize(w_copies[i % len(w_copies)], "mxfp4", *qf), steps, 10)
+        put("fp_quantize_mxfp4", t, steps, nbytes(w2) + nbytes(*qf), "GB/s",
+            {"workload": "W bf16 [14336,4096] -> MXFP4 codes and E8M0 scales"})
+        del w_copies
+        for mode in ("mxfp4", "mxfp8", "nvfp4"):
+            qm = fp_weights(mode, (14336,), 4096, 31)
+            cps = rotated(qm)
+            t = timer.run(lambda i: B.nq_fp_qmm(x2, *cps[i % len(cps)], mode, y=y2), steps, 10)
+            put(f"fp_decode_{mode}", t, steps, nbytes(*qm), "GB/s",
+                {"workload": f"x bf16 [1,4096] . W[14336,4096]^T {mode}"})
+            if mode == "mxfp4":
+                t = timer.run(lambda i: B.nq_fp_dequantize(*cps[i % len(cps)], mode, out=wout), steps, 10)
+                put("fp_dequantize_mxfp4", t, steps, nbytes(wout) + nbytes(*qm), "GB/s",
+                    {"workload": "MXFP4 [14336,4096] -> bf16"})
+                yp = torch.empty((2048, 14336), dtype=torch.bfloat16, device="cuda")
+                tp = timer.run(lambda i: B.nq_fp_qmm(x4, *qm, mode, y=yp), max(2, steps // 20), 2)
+                put("fp_prefill_mxfp4", tp, max(2, steps // 20), 2 * 2048 * 14336 * 4096, "TFLOP/s",
+                    {"workload": "x bf16 [2048,4096] . W[14336,4096]^T mxfp4 (128x128 tiles)"})
+                del yp
+            del cps, qm
+        del wout
+        cg, sg = fp_weights("nvfp4", (32, 1408), 2048, 32)
+        gsc = torch.rand(32, dtype=torch.float32, device="cuda") + 0.5
+        xg = dev(synthetic.generate("moe_gather")["x"])
+        idg = dev(synthetic.generate("moe_gather")["ids"])
+        t = timer.run(lambda i: B.nq_fp_gather_qmm(xg, cg, sg, "nvfp4", idg, global_scales=gsc, y=yg),
+                      steps, 10)
+        put("fp_gather_nvfp4", t, steps, nbytes(cg, sg), "GB/s",
+            {"workload": "x bf16 [512,1,2048], 32 NVFP4 experts W[1408,2048] with global scales, "
+                         "one matrix-vector product per row"})
     out["rows"] = rows
 
     # ---------------------------------------------------------------- measured ceilings

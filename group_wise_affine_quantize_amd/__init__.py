@@ -12,6 +12,10 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     nq_dequantize,
+    nq_fp_dequantize,
+    nq_fp_gather_qmm,
+    nq_fp_qmm,
+    nq_fp_quantize,
     nq_gather_qmm,
     nq_gather_qmm_row_exact,
     nq_gather_qmm_lhs,

@@ -15,6 +15,9 @@ _LIB_NAME = "libnq.so"
 NQ_ROW_INDEPENDENT_ROWS = 8
 NQ_F32, NQ_BF16 = 0, 1
 NQ_ROUTE_GEMV, NQ_ROUTE_TILED = 1, 2
+NQ_MXFP4, NQ_MXFP8, NQ_NVFP4 = 1, 2, 3
+# floating-point mode -> (C enum, bits per code, group size)
+FP_MODES = {"mxfp4": (NQ_MXFP4, 4, 32), "mxfp8": (NQ_MXFP8, 8, 32), "nvfp4": (NQ_NVFP4, 4, 16)}
 
 _lib = None
 
@@ -69,6 +72,10 @@ _SIGNATURES = {
     "nq_qmm_notrans_row_exact": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P,
                                  _SZ, _P],
     "nq_qmm_grad_scales_biases": [_P, _P, _I32, _I64, _I64, _P, _I64, _I32, _I32, _P, _P, _I32, _P],
+    "nq_fp_quantize": [_P, _I32, _I64, _I64, _I32, _P, _P, _P],
+    "nq_fp_dequantize": [_P, _P, _I64, _I64, _I32, _P, _I32, _P],
+    "nq_fp_qmm": [_P, _I32, _I64, _I64, _P, _P, _P, _I64, _I32, _I32, _P, _P],
+    "nq_fp_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _P],
     "nq_status_string": [_I32],
     "nq_last_error": [],
     "nq_version": [],
@@ -411,4 +418,87 @@ def nq_gather_qmm_lhs(x, codes, scales, biases, group_size, bits, lhs_idx, rhs_i
                                  _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(lhs_idx),
                                  _ptr(rhs_idx), int(bool(sorted_hint)), int(bool(row_exact)),
                                  _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+# ---------------------------------------------------------------- floating-point modes
+def _fp(mode):
+    if mode not in FP_MODES:
+        raise ValueError(f"unknown floating-point mode {mode!r} (one of {sorted(FP_MODES)})")
+    return FP_MODES[mode]
+
+
+def nq_fp_quantize(w, mode, codes=None, scales=None, stream=None):
+    """w [..., k] (f32 or bf16) -> (codes uint32-as-int32 [..., k*bits/32],
+    scales uint8 [..., k/group]) in mode "mxfp4", "mxfp8" or "nvfp4"."""
+    torch = _torch()
+    lib = load_library()
+    mid, bits, gs = _fp(mode)
+    _contig("w", w)
+    k = w.shape[-1]
+    n = w.numel() // k if k else 0
+    lead = tuple(w.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (words_per_row(k, bits),), dtype=torch.int32, device=w.device)
+    if scales is None:
+        scales = torch.empty(lead + (k // gs,), dtype=torch.uint8, device=w.device)
+    _check(lib.nq_fp_quantize(_ptr(w), _dt(w), n, k, mid, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def nq_fp_dequantize(codes, scales, mode, out_dtype=None, out=None, stream=None):
+    """-> w_hat [..., k] in out_dtype (default bf16)."""
+    torch = _torch()
+    lib = load_library()
+    mid, bits, gs = _fp(mode)
+    for name, t in (("codes", codes), ("scales", scales)):
+        _contig(name, t)
+    k = scales.shape[-1] * gs
+    n = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
+    if out is None:
+        out = torch.empty(tuple(scales.shape[:-1]) + (k,), dtype=out_dtype or torch.bfloat16,
+                          device=scales.device)
+    _check(lib.nq_fp_dequantize(_ptr(codes), _ptr(scales), n, k, mid, _ptr(out), _dt(out),
+                                _stream(stream)))
+    return out
+
+
+def nq_fp_qmm(x, codes, scales, mode, global_scale=None, row_exact=False, y=None, stream=None):
+    """y [m, n] = x [m, k] times the transposed weights (times the fp32 global
+    scale, a one-element GPU tensor, NVFP4 only), in x's dtype."""
+    torch = _torch()
+    lib = load_library()
+    mid, bits, gs = _fp(mode)
+    for name, t in (("x", x), ("codes", codes), ("scales", scales)):
+        _contig(name, t)
+    m, k = x.shape
+    n = scales.shape[0]
+    if scales.shape[1] * gs != k or codes.shape != (n, words_per_row(k, bits)):
+        raise ValueError("codes/scales shapes do not match x and the mode")
+    if y is None:
+        y = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    _check(lib.nq_fp_qmm(_ptr(x), _dt(x), m, k, _ptr(codes), _ptr(scales), _ptr(global_scale), n, mid,
+                         int(bool(row_exact)), _ptr(y), _stream(stream)))
+    return y
+
+
+def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, y=None, stream=None):
+    """x [rows, l, k], stacked experts codes [e, n, words] and scales [e, n,
+    groups], rhs_idx [rows] (uint32 as int32), optional per-expert fp32 global
+    scales [e] (NVFP4) -> y [rows, l, n]."""
+    torch = _torch()
+    lib = load_library()
+    mid, bits, gs = _fp(mode)
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("rhs_idx", rhs_idx)):
+        _contig(name, t)
+    rows, l, k = x.shape
+    e, n = scales.shape[0], scales.shape[1]
+    if scales.shape[2] * gs != k or codes.shape != (e, n, words_per_row(k, bits)):
+        raise ValueError("codes/scales shapes do not match x and the mode")
+    if rhs_idx.numel() != rows:
+        raise ValueError("rhs_idx must hold one expert per row")
+    if y is None:
+        y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+    _check(lib.nq_fp_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
+                                _ptr(global_scales), e, n, mid, _ptr(rhs_idx), _ptr(y), _stream(stream)))
     return y

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["nq_api.hip", "quantize.hip", "gemv.hip", "tiled.hip", "notrans.hip"]
+SOURCES = ["nq_api.hip", "quantize.hip", "gemv.hip", "tiled.hip", "notrans.hip", "fp.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

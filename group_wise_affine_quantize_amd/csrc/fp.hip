@@ -1,0 +1,598 @@
+// Floating-point quantization modes on gfx950: MXFP4, MXFP8 and NVFP4.
+//
+// Method: "Quantization" page of the nuvec documentation, section
+// "Floating-point formats" (every weight a small float, one uint8 scale
+// code per group, no biases; dequantize gives bf16; a product comes out in
+// x's dtype) and section "Mixture of experts" (an NVFP4 expert may carry one
+// fp32 global scale).  The encodings are the public format definitions:
+// OCP Microscaling Formats v1.0 -- blocks of 32 elements sharing an E8M0
+// scale 2^(s - 127) (s = 255: NaN), elements FP4 E2M1 or FP8 E4M3 -- and
+// NVFP4 -- blocks of 16 E2M1 elements sharing an E4M3 scale.  Codes are
+// packed LSB-first into uint32 words like the affine codes.
+//
+// Every kernel takes 32-element chunks: one MX block, or two NVFP4 blocks.
+//   quantize    MX: s = clamp(biased exponent of max|w| - emax, 0, 254)
+//               (emax 2 for E2M1, 8 for E4M3; an all-zero block gets 0),
+//               element = round(ldexp(w, 127 - s)).  NVFP4: s =
+//               e4m3(fp32(max|w| / 6)), element = round(fp32(w / S)) with S
+//               the decoded scale (zero codes when S is 0).  round: nearest
+//               value, ties to the even code, saturating at the largest
+//               magnitude, sign kept.
+//   dequantize  S * E in fp32 (exact), rounded to bf16 (NaN -> 0x7fc0) or
+//               kept in fp32.
+//   products    the hardware conversions v_cvt_scalef32_pk_{bf16,f32}_{fp4,fp8}
+//               with scale 1 (exact) turn elements into bf16 or fp32 pairs;
+//               the matrix-vector kernel dots them with x per group and
+//               scales each group sum in fp32, the tiled kernel writes
+//               bf16(S * E) tiles to LDS for bf16 MFMA.  A global scale
+//               multiplies the fp32 result.
+#include <algorithm>
+#include <type_traits>
+
+#include "nq_device.h"
+#include "nq_internal.h"
+
+namespace nqk {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int MODE> struct Fp;
+template <> struct Fp<FP_MXFP4> {
+    static constexpr int bits = 4, gs = 32, emax = 2;
+    static constexpr bool fp8 = false, e8m0 = true;
+};
+template <> struct Fp<FP_MXFP8> {
+    static constexpr int bits = 8, gs = 32, emax = 8;
+    static constexpr bool fp8 = true, e8m0 = true;
+};
+template <> struct Fp<FP_NVFP4> {
+    static constexpr int bits = 4, gs = 16, emax = 2;
+    static constexpr bool fp8 = false, e8m0 = false;
+};
+
+constexpr uint32_t kQuietNan = 0x7fc00000u;
+
+// ---------------------------------------------------------------- decoding
+// E2M1: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0; exponent 0
+// is subnormal (m * 0.5).
+__device__ __forceinline__ float e2m1_value(uint32_t c)
+{
+    const uint32_t mag = c & 7u;
+    const uint32_t b = mag >= 2u ? (((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22)
+                                 : (mag ? 0x3f000000u : 0u);
+    return __uint_as_float(b | ((c & 8u) << 28));
+}
+
+// E4M3 (OCP): sign bit 7, exponent bits 6:3 (bias 7), mantissa bits 2:0;
+// exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    if ((c & 0x7fu) == 0x7fu) return __uint_as_float(kQuietNan);
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// E8M0: 2^(s - 127); s = 0 is the fp32 subnormal 2^-127; s = 255 is NaN.
+__device__ __forceinline__ float e8m0_value(uint32_t s)
+{
+    return __uint_as_float(s == 255u ? kQuietNan : s == 0u ? 0x00400000u : s << 23);
+}
+
+template <int MODE>
+__device__ __forceinline__ float scale_value(uint32_t s)
+{
+    return Fp<MODE>::e8m0 ? e8m0_value(s) : e4m3_value(s);
+}
+
+template <int MODE>
+__device__ __forceinline__ float elem_value(uint32_t c)
+{
+    return Fp<MODE>::fp8 ? e4m3_value(c) : e2m1_value(c);
+}
+
+// ---------------------------------------------------------------- encoding
+// Nearest E2M1 value, ties to the even code, saturating at 6: the code is
+// the number of decision points below |v| (strict where the tie goes down).
+__device__ __forceinline__ uint32_t e2m1_code(float v)
+{
+    const float a = fabsf(v);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Nearest E4M3 value, ties to the even code, saturating at 448.  Below 2^-6
+// the spacing is 2^-9 (codes 0..8); above, the fp32 mantissa is rounded to 3
+// bits (a carry moves into the exponent) and the exponent rebased.
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a < 0x1p-6f) {
+        c = (uint32_t)rintf(a * 512.0f);
+    } else {
+        uint32_t u = __float_as_uint(a);
+        u += 0x7ffffu + ((u >> 20) & 1u);
+        c = min((u >> 20) - (120u << 3), 0x7eu);
+    }
+    return c | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+template <int MODE>
+__device__ __forceinline__ uint32_t elem_code(float v)
+{
+    return Fp<MODE>::fp8 ? e4m3_code(v) : e2m1_code(v);
+}
+
+// ---------------------------------------------------------------- quantize
+template <int MODE, typename WT>
+__global__ void __launch_bounds__(256) fp_quantize_kernel(const WT *__restrict__ w, int64_t chunks,
+                                                          uint32_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    float v[32];
+    load32_f32<WT>(w + c * 32, v);
+    uint32_t q[32];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < GS; ++j) amax = fmaxf(amax, fabsf(v[g * GS + j]));
+        uint32_t s;
+        if constexpr (Fp<MODE>::e8m0) {
+            s = (uint32_t)min(max((int)(__float_as_uint(amax) >> 23) - Fp<MODE>::emax, 0), 254);
+            const int sh = 127 - (int)s;
+#pragma unroll
+            for (int j = 0; j < GS; ++j) q[g * GS + j] = elem_code<MODE>(ldexpf(v[g * GS + j], sh));
+        } else {
+            s = e4m3_code(amax / 6.0f);
+            const float S = e4m3_value(s);
+#pragma unroll
+            for (int j = 0; j < GS; ++j) q[g * GS + j] = S == 0.0f ? 0u : e2m1_code(v[g * GS + j] / S);
+        }
+        scales[c * NG + g] = (uint8_t)s;
+    }
+    uint32_t wd[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) wd[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) wd[j * BITS / 32] |= q[j] << ((j * BITS) % 32);
+    uint4 *dst = reinterpret_cast<uint4 *>(codes + c * BITS);
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) dst[i] = make_uint4(wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------- dequantize
+template <int MODE, typename OT>
+__global__ void __launch_bounds__(256) fp_dequantize_kernel(const uint32_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            int64_t chunks, OT *__restrict__ out)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    uint32_t wd[BITS];
+    const uint4 *src = reinterpret_cast<const uint4 *>(codes + c * BITS);
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) {
+        const uint4 t = src[i];
+        wd[4 * i] = t.x, wd[4 * i + 1] = t.y, wd[4 * i + 2] = t.z, wd[4 * i + 3] = t.w;
+    }
+    float S[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) S[g] = scale_value<MODE>(scales[c * NG + g]);
+    float o[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const uint32_t q = (wd[j * BITS / 32] >> ((j * BITS) % 32)) & ((1u << BITS) - 1u);
+        const float x = S[j / GS] * elem_value<MODE>(q);
+        o[j] = x != x ? __uint_as_float(kQuietNan) : x;
+    }
+    if constexpr (std::is_same<OT, float>::value) {
+        uint4 *dst = reinterpret_cast<uint4 *>(out + c * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dst[i] = make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
+                                __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3]));
+    } else {
+        uint32_t h[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) h[i] = f32_to_bf16(o[2 * i]) | (f32_to_bf16(o[2 * i + 1]) << 16);
+        uint4 *dst = reinterpret_cast<uint4 *>(out + c * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+    }
+}
+
+// ---------------------------------------------------------------- element pairs
+// Elements 2p and 2p + 1 of a chunk's code words as bf16 or fp32 pairs (the
+// scaled conversions with scale 1: exact for these formats).
+template <int MODE>
+__device__ __forceinline__ bf16x2_t pair_bf16(const uint32_t *wd, int p)
+{
+    if constexpr (Fp<MODE>::fp8) {
+        const uint32_t w = wd[p >> 1];
+        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    } else {
+        const uint32_t w = wd[p >> 2];
+        switch (p & 3) {   // the byte select is an immediate
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+        }
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ f32x2_t pair_f32(const uint32_t *wd, int p)
+{
+    if constexpr (Fp<MODE>::fp8) {
+        const uint32_t w = wd[p >> 1];
+        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    } else {
+        const uint32_t w = wd[p >> 2];
+        switch (p & 3) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- matrix-vector
+// A wave owns RW consecutive weight rows and MR activation vectors; lane L
+// takes the 32-element chunks L, L + 64, ... of K.  Per chunk and group it
+// forms the dot product of the group's elements with x (bf16 pairs through
+// v_dot2_f32_bf16, or fp32 fused multiply-adds, in element order), then adds
+// scale * sum to its running sum; the 64 lanes' sums are added by a xor
+// butterfly.  A vector's arithmetic is the same for any MR, RW or launch
+// chunk, so every row equals its one-row product bit for bit.
+struct FpGemvParams {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const uint8_t *scales;
+    const float *gscale;     // per expert (or the only matrix); null: 1
+    const uint32_t *idx;     // expert of each item; null: one weight matrix
+    int64_t vpi, cpi;        // vectors per item, MR-chunks per item
+    int64_t n, k, e;
+    int64_t y0;              // first (item, chunk) index of this launch
+};
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int MODE, typename XT, int MR, int RW>
+__global__ void __launch_bounds__(256) fp_gemv_kernel(FpGemvParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    constexpr bool kBf16 = std::is_same<XT, bf16_bits>::value;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t yb = p.y0 + blockIdx.y;
+    const int64_t item = yb / p.cpi;
+    const int64_t v0 = (yb % p.cpi) * MR;
+    const int mr = (int)min((int64_t)MR, p.vpi - v0);
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RW;
+    if (row0 >= p.n) return;
+    const uint32_t ex = p.idx ? p.idx[item] : 0u;
+    XT *y = reinterpret_cast<XT *>(p.y) + (item * p.vpi + v0) * p.n;
+    if ((int64_t)ex >= p.e) {   // no such expert: zero rows
+        if (lane < RW && row0 + lane < p.n)
+            for (int i = 0; i < mr; ++i) Elt<XT>::store(y, i * p.n + row0 + lane, 0.0f);
+        return;
+    }
+    const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS, chunks = p.k / 32;
+    const uint32_t *codes = p.codes + (int64_t)ex * p.n * wpr;
+    const uint8_t *scales = p.scales + (int64_t)ex * p.n * gpr;
+    const XT *x = reinterpret_cast<const XT *>(p.x) + (item * p.vpi + v0) * p.k;
+
+    float acc[MR][RW];
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[i][r] = 0.0f;
+
+    for (int64_t c = lane; c < chunks; c += 64) {
+        uint32_t wd[RW][BITS];
+        uint32_t sc[RW][NG];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const int64_t row = min(row0 + r, p.n - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(codes + row * wpr + c * BITS);
+#pragma unroll
+            for (int i = 0; i < BITS / 4; ++i) {
+                const uint4 t = src[i];
+                wd[r][4 * i] = t.x, wd[r][4 * i + 1] = t.y, wd[r][4 * i + 2] = t.z, wd[r][4 * i + 3] = t.w;
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) sc[r][g] = scales[row * gpr + c * NG + g];
+        }
+#pragma unroll
+        for (int i = 0; i < MR; ++i) {
+            const XT *xr = x + (int64_t)min(i, mr - 1) * p.k + c * 32;
+            uint32_t xw[kBf16 ? 16 : 32];
+            const uint4 *xs = reinterpret_cast<const uint4 *>(xr);
+#pragma unroll
+            for (int t = 0; t < (kBf16 ? 4 : 8); ++t) {
+                const uint4 u = xs[t];
+                xw[4 * t] = u.x, xw[4 * t + 1] = u.y, xw[4 * t + 2] = u.z, xw[4 * t + 3] = u.w;
+            }
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < GS / 2; ++q) {
+                        const int pi = g * (GS / 2) + q;   // element pair of the chunk
+                        if constexpr (kBf16) {
+                            s = __builtin_amdgcn_fdot2_f32_bf16(pair_bf16<MODE>(wd[r], pi),
+                                                                __builtin_bit_cast(bf16x2_t, xw[pi]), s, false);
+                        } else {
+                            const f32x2_t e = pair_f32<MODE>(wd[r], pi);
+                            s = fmaf(__uint_as_float(xw[2 * pi]), e[0], s);
+                            s = fmaf(__uint_as_float(xw[2 * pi + 1]), e[1], s);
+                        }
+                    }
+                    acc[i][r] = fmaf(scale_value<MODE>(sc[r][g]), s, acc[i][r]);
+                }
+        }
+    }
+    const float gsc = p.gscale ? p.gscale[ex] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const float t = wave_sum(acc[i][r]);
+            if (lane == 0 && i < mr && row0 + r < p.n) Elt<XT>::store(y, i * p.n + row0 + r, t * gsc);
+        }
+}
+
+// ---------------------------------------------------------------- tiled (bf16 MFMA)
+// 128 x 128 tiles of y, four waves of 64 x 64 (2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16), K steps of 64.  Thread t stages row t / 2 of
+// the x tile and of the weight tile, 32 elements at k = 32 (t % 2): x as it
+// is, the weights as bf16(S * E) (exact: an E2M1 or E4M3 value times a power
+// of two or an E4M3 scale).  The next step's loads are issued before the
+// current step's MFMAs.  Rows past m or n stage zeros; K is a multiple of 64.
+struct FpTiledParams {
+    const bf16_bits *x;
+    bf16_bits *y;
+    const uint32_t *codes;
+    const uint8_t *scales;
+    const float *gscale;
+    int64_t m, n, k;
+};
+
+constexpr int kFpTM = 128, kFpTN = 128, kFpBK = 64, kFpLd = kFpBK + 8;
+
+template <int MODE>
+__global__ void __launch_bounds__(256) fp_tiled_kernel(FpTiledParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    __shared__ __attribute__((aligned(16))) bf16_bits xs[kFpTM * kFpLd];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[kFpTN * kFpLd];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kFpTM, n0 = (int64_t)blockIdx.x * kFpTN;
+    const int lrow = tid >> 1, lhalf = tid & 1;
+    const int64_t xm = m0 + lrow, wr = n0 + lrow;
+    const int64_t xmc = min(xm, p.m - 1), wrc = min(wr, p.n - 1);
+    const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS;
+    const int nsteps = (int)(p.k / kFpBK);
+
+    struct Ld {
+        uint4 x[4];
+        uint4 c[BITS / 4];
+        uint32_t s[NG];
+    };
+    auto load = [&](int step, Ld &l) {
+        const int64_t e0 = (int64_t)step * kFpBK + 32 * lhalf;
+        const uint4 *xsrc = reinterpret_cast<const uint4 *>(p.x + xmc * p.k + e0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) l.x[u] = xsrc[u];
+        const uint4 *csrc = reinterpret_cast<const uint4 *>(p.codes + wrc * wpr + e0 * BITS / 32);
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u) l.c[u] = csrc[u];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) l.s[g] = p.scales[wrc * gpr + e0 / GS + g];
+    };
+    auto store = [&](const Ld &l) {
+        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * kFpLd + 32 * lhalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xd[u] = xm < p.m ? l.x[u] : make_uint4(0u, 0u, 0u, 0u);
+        uint32_t wd[BITS];
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u)
+            wd[4 * u] = l.c[u].x, wd[4 * u + 1] = l.c[u].y, wd[4 * u + 2] = l.c[u].z, wd[4 * u + 3] = l.c[u].w;
+        uint32_t o[16];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float S = scale_value<MODE>(l.s[g]);
+#pragma unroll
+            for (int q = 0; q < GS / 2; ++q) {
+                const int pi = g * (GS / 2) + q;
+                const f32x2_t e = pair_f32<MODE>(wd, pi);
+                const f32x2_t v = {S * e[0], S * e[1]};
+                o[pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+            }
+        }
+        uint4 *wdst = reinterpret_cast<uint4 *>(ws + lrow * kFpLd + 32 * lhalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            wdst[u] = wr < p.n ? make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3])
+                               : make_uint4(0u, 0u, 0u, 0u);
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+    Ld cur, nxt;
+    if (nsteps > 0) load(0, cur);
+    for (int step = 0; step < nsteps; ++step) {
+        store(cur);
+        __syncthreads();
+        if (step + 1 < nsteps) load(step + 1, nxt);
+#pragma unroll
+        for (int ks = 0; ks < kFpBK / 16; ++ks) {
+            const int kk = ks * 16 + 8 * (lane >> 5);
+            bf16x8_t a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8_t *>(xs + (wm * 64 + i * 32 + (lane & 31)) * kFpLd + kk);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const bf16x8_t *>(ws + (wn * 64 + j * 32 + (lane & 31)) * kFpLd + kk);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+        cur = nxt;
+    }
+
+    const float gsc = p.gscale ? *p.gscale : 1.0f;
+    // D layout of the 32x32 MFMA: lane l holds column l % 32 and rows
+    // 8 (v / 4) + 4 (l / 32) + v % 4.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < p.m && col < p.n) p.y[row * p.n + col] = (bf16_bits)f32_to_bf16(acc[i][j][v] * gsc);
+            }
+        }
+}
+
+// ---------------------------------------------------------------- launchers
+namespace {
+
+template <template <int> class F, typename... A>
+hipError_t by_mode(int mode, A &&...a)
+{
+    switch (mode) {
+    case FP_MXFP4: return F<FP_MXFP4>::run(a...);
+    case FP_MXFP8: return F<FP_MXFP8>::run(a...);
+    default: return F<FP_NVFP4>::run(a...);
+    }
+}
+
+template <int MODE> struct QuantRun {
+    static hipError_t run(const void *w, int w_dt, int64_t chunks, uint32_t *codes, uint8_t *scales,
+                          hipStream_t stream)
+    {
+        const dim3 grid((unsigned)((chunks + 255) / 256));
+        if (w_dt == DT_BF16)
+            fp_quantize_kernel<MODE, bf16_bits><<<grid, 256, 0, stream>>>(
+                static_cast<const bf16_bits *>(w), chunks, codes, scales);
+        else
+            fp_quantize_kernel<MODE, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(w),
+                                                                       chunks, codes, scales);
+        return hipGetLastError();
+    }
+};
+
+template <int MODE> struct DequantRun {
+    static hipError_t run(const uint32_t *codes, const uint8_t *scales, int64_t chunks, void *out,
+                          int out_dt, hipStream_t stream)
+    {
+        const dim3 grid((unsigned)((chunks + 255) / 256));
+        if (out_dt == DT_BF16)
+            fp_dequantize_kernel<MODE, bf16_bits><<<grid, 256, 0, stream>>>(codes, scales, chunks,
+                                                                             static_cast<bf16_bits *>(out));
+        else
+            fp_dequantize_kernel<MODE, float><<<grid, 256, 0, stream>>>(codes, scales, chunks,
+                                                                         static_cast<float *>(out));
+        return hipGetLastError();
+    }
+};
+
+template <int MODE, typename XT, int MR>
+hipError_t gemv_mr(const FpQmmLaunch &a, hipStream_t stream)
+{
+    constexpr int RW = MR <= 2 ? 4 : MR == 4 ? 2 : 1;
+    FpGemvParams p;
+    p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale, p.idx = a.idx;
+    p.vpi = a.vpi, p.cpi = (a.vpi + MR - 1) / MR;
+    p.n = a.n, p.k = a.k, p.e = a.idx ? a.e : 1;
+    const int64_t total = a.items * p.cpi;
+    for (p.y0 = 0; p.y0 < total; p.y0 += 65535) {   // grid.y is at most 65535
+        const dim3 grid((unsigned)((a.n + 4 * RW - 1) / (4 * RW)), (unsigned)std::min<int64_t>(65535, total - p.y0));
+        fp_gemv_kernel<MODE, XT, MR, RW><<<grid, 256, 0, stream>>>(p);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+template <int MODE> struct QmmRun {
+    static hipError_t run(const FpQmmLaunch &a, hipStream_t stream)
+    {
+        if (a.tiled) {
+            FpTiledParams p;
+            p.x = static_cast<const bf16_bits *>(a.x), p.y = static_cast<bf16_bits *>(a.y);
+            p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
+            p.m = a.vpi, p.n = a.n, p.k = a.k;
+            const dim3 grid((unsigned)((a.n + kFpTN - 1) / kFpTN), (unsigned)((a.vpi + kFpTM - 1) / kFpTM));
+            fp_tiled_kernel<MODE><<<grid, 256, 0, stream>>>(p);
+            return hipGetLastError();
+        }
+        const int64_t v = a.vpi;
+        if (a.x_dt == DT_BF16) {
+            if (v <= 1) return gemv_mr<MODE, bf16_bits, 1>(a, stream);
+            if (v <= 2) return gemv_mr<MODE, bf16_bits, 2>(a, stream);
+            if (v <= 4) return gemv_mr<MODE, bf16_bits, 4>(a, stream);
+            return gemv_mr<MODE, bf16_bits, 8>(a, stream);
+        }
+        if (v <= 1) return gemv_mr<MODE, float, 1>(a, stream);
+        if (v <= 2) return gemv_mr<MODE, float, 2>(a, stream);
+        if (v <= 4) return gemv_mr<MODE, float, 4>(a, stream);
+        return gemv_mr<MODE, float, 8>(a, stream);
+    }
+};
+
+}  // namespace
+
+hipError_t launch_fp_quantize(const void *w, int w_dt, int64_t n, int64_t k, int mode, uint32_t *codes,
+                              uint8_t *scales, hipStream_t stream)
+{
+    return by_mode<QuantRun>(mode, w, w_dt, n * (k / 32), codes, scales, stream);
+}
+
+hipError_t launch_fp_dequantize(const uint32_t *codes, const uint8_t *scales, int64_t n, int64_t k, int mode,
+                                void *out, int out_dt, hipStream_t stream)
+{
+    return by_mode<DequantRun>(mode, codes, scales, n * (k / 32), out, out_dt, stream);
+}
+
+hipError_t launch_fp_qmm(const FpQmmLaunch &a, hipStream_t stream)
+{
+    return by_mode<QmmRun>(a.mode, a, stream);
+}
+
+}  // namespace nqk

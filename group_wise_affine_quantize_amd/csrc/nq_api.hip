@@ -320,6 +320,34 @@ nq_status qmm_nt_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     return check_launch(op, nqk::launch_qmm_nt(a, stream));
 }
 
+// ---- floating-point modes
+bool fp_mode_ok(int mode) { return mode == NQ_MXFP4 || mode == NQ_MXFP8 || mode == NQ_NVFP4; }
+
+nq_status check_fp(const char *op, int mode, int64_t n, int64_t k)
+{
+    if (!fp_mode_ok(mode))
+        return fail(NQ_ERR_QUANT, "%s: mode=%d is not NQ_MXFP4, NQ_MXFP8 or NQ_NVFP4", op, mode);
+    if (n < 0 || k < 0) return fail(NQ_ERR_SHAPE, "%s: negative size (n=%lld, k=%lld)", op,
+                                    (long long)n, (long long)k);
+    if (n >= kMaxDim || k >= kMaxDim || (k > 0 && n > kMaxElems / k))
+        return fail(NQ_ERR_SHAPE, "%s: size too large (n=%lld, k=%lld)", op, (long long)n,
+                    (long long)k);
+    if (k % 32 != 0)
+        return fail(NQ_ERR_SHAPE, "%s: k=%lld is not a multiple of 32", op, (long long)k);
+    return NQ_OK;
+}
+
+int64_t fp_code_bytes(int mode, int64_t n, int64_t k) { return n * (k * nqk::fp_mode_bits(mode) / 32) * 4; }
+int64_t fp_scale_bytes(int mode, int64_t n, int64_t k) { return n * (k / nqk::fp_mode_group(mode)); }
+
+nq_status check_global_scale(const char *op, int mode, const float *g)
+{
+    if (g && mode != NQ_NVFP4)
+        return fail(NQ_ERR_QUANT, "%s: a global scale is only defined for NQ_NVFP4", op);
+    if (g && !aligned_to(g, 4)) return fail(NQ_ERR_ALIGN, "%s: global scales must be 4-byte aligned", op);
+    return NQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -767,6 +795,106 @@ nq_status nq_gather_qmm_lhs(const void *x, nq_dtype x_dt, int64_t x_items, int64
     }
     return gather_impl(op, row_exact ? 1 : 0, x, x_dt, rows, l, k, codes, scales, biases, sb_dt, e, n,
                        group_size, bits, lhs_idx, x_items, rhs_idx, y, workspace, workspace_bytes, stream);
+}
+
+nq_status nq_fp_quantize(const void *w, nq_dtype w_dt, int64_t n, int64_t k, int32_t mode,
+                         uint32_t *codes, uint8_t *scales, hipStream_t stream)
+{
+    const char *op = "nq_fp_quantize";
+    g_last_error.clear();
+    if (!dtype_ok(w_dt)) return fail(NQ_ERR_DTYPE, "%s: unknown dtype w_dt=%d", op, (int)w_dt);
+    nq_status st = check_fp(op, mode, n, k);
+    if (st) return st;
+    if (n == 0 || k == 0) return NQ_OK;
+    if (!w || !codes || !scales) return fail(NQ_ERR_NULL, "%s: w, codes and scales must be non-null", op);
+    if (!aligned16(w) || !aligned16(codes))
+        return fail(NQ_ERR_ALIGN, "%s: w and codes must be 16-byte aligned", op);
+    const Span sw{w, n * k * dtype_bytes(w_dt)}, sc{codes, fp_code_bytes(mode, n, k)},
+        ss{scales, fp_scale_bytes(mode, n, k)};
+    if (overlap(sc, sw) || overlap(ss, sw)) return fail(NQ_ERR_ALIAS, "%s: an output overlaps w", op);
+    if (overlap(sc, ss)) return fail(NQ_ERR_ALIAS, "%s: codes and scales overlap", op);
+    return check_launch(op, nqk::launch_fp_quantize(w, w_dt, n, k, mode, codes, scales, stream));
+}
+
+nq_status nq_fp_dequantize(const uint32_t *codes, const uint8_t *scales, int64_t n, int64_t k,
+                           int32_t mode, void *w_out, nq_dtype out_dt, hipStream_t stream)
+{
+    const char *op = "nq_fp_dequantize";
+    g_last_error.clear();
+    if (!dtype_ok(out_dt)) return fail(NQ_ERR_DTYPE, "%s: unknown dtype out_dt=%d", op, (int)out_dt);
+    nq_status st = check_fp(op, mode, n, k);
+    if (st) return st;
+    if (n == 0 || k == 0) return NQ_OK;
+    if (!codes || !scales || !w_out)
+        return fail(NQ_ERR_NULL, "%s: codes, scales and w_out must be non-null", op);
+    if (!aligned16(codes) || !aligned16(w_out))
+        return fail(NQ_ERR_ALIGN, "%s: codes and w_out must be 16-byte aligned", op);
+    const Span so{w_out, n * k * dtype_bytes(out_dt)};
+    if (overlap(so, Span{codes, fp_code_bytes(mode, n, k)}) || overlap(so, Span{scales, fp_scale_bytes(mode, n, k)}))
+        return fail(NQ_ERR_ALIAS, "%s: w_out overlaps an input", op);
+    return check_launch(op, nqk::launch_fp_dequantize(codes, scales, n, k, mode, w_out, out_dt, stream));
+}
+
+static nq_status fp_qmm_impl(const char *op, const void *x, nq_dtype x_dt, int64_t items, int64_t vpi,
+                             int64_t k, const uint32_t *codes, const uint8_t *scales, const float *gscale,
+                             int64_t e, int64_t n, int32_t mode, const uint32_t *idx, int32_t row_exact,
+                             void *y, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (!dtype_ok(x_dt)) return fail(NQ_ERR_DTYPE, "%s: unknown dtype x_dt=%d", op, (int)x_dt);
+    nq_status st = check_fp(op, mode, n, k);
+    if (st) return st;
+    if ((st = check_global_scale(op, mode, gscale))) return st;
+    if (items < 0 || vpi < 0 || e < 1)
+        return fail(NQ_ERR_SHAPE, "%s: bad sizes (rows=%lld, l=%lld, e=%lld)", op, (long long)items,
+                    (long long)vpi, (long long)e);
+    if (items >= kMaxDim || vpi >= kMaxDim || (vpi > 0 && items > kMaxDim / vpi) || e > 65536 ||
+        (k > 0 && items * vpi > kMaxElems / std::max<int64_t>(k, n)) || e * n >= kMaxDim)
+        return fail(NQ_ERR_SHAPE, "%s: size too large", op);
+    if (items == 0 || vpi == 0 || n == 0) return NQ_OK;
+    if (!y || (idx == nullptr && e != 1) || (k > 0 && (!x || !codes || !scales)))
+        return fail(NQ_ERR_NULL, "%s: x, codes, scales, y (and rhs_idx) must be non-null", op);
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(y))
+        return fail(NQ_ERR_ALIGN, "%s: x, codes and y must be 16-byte aligned", op);
+    if (idx && !aligned_to(idx, 4)) return fail(NQ_ERR_ALIGN, "%s: rhs_idx must be 4-byte aligned", op);
+    const int64_t xb = dtype_bytes(x_dt);
+    const Span sy{y, items * vpi * n * xb};
+    if (overlap(sy, Span{x, items * vpi * k * xb}) || overlap(sy, Span{codes, e * fp_code_bytes(mode, n, k)}) ||
+        overlap(sy, Span{scales, e * fp_scale_bytes(mode, n, k)}) ||
+        overlap(sy, Span{gscale, gscale ? (idx ? e : 1) * 4 : 0}) || overlap(sy, Span{idx, idx ? items * 4 : 0}))
+        return fail(NQ_ERR_ALIAS, "%s: y overlaps an input", op);
+    nqk::FpQmmLaunch a;
+    a.x = x, a.y = y, a.codes = codes, a.scales = scales, a.gscale = gscale, a.idx = idx;
+    a.x_dt = x_dt, a.mode = mode;
+    a.items = items, a.vpi = vpi, a.n = n, a.k = k, a.e = e;
+    a.tiled = idx == nullptr && !row_exact && vpi > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && k % 64 == 0 &&
+              vpi <= (int64_t)65535 * 128;   // row tiles along grid.y
+    return check_launch(op, nqk::launch_fp_qmm(a, stream));
+}
+
+nq_status nq_fp_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const uint32_t *codes,
+                    const uint8_t *scales, const float *global_scale, int64_t n, int32_t mode,
+                    int32_t row_exact, void *y, hipStream_t stream)
+{
+    if (m < 0) {
+        g_last_error.clear();
+        return fail(NQ_ERR_SHAPE, "nq_fp_qmm: negative m=%lld", (long long)m);
+    }
+    return fp_qmm_impl("nq_fp_qmm", x, x_dt, 1, m, k, codes, scales, global_scale, 1, n, mode, nullptr,
+                       row_exact, y, stream);
+}
+
+nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                           const uint32_t *codes, const uint8_t *scales, const float *global_scales,
+                           int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, void *y,
+                           hipStream_t stream)
+{
+    if (!rhs_idx && rows > 0 && l > 0 && n > 0) {
+        g_last_error.clear();
+        return fail(NQ_ERR_NULL, "nq_fp_gather_qmm: rhs_idx must be non-null");
+    }
+    return fp_qmm_impl("nq_fp_gather_qmm", x, x_dt, rows, l, k, codes, scales, global_scales, e, n, mode,
+                       rhs_idx, 1, y, stream);
 }
 
 const char *nq_status_string(nq_status s)

@@ -145,4 +145,33 @@ struct GradLaunch {
 };
 hipError_t launch_grad_sb(const GradLaunch &a, hipStream_t stream);
 
+// ---- floating-point modes (fp.hip): element and scale formats per mode,
+// codes packed like the affine codes, uint8 scale codes, no biases; K a
+// multiple of 32 (one lane chunk: one MX block or two NVFP4 blocks).
+enum { FP_MXFP4 = 1, FP_MXFP8 = 2, FP_NVFP4 = 3 };
+inline int fp_mode_bits(int mode) { return mode == FP_MXFP8 ? 8 : 4; }
+inline int fp_mode_group(int mode) { return mode == FP_NVFP4 ? 16 : 32; }
+
+hipError_t launch_fp_quantize(const void *w, int w_dt, int64_t n, int64_t k, int mode, uint32_t *codes,
+                              uint8_t *scales, hipStream_t stream);
+hipError_t launch_fp_dequantize(const uint32_t *codes, const uint8_t *scales, int64_t n, int64_t k, int mode,
+                                void *out, int out_dt, hipStream_t stream);
+// items products of vpi vectors each: item i multiplies its vectors with
+// expert idx[i]'s weights (idx null: the only weight matrix; idx[i] >= e:
+// zero rows) and the expert's global scale (gscale null: 1).  tiled: one
+// item, bf16 x, k a multiple of 64 (128 x 128 MFMA tiles); otherwise the
+// matrix-vector kernel in chunks of up to 8 vectors.
+struct FpQmmLaunch {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const uint8_t *scales;
+    const float *gscale;
+    const uint32_t *idx;
+    int x_dt, mode;
+    int64_t items, vpi, n, k, e;
+    bool tiled;
+};
+hipError_t launch_fp_qmm(const FpQmmLaunch &a, hipStream_t stream);
+
 }  // namespace nqk

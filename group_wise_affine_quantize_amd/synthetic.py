@@ -77,3 +77,23 @@ def random_case(seed, w_shape, x_shape, w_sigma=1.0, dtype="f32", x_dtype=None):
     if (x_dtype or dtype) == "bf16":
         x = to_bf16_bits(x)
     return w, x
+
+
+def random_fp_matrix(seed, lead_shape, k, bits, group_size, scale_codes, finite_bytes=False):
+    """Seeded uniformly random packed codes and uint8 scale codes of a
+    floating-point-mode matrix [*lead_shape, k]: the code words are uniform
+    random bits (every 4-bit code equally likely); with finite_bytes (8-bit
+    codes) each byte is drawn from 0..0x7e with a random top bit instead, so
+    no byte has its low seven bits all set.  Scale codes are drawn uniformly
+    from the inclusive range scale_codes = (lo, hi)."""
+    rng = np.random.default_rng(seed)
+    lead = tuple(lead_shape)
+    if bits == 8 and finite_bytes:
+        b = rng.integers(0, 0x7F, size=lead + (k,), dtype=np.uint8)
+        b |= rng.integers(0, 2, size=lead + (k,), dtype=np.uint8) << np.uint8(7)
+        words = np.ascontiguousarray(b).view(np.uint32)
+    else:
+        words = rng.integers(0, 1 << 32, size=lead + (k * bits // 32,), dtype=np.uint32)
+    lo, hi = scale_codes
+    scales = rng.integers(lo, hi + 1, size=lead + (k // group_size,), dtype=np.uint8)
+    return words, scales

@@ -297,6 +297,72 @@ nq_status nq_gather_qmm_lhs(const void *x, nq_dtype x_dt, int64_t x_items, int64
                             int32_t row_exact, void *y, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* ---------------------------------------------------------------- floating-point modes */
+
+/* Floating-point quantization modes ("Quantization" page, section
+ * "Floating-point formats": every weight a small float, one uint8 scale code
+ * per group, no biases; dequantize gives bf16; products in x's dtype).  The
+ * page names the modes; their encodings are the public format definitions:
+ *   NQ_MXFP4  OCP Microscaling Formats v1.0, MXFP4: groups of 32 FP4 E2M1
+ *             elements (4-bit codes) sharing one E8M0 scale code s, value
+ *             2^(s - 127) (s = 255: NaN).
+ *   NQ_MXFP8  the same with FP8 E4M3 elements (8-bit codes; bias 7, largest
+ *             value 448, S.1111.111 NaN, no infinities).
+ *   NQ_NVFP4  groups of 16 E2M1 elements sharing one E4M3 scale code, and in
+ *             products an optional fp32 global scale (section "Mixture of
+ *             experts": one per expert).
+ * Layout of a matrix of n rows and k columns: codes [n, k*bits/32] uint32,
+ * packed LSB-first exactly like the affine codes (bits = 4 or 8); scales
+ * [n, k/group] uint8.  k must be a multiple of 32 (NQ_ERR_SHAPE); an
+ * unknown mode is NQ_ERR_QUANT.  A weight's value is S * E (S the decoded
+ * scale, E the decoded element), times the global scale in products. */
+typedef enum { NQ_MXFP4 = 1, NQ_MXFP8 = 2, NQ_NVFP4 = 3 } nq_fp_mode;
+
+/* Quantize w [n, k] (w_dt) -- a reading of the formats' conversion rules,
+ * every decision taken on fp32 values, bit-exact:
+ *   MX: s = clamp(floor(log2(max |w| of the group)) - emax + 127, 0, 254),
+ *       emax = 2 (E2M1) or 8 (E4M3), an all-zero group gets s = 0; each code
+ *       is the element nearest to w * 2^(127 - s).
+ *   NVFP4: s = the E4M3 code nearest to fp32(max |w| / 6); each code is the
+ *       E2M1 element nearest to fp32(w / S), S the decoded scale; S = 0 gives
+ *       zero codes.
+ * "Nearest" breaks ties to the even code, saturates at the largest finite
+ * magnitude (6 or 448) and keeps the value's sign (also for a zero).
+ * Outputs codes and scales as laid out above.  Non-finite weights are
+ * outside the contract. */
+nq_status nq_fp_quantize(const void *w, nq_dtype w_dt, int64_t n, int64_t k, int32_t mode,
+                         uint32_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Dequantize: w_out[r, j] = S * E computed in fp32 (exact for these formats
+ * unless it overflows to infinity), rounded to nearest even into out_dt
+ * (bf16 is the page's default); a NaN scale or element gives the quiet NaN
+ * 0x7fc0 (bf16) or 0x7fc00000 (fp32). */
+nq_status nq_fp_dequantize(const uint32_t *codes, const uint8_t *scales, int64_t n, int64_t k,
+                           int32_t mode, void *w_out, nq_dtype out_dt, hipStream_t stream);
+
+/* y[m, n] = x[m, k] . (g * w_hat)^T in x's dtype with fp32 accumulation, g =
+ * *global_scale (a device pointer to one fp32; NVFP4 only, else NQ_ERR_QUANT;
+ * null: 1).  With m <= 8 or row_exact = 1 the matrix-vector kernel runs in
+ * chunks of up to 8 rows, and every row is bit-equal to its one-row product;
+ * otherwise (bf16 x, k a multiple of 64) 128 x 128 bf16-MFMA tiles, whose
+ * B operands are bf16(S * E) (exact).  Tolerance as for the affine
+ * products. */
+nq_status nq_fp_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const uint32_t *codes,
+                    const uint8_t *scales, const float *global_scale, int64_t n, int32_t mode,
+                    int32_t row_exact, void *y, hipStream_t stream);
+
+/* gather_qmm in a floating-point mode ("Mixture of experts" section): x
+ * [rows, l, k]; experts codes [e, n, k*bits/32] and scales [e, n, k/group];
+ * global_scales [e] fp32 (NVFP4 only; null: 1); rhs_idx [rows] uint32.
+ * y [rows, l, n]: y[r, j, :] = x[r, j, :] . (g[i] * w_hat[i])^T with i =
+ * rhs_idx[r]; rhs_idx[r] >= e gives an all-zero row.  Every row is bit-equal
+ * to nq_fp_qmm(row_exact = 1) of x[r] with expert i's weights and global
+ * scale. */
+nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                           const uint32_t *codes, const uint8_t *scales, const float *global_scales,
+                           int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, void *y,
+                           hipStream_t stream);
+
 /* ---------------------------------------------------------------- errors */
 
 /* A static description of a status code. */

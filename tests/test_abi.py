@@ -405,3 +405,71 @@ def test_grad_scales_biases_argument_errors(lib):
         err = lib.nq_last_error().decode()
         assert err.startswith(op + ":") and msg in err, (kw, err)
     assert _grad(lib, n=0, x=0, dy=0, codes=0, ds=0, db=0) == NQ_OK
+
+
+def test_fp_mode_constants_match_binding():
+    text = open(HEADER).read()
+    assert re.search(r"NQ_MXFP4 = 1, NQ_MXFP8 = 2, NQ_NVFP4 = 3", text)
+    assert (B.NQ_MXFP4, B.NQ_MXFP8, B.NQ_NVFP4) == (1, 2, 3)
+    assert {m: v[1:] for m, v in B.FP_MODES.items()} == {"mxfp4": (4, 32), "mxfp8": (8, 32),
+                                                         "nvfp4": (4, 16)}
+
+
+def _fp_qmm(lib, x=FAKE, x_dt=BF16, m=4, k=128, codes=FAKE2, scales=FAKE2 + 0x100000, g=0, n=64,
+            mode=1, row_exact=0, y=FAKE2 + 0x300000):
+    return lib.nq_fp_qmm(x, x_dt, m, k, codes, scales, g, n, mode, row_exact, y, None)
+
+
+def test_fp_qmm_argument_errors(lib):
+    cases = [
+        (dict(x_dt=5), NQ_ERR_DTYPE, "dtype"),
+        (dict(mode=0), NQ_ERR_QUANT, "mode=0"),
+        (dict(mode=4), NQ_ERR_QUANT, "mode=4"),
+        (dict(g=FAKE2 + 0x400000), NQ_ERR_QUANT, "only defined for NQ_NVFP4"),
+        (dict(mode=3, g=FAKE2 + 0x400002), NQ_ERR_ALIGN, "4-byte"),
+        (dict(k=48), NQ_ERR_SHAPE, "multiple of 32"),
+        (dict(m=-1), NQ_ERR_SHAPE, "negative"),
+        (dict(n=-1), NQ_ERR_SHAPE, "negative"),
+        (dict(k=1 << 33), NQ_ERR_SHAPE, "too large"),
+        (dict(x=0), NQ_ERR_NULL, "non-null"),
+        (dict(scales=0), NQ_ERR_NULL, "non-null"),
+        (dict(y=0), NQ_ERR_NULL, "non-null"),
+        (dict(x=FAKE + 8), NQ_ERR_ALIGN, "aligned"),
+        (dict(y=FAKE), NQ_ERR_ALIAS, "y overlaps"),
+        (dict(y=FAKE2 + 0x100000), NQ_ERR_ALIAS, "y overlaps"),
+    ]
+    for kw, want, msg in cases:
+        st = _fp_qmm(lib, **kw)
+        assert st == want, (kw, st, lib.nq_last_error())
+        err = lib.nq_last_error().decode()
+        assert err.startswith("nq_fp_qmm:") and msg in err, (kw, err)
+    # empty products enqueue nothing and succeed, even with null pointers
+    assert _fp_qmm(lib, m=0, x=0, y=0) == NQ_OK
+    assert _fp_qmm(lib, n=0, x=0, y=0) == NQ_OK
+
+
+def test_fp_storage_and_gather_argument_errors(lib):
+    q = lambda **kw: lib.nq_fp_quantize(kw.get("w", FAKE), kw.get("dt", F32), kw.get("n", 4),
+                                        kw.get("k", 64), kw.get("mode", 3), kw.get("codes", FAKE2),
+                                        kw.get("scales", FAKE2 + 0x100000), None)
+    assert q(mode=9) == NQ_ERR_QUANT
+    assert q(k=16) == NQ_ERR_SHAPE
+    assert q(codes=0) == NQ_ERR_NULL
+    assert q(codes=FAKE2 + 4) == NQ_ERR_ALIGN
+    assert q(scales=FAKE + 16) == NQ_ERR_ALIAS and b"overlaps w" in lib.nq_last_error()
+    assert q(n=0, w=0) == NQ_OK
+    d = lambda **kw: lib.nq_fp_dequantize(kw.get("codes", FAKE2), kw.get("scales", FAKE2 + 0x100000),
+                                          4, 64, kw.get("mode", 2), kw.get("out", FAKE), kw.get("dt", BF16),
+                                          None)
+    assert d(dt=3) == NQ_ERR_DTYPE
+    assert d(out=FAKE2) == NQ_ERR_ALIAS
+    assert d(out=FAKE + 2) == NQ_ERR_ALIGN
+    assert d(scales=0) == NQ_ERR_NULL
+    gq = lambda **kw: lib.nq_fp_gather_qmm(FAKE, BF16, 4, 1, 64, FAKE2, FAKE2 + 0x100000, kw.get("g", 0),
+                                           kw.get("e", 8), 32, kw.get("mode", 3), kw.get("idx", FAKE2 + 0x200000),
+                                           FAKE2 + 0x300000, None)
+    assert gq(idx=0) == NQ_ERR_NULL and b"rhs_idx" in lib.nq_last_error()
+    assert gq(idx=FAKE2 + 0x200002) == NQ_ERR_ALIGN
+    assert gq(e=0) == NQ_ERR_SHAPE
+    assert gq(mode=1, g=FAKE2 + 0x400000) == NQ_ERR_QUANT
+    assert gq(g=FAKE2 + 0x300000) == NQ_ERR_ALIAS

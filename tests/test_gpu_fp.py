@@ -1,0 +1,194 @@
+"""GPU parity of the floating-point modes (MXFP4, MXFP8, NVFP4) against the
+CPU oracle (oracle/fp.py): quantize and dequantize bit for bit, products
+within the affine products' tolerance, every element code exactly through
+both product kernels, row independence, gathered products with global
+scales, and the decode and prefill workload sizes."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_rows_close, bits_equal, dev, host, tolerance, values
+from group_wise_affine_quantize_amd import _binding as B
+from group_wise_affine_quantize_amd import synthetic
+from oracle import fp as F
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["mxfp4", "mxfp8", "nvfp4"]
+# scale codes of moderate magnitude: E8M0 2^-7 .. 2^7, E4M3 0.125 .. 8
+SCALES = {"mxfp4": (120, 134), "mxfp8": (120, 134), "nvfp4": (0x20, 0x50)}
+
+
+def u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def codes_case(seed, lead, k, mode, finite=True):
+    _, bits, gs, _ = F.mode_info(mode)
+    return synthetic.random_fp_matrix(seed, lead, k, bits, gs, SCALES[mode], finite_bytes=finite)
+
+
+# ---------------------------------------------------------------- storage ops
+def _quantize_inputs(seed, n, k, dtype):
+    rng = np.random.default_rng(seed)
+    w = synthetic.normal(rng, (n, k), 1.0) * np.exp(rng.uniform(-6, 6, (n, 1))).astype(np.float32)
+    # edge blocks: all zeros, minus zeros, tiny values, exact element values
+    # at a fixed scale (ties after scaling), a huge value
+    w[0, :32] = 0.0
+    w[1, :32] = -0.0
+    w[2, :32] = np.float32(1e-41)
+    w[3, :32] = np.float32(np.ldexp(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4), -3))
+    w[4, :32] = np.float32(3e38) * np.sign(w[4, :32])
+    w[5, 32:64] = np.float32(np.ldexp(np.arange(32) / 16.0, -130))
+    if dtype == "bf16":
+        return synthetic.to_bf16_bits(w)
+    return w
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_bit_exact(mode, dtype):
+    w = _quantize_inputs(21, 37, 320, dtype)
+    cq, sq = F.quantize(w, mode)
+    c, s = B.nq_fp_quantize(dev(w), mode)
+    assert np.array_equal(host(c), cq), mode
+    assert np.array_equal(s.cpu().numpy(), sq), mode
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dequantize_every_code_bit_exact(mode, out):
+    # uniformly random words and every scale code, NaN ones included
+    _, bits, gs, _ = F.mode_info(mode)
+    words, _ = synthetic.random_fp_matrix(5, (64,), 512, bits, gs, (0, 255))
+    scales = np.arange(64 * 512 // gs, dtype=np.int64).reshape(64, -1) % 256
+    ref = F.dequantize(words, scales.astype(np.uint8), mode, 512, out)
+    got = host(B.nq_fp_dequantize(dev(words), u8(scales), mode,
+                                  out_dtype=torch.bfloat16 if out == "bf16" else torch.float32))
+    if out == "bf16":
+        assert np.array_equal(got, ref)
+    else:
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- products
+def _one_hot(k, dtype):
+    x = np.eye(k, dtype=np.float32)
+    return synthetic.to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("route", ["gemv_f32", "gemv_bf16", "tiled"])
+def test_products_pick_every_element_exactly(mode, route):
+    # x one-hot rows: y[i, r] = w_hat[r, i], exact in bf16 and fp32, so every
+    # element code (all 16, or all 254 finite 8-bit ones) and scale goes
+    # through the kernel's conversion without rounding
+    k, n = 128, 96
+    words, scales = codes_case(6, (n,), k, mode)
+    dtype = "f32" if route == "gemv_f32" else "bf16"
+    x = _one_hot(k, dtype)
+    exact = F.dequantize_f64(words, scales, mode, k).T          # [k, n]
+    y = B.nq_fp_qmm(dev(x), dev(words), u8(scales), mode, row_exact=route != "tiled")
+    got = values(host(y))
+    assert np.array_equal(got, exact), (mode, route, np.argwhere(got != exact)[:4])
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("m,n,k,dtype,row_exact", [
+    (1, 200, 320, "bf16", False),
+    (3, 77, 96, "f32", False),
+    (8, 128, 2048 + 96, "bf16", False),
+    (40, 200, 320, "bf16", False),      # tiles, ragged m and n
+    (130, 260, 448, "bf16", False),     # several tiles
+    (40, 200, 96, "bf16", False),       # k not a multiple of 64: matrix-vector chunks
+    (13, 150, 320, "bf16", True),
+    (20, 64, 256, "f32", False),
+])
+def test_qmm_matches_oracle(mode, m, n, k, dtype, row_exact):
+    rng_seed = 100 + m + n + k
+    words, scales = codes_case(rng_seed, (n,), k, mode)
+    _, x = synthetic.random_case(rng_seed, (1, k), (m, k), 1.0, dtype)
+    ref = F.qmm_f64(x, words, scales, mode)
+    y = B.nq_fp_qmm(dev(x), dev(words), u8(scales), mode, row_exact=row_exact)
+    assert_rows_close(values(host(y)), ref, tolerance(y.dtype), (mode, m, n, k, dtype))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rows_keep_their_one_row_bits(mode, dtype):
+    words, scales = codes_case(8, (300,), 2048 + 320, mode)
+    _, x = synthetic.random_case(9, (1, 2048 + 320), (13, 2048 + 320), 1.0, dtype)
+    xs, cs, ss = dev(x), dev(words), u8(scales)
+    full = B.nq_fp_qmm(xs, cs, ss, mode, row_exact=True)
+    few = B.nq_fp_qmm(xs[:5], cs, ss, mode)
+    for i in range(13):
+        one = B.nq_fp_qmm(xs[i:i + 1], cs, ss, mode)
+        assert bits_equal(full[i:i + 1], one), (mode, i)
+        if i < 5:
+            assert bits_equal(few[i:i + 1], one), (mode, i)
+
+
+def test_nvfp4_global_scale():
+    words, scales = codes_case(10, (200,), 320, "nvfp4")
+    _, x = synthetic.random_case(10, (1, 320), (40, 320), 1.0, "bf16")
+    g = np.float32(0.0371)
+    gt = torch.tensor([g], dtype=torch.float32, device="cuda")
+    for m in (1, 40):
+        ref = F.qmm_f64(x[:m], words, scales, "nvfp4", g)
+        y = B.nq_fp_qmm(dev(x[:m]), dev(words), u8(scales), "nvfp4", global_scale=gt)
+        assert_rows_close(values(host(y)), ref, tolerance(y.dtype), m)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_gather_rows_match_their_expert(mode):
+    e, n, k, rows, l = 4, 96, 256, 10, 2
+    words, scales = codes_case(12, (e, n), k, mode)
+    _, x = synthetic.random_case(12, (1, k), (rows, l, k), 1.0, "bf16")
+    idx = np.array([3, 0, 0, 1, 9, 2, 3, 3, 1, 0], np.uint32)          # 9: no such expert
+    gsc = np.array([0.5, 1.25, 2.0, 0.75], np.float32) if mode == "nvfp4" else None
+    gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
+    assert not values(host(y[4])).any()
+    keep = [r for r in range(rows) if idx[r] < e]
+    assert_rows_close(values(host(y[keep])), ref[keep], tolerance(y.dtype), mode)
+    for r in keep:
+        ex = int(idx[r])
+        one = B.nq_fp_qmm(dev(x[r]), dev(words[ex]), u8(scales[ex]), mode,
+                          global_scale=None if gt is None else gt[ex:ex + 1], row_exact=True)
+        assert bits_equal(y[r], one), (mode, r)
+
+
+def test_empty_and_zero_k():
+    words, scales = codes_case(13, (64,), 64, "mxfp4")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    assert B.nq_fp_qmm(x, dev(words), u8(scales), "mxfp4").shape == (0, 64)
+    x0 = torch.ones((20, 0), dtype=torch.bfloat16, device="cuda")
+    c0 = torch.zeros((64, 0), dtype=torch.int32, device="cuda")
+    s0 = torch.zeros((64, 0), dtype=torch.uint8, device="cuda")
+    for m in (1, 20):
+        y = B.nq_fp_qmm(x0[:m], c0, s0, "mxfp4")
+        torch.cuda.synchronize()
+        assert not y.float().abs().sum().item()
+
+
+# ---------------------------------------------------------------- workload sizes
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_size(mode):
+    # [1, 4096] . [14336, 4096]^T, all outputs against the oracle
+    words, scales = codes_case(14, (14336,), 4096, mode)
+    _, x = synthetic.random_case(14, (1, 4096), (1, 4096), 1.0, "bf16")
+    y = B.nq_fp_qmm(dev(x), dev(words), u8(scales), mode)
+    ref = F.qmm_f64(x, words, scales, mode)
+    assert_rows_close(values(host(y)), ref, tolerance(y.dtype), mode)
+
+
+def test_prefill_size_sampled_rows():
+    # [2048, 4096] . [14336, 4096]^T in tiles; 16 sampled rows against the oracle
+    mode = "mxfp4"
+    words, scales = codes_case(15, (14336,), 4096, mode)
+    _, x = synthetic.random_case(15, (1, 4096), (2048, 4096), 1.0, "bf16")
+    y = B.nq_fp_qmm(dev(x), dev(words), u8(scales), mode)
+    rows = np.random.default_rng(15).choice(2048, 16, replace=False)
+    ref = F.qmm_f64(x[rows], words, scales, mode)
+    assert_rows_close(values(host(y[torch.from_numpy(rows).cuda()])), ref, tolerance(y.dtype), mode)
