@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     nq_dequantize,
     nq_fp_dequantize,
     nq_fp_gather_qmm,
+    nq_fp_gather_qmm_workspace_bytes,
     nq_fp_qmm,
     nq_fp_quantize,
     nq_gather_qmm,

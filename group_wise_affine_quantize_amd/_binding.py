@@ -75,13 +75,15 @@ _SIGNATURES = {
     "nq_fp_quantize": [_P, _I32, _I64, _I64, _I32, _P, _P, _P],
     "nq_fp_dequantize": [_P, _P, _I64, _I64, _I32, _P, _I32, _P],
     "nq_fp_qmm": [_P, _I32, _I64, _I64, _P, _P, _P, _I64, _I32, _I32, _P, _P],
-    "nq_fp_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _P],
+    "nq_fp_gather_qmm_workspace_bytes": [_I64, _I64, _I64, _I64, _I64],
+    "nq_fp_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _P, _SZ,
+                         _P],
     "nq_status_string": [_I32],
     "nq_last_error": [],
     "nq_version": [],
 }
 _RESTYPES = {"nq_qmm_workspace_bytes": _SZ, "nq_gather_qmm_workspace_bytes": _SZ,
-             "nq_qmm_notrans_workspace_bytes": _SZ,
+             "nq_qmm_notrans_workspace_bytes": _SZ, "nq_fp_gather_qmm_workspace_bytes": _SZ,
              "nq_status_string": ctypes.c_char_p, "nq_last_error": ctypes.c_char_p,
              "nq_version": ctypes.c_char_p}
 
@@ -482,10 +484,16 @@ def nq_fp_qmm(x, codes, scales, mode, global_scale=None, row_exact=False, y=None
     return y
 
 
-def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, y=None, stream=None):
+def nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n):
+    return load_library().nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n)
+
+
+def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, y=None, workspace=None,
+                     stream=None):
     """x [rows, l, k], stacked experts codes [e, n, words] and scales [e, n,
     groups], rhs_idx [rows] (uint32 as int32), optional per-expert fp32 global
-    scales [e] (NVFP4) -> y [rows, l, n]."""
+    scales [e] (NVFP4) -> y [rows, l, n].  The workspace (bytes from
+    nq_fp_gather_qmm_workspace_bytes) is allocated here when not given."""
     torch = _torch()
     lib = load_library()
     mid, bits, gs = _fp(mode)
@@ -499,6 +507,11 @@ def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, y=None
         raise ValueError("rhs_idx must hold one expert per row")
     if y is None:
         y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        need = lib.nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_fp_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
-                                _ptr(global_scales), e, n, mid, _ptr(rhs_idx), _ptr(y), _stream(stream)))
+                                _ptr(global_scales), e, n, mid, _ptr(rhs_idx), _ptr(y), _ptr(workspace),
+                                ws_bytes, _stream(stream)))
     return y

@@ -129,6 +129,45 @@ __device__ __forceinline__ uint32_t elem_code(float v)
     return Fp<MODE>::fp8 ? e4m3_code(v) : e2m1_code(v);
 }
 
+// ---------------------------------------------------------------- element pairs
+// Elements 2p and 2p + 1 of a chunk's code words as bf16 or fp32 pairs (the
+// scaled conversions with scale 1: exact for these formats).
+template <int MODE>
+__device__ __forceinline__ bf16x2_t pair_bf16(const uint32_t *wd, int p)
+{
+    if constexpr (Fp<MODE>::fp8) {
+        const uint32_t w = wd[p >> 1];
+        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    } else {
+        const uint32_t w = wd[p >> 2];
+        switch (p & 3) {   // the byte select is an immediate
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+        }
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ f32x2_t pair_f32(const uint32_t *wd, int p)
+{
+    if constexpr (Fp<MODE>::fp8) {
+        const uint32_t w = wd[p >> 1];
+        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    } else {
+        const uint32_t w = wd[p >> 2];
+        switch (p & 3) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- quantize
 template <int MODE, typename WT>
 __global__ void __launch_bounds__(256) fp_quantize_kernel(const WT *__restrict__ w, int64_t chunks,
@@ -171,14 +210,23 @@ __global__ void __launch_bounds__(256) fp_quantize_kernel(const WT *__restrict__
 }
 
 // ---------------------------------------------------------------- dequantize
+// A wave's 64 chunks are one contiguous run of the output: each lane puts
+// its piece (64 or 128 bytes) into LDS and the wave stores the run with
+// every instruction writing 1 KB contiguous.  Lane pieces sit 16 bytes
+// apart beyond their length (stride P + 1 uint4), which keeps the 16-byte
+// writes of 16 lanes on distinct banks.
 template <int MODE, typename OT>
 __global__ void __launch_bounds__(256) fp_dequantize_kernel(const uint32_t *__restrict__ codes,
                                                             const uint8_t *__restrict__ scales,
                                                             int64_t chunks, OT *__restrict__ out)
 {
     constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= chunks) return;
+    constexpr int P = 32 * (int)sizeof(OT) / 16;   // uint4 pieces per lane
+    __shared__ uint4 stage[4][64 * (P + 1)];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t cw = ((int64_t)blockIdx.x * 4 + wave) * 64;   // the wave's first chunk
+    if (cw >= chunks) return;
+    const int64_t c = min(cw + lane, chunks - 1);
     uint32_t wd[BITS];
     const uint4 *src = reinterpret_cast<const uint4 *>(codes + c * BITS);
 #pragma unroll
@@ -186,68 +234,55 @@ __global__ void __launch_bounds__(256) fp_dequantize_kernel(const uint32_t *__re
         const uint4 t = src[i];
         wd[4 * i] = t.x, wd[4 * i + 1] = t.y, wd[4 * i + 2] = t.z, wd[4 * i + 3] = t.w;
     }
-    float S[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) S[g] = scale_value<MODE>(scales[c * NG + g]);
+    // S * E in fp32 (exact) from the hardware pair conversion; a NaN scale
+    // makes its whole group NaN, a NaN element (E4M3 only) its own value;
+    // every NaN leaves as the canonical quiet NaN
     float o[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const uint32_t q = (wd[j * BITS / 32] >> ((j * BITS) % 32)) & ((1u << BITS) - 1u);
-        const float x = S[j / GS] * elem_value<MODE>(q);
-        o[j] = x != x ? __uint_as_float(kQuietNan) : x;
+    for (int g = 0; g < NG; ++g) {
+        const float S = scale_value<MODE>(scales[c * NG + g]);
+        const bool snan = S != S;
+#pragma unroll
+        for (int q = 0; q < GS / 2; ++q) {
+            const int pi = g * (GS / 2) + q;
+            const f32x2_t e = pair_f32<MODE>(wd, pi);
+            float v0 = S * e[0], v1 = S * e[1];
+            if constexpr (Fp<MODE>::fp8) {
+                v0 = v0 != v0 ? __uint_as_float(kQuietNan) : v0;
+                v1 = v1 != v1 ? __uint_as_float(kQuietNan) : v1;
+            }
+            o[2 * pi] = snan ? __uint_as_float(kQuietNan) : v0;
+            o[2 * pi + 1] = snan ? __uint_as_float(kQuietNan) : v1;
+        }
     }
+    uint4 *st = stage[wave];
     if constexpr (std::is_same<OT, float>::value) {
-        uint4 *dst = reinterpret_cast<uint4 *>(out + c * 32);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            dst[i] = make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
-                                __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3]));
+            st[lane * (P + 1) + i] = make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
+                                                __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3]));
     } else {
+        // hardware round-to-nearest-even packing (the canonical NaN stays 0x7fc0)
         uint32_t h[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) h[i] = f32_to_bf16(o[2 * i]) | (f32_to_bf16(o[2 * i + 1]) << 16);
-        uint4 *dst = reinterpret_cast<uint4 *>(out + c * 32);
+        for (int i = 0; i < 16; ++i) {
+            const f32x2_t v = {o[2 * i], o[2 * i + 1]};
+            h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+        for (int i = 0; i < 4; ++i)
+            st[lane * (P + 1) + i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
     }
-}
-
-// ---------------------------------------------------------------- element pairs
-// Elements 2p and 2p + 1 of a chunk's code words as bf16 or fp32 pairs (the
-// scaled conversions with scale 1: exact for these formats).
-template <int MODE>
-__device__ __forceinline__ bf16x2_t pair_bf16(const uint32_t *wd, int p)
-{
-    if constexpr (Fp<MODE>::fp8) {
-        const uint32_t w = wd[p >> 1];
-        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    } else {
-        const uint32_t w = wd[p >> 2];
-        switch (p & 3) {   // the byte select is an immediate
-        case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-        case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
-        case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
-        default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
-        }
-    }
-}
-
-template <int MODE>
-__device__ __forceinline__ f32x2_t pair_f32(const uint32_t *wd, int p)
-{
-    if constexpr (Fp<MODE>::fp8) {
-        const uint32_t w = wd[p >> 1];
-        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
-                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
-    } else {
-        const uint32_t w = wd[p >> 2];
-        switch (p & 3) {
-        case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-        case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-        case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-        default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-        }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // store instruction u writes uint4 j = 64 u + lane of the wave's run
+    const int64_t valid = min((int64_t)64, chunks - cw) * P;   // uint4 of the run inside the output
+    uint4 *dst = reinterpret_cast<uint4 *>(out + cw * 32);
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int j = 64 * u + lane;
+        if (j < valid) dst[j] = st[(j / P) * (P + 1) + j % P];
     }
 }
 
@@ -269,6 +304,11 @@ struct FpGemvParams {
     int64_t vpi, cpi;        // vectors per item, MR-chunks per item
     int64_t n, k, e;
     int64_t y0;              // first (item, chunk) index of this launch
+    // grouped gather: workgroup row c runs chunk c of the table built by the
+    // grouping pass (uint4 {expert, first, count, 0} over perm); chunks past
+    // *nchunks do nothing
+    const uint4 *chunks;
+    const uint32_t *perm, *nchunks;
 };
 
 __device__ __forceinline__ float wave_sum(float v)
@@ -285,22 +325,35 @@ __global__ void __launch_bounds__(256) fp_gemv_kernel(FpGemvParams p)
     constexpr bool kBf16 = std::is_same<XT, bf16_bits>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t yb = p.y0 + blockIdx.y;
-    const int64_t item = yb / p.cpi;
-    const int64_t v0 = (yb % p.cpi) * MR;
-    const int mr = (int)min((int64_t)MR, p.vpi - v0);
     const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RW;
     if (row0 >= p.n) return;
-    const uint32_t ex = p.idx ? p.idx[item] : 0u;
-    XT *y = reinterpret_cast<XT *>(p.y) + (item * p.vpi + v0) * p.n;
+    // the chunk's vectors (rows of x and y) and their expert
+    int64_t vec[MR];
+    int mr;
+    uint32_t ex;
+    if (p.chunks) {
+        if (yb >= *p.nchunks) return;   // uniform over the workgroup
+        const uint4 ch = p.chunks[yb];
+        ex = ch.x, mr = (int)ch.z;
+#pragma unroll
+        for (int i = 0; i < MR; ++i) vec[i] = p.perm[ch.y + min(i, mr - 1)];
+    } else {
+        const int64_t item = yb / p.cpi, v0 = (yb % p.cpi) * MR;
+        mr = (int)min((int64_t)MR, p.vpi - v0);
+        ex = p.idx ? p.idx[item] : 0u;
+#pragma unroll
+        for (int i = 0; i < MR; ++i) vec[i] = item * p.vpi + v0 + min(i, mr - 1);
+    }
+    XT *y = reinterpret_cast<XT *>(p.y);
     if ((int64_t)ex >= p.e) {   // no such expert: zero rows
         if (lane < RW && row0 + lane < p.n)
-            for (int i = 0; i < mr; ++i) Elt<XT>::store(y, i * p.n + row0 + lane, 0.0f);
+            for (int i = 0; i < mr; ++i) Elt<XT>::store(y, vec[i] * p.n + row0 + lane, 0.0f);
         return;
     }
     const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS, chunks = p.k / 32;
     const uint32_t *codes = p.codes + (int64_t)ex * p.n * wpr;
     const uint8_t *scales = p.scales + (int64_t)ex * p.n * gpr;
-    const XT *x = reinterpret_cast<const XT *>(p.x) + (item * p.vpi + v0) * p.k;
+    const XT *x = reinterpret_cast<const XT *>(p.x);
 
     float acc[MR][RW];
 #pragma unroll
@@ -308,24 +361,36 @@ __global__ void __launch_bounds__(256) fp_gemv_kernel(FpGemvParams p)
 #pragma unroll
         for (int r = 0; r < RW; ++r) acc[i][r] = 0.0f;
 
-    for (int64_t c = lane; c < chunks; c += 64) {
-        uint32_t wd[RW][BITS];
-        uint32_t sc[RW][NG];
+    // U chunks per pass (their loads issued together); a lane still adds its
+    // chunks in increasing order
+    constexpr int U = 2;
+    for (int64_t c0 = lane; c0 < chunks; c0 += 64 * U) {
+        uint32_t wd[U][RW][BITS];
+        uint32_t sc[U][RW][NG];
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int64_t row = min(row0 + r, p.n - 1);
-            const uint4 *src = reinterpret_cast<const uint4 *>(codes + row * wpr + c * BITS);
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + 64 * u < chunks ? c0 + 64 * u : c0;
 #pragma unroll
-            for (int i = 0; i < BITS / 4; ++i) {
-                const uint4 t = src[i];
-                wd[r][4 * i] = t.x, wd[r][4 * i + 1] = t.y, wd[r][4 * i + 2] = t.z, wd[r][4 * i + 3] = t.w;
+            for (int r = 0; r < RW; ++r) {
+                const int64_t row = min(row0 + r, p.n - 1);
+                const uint4 *src = reinterpret_cast<const uint4 *>(codes + row * wpr + c * BITS);
+#pragma unroll
+                for (int i = 0; i < BITS / 4; ++i) {
+                    const uint4 t = src[i];
+                    wd[u][r][4 * i] = t.x, wd[u][r][4 * i + 1] = t.y, wd[u][r][4 * i + 2] = t.z,
+                    wd[u][r][4 * i + 3] = t.w;
+                }
+#pragma unroll
+                for (int g = 0; g < NG; ++g) sc[u][r][g] = scales[row * gpr + c * NG + g];
             }
-#pragma unroll
-            for (int g = 0; g < NG; ++g) sc[r][g] = scales[row * gpr + c * NG + g];
         }
 #pragma unroll
+        for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + 64 * u;
+        if (c >= chunks) break;
+#pragma unroll
         for (int i = 0; i < MR; ++i) {
-            const XT *xr = x + (int64_t)min(i, mr - 1) * p.k + c * 32;
+            const XT *xr = x + vec[i] * p.k + c * 32;
             uint32_t xw[kBf16 ? 16 : 32];
             const uint4 *xs = reinterpret_cast<const uint4 *>(xr);
 #pragma unroll
@@ -342,16 +407,17 @@ __global__ void __launch_bounds__(256) fp_gemv_kernel(FpGemvParams p)
                     for (int q = 0; q < GS / 2; ++q) {
                         const int pi = g * (GS / 2) + q;   // element pair of the chunk
                         if constexpr (kBf16) {
-                            s = __builtin_amdgcn_fdot2_f32_bf16(pair_bf16<MODE>(wd[r], pi),
+                            s = __builtin_amdgcn_fdot2_f32_bf16(pair_bf16<MODE>(wd[u][r], pi),
                                                                 __builtin_bit_cast(bf16x2_t, xw[pi]), s, false);
                         } else {
-                            const f32x2_t e = pair_f32<MODE>(wd[r], pi);
+                            const f32x2_t e = pair_f32<MODE>(wd[u][r], pi);
                             s = fmaf(__uint_as_float(xw[2 * pi]), e[0], s);
                             s = fmaf(__uint_as_float(xw[2 * pi + 1]), e[1], s);
                         }
                     }
-                    acc[i][r] = fmaf(scale_value<MODE>(sc[r][g]), s, acc[i][r]);
+                    acc[i][r] = fmaf(scale_value<MODE>(sc[u][r][g]), s, acc[i][r]);
                 }
+        }
         }
     }
     const float gsc = p.gscale ? p.gscale[ex] : 1.0f;
@@ -360,8 +426,96 @@ __global__ void __launch_bounds__(256) fp_gemv_kernel(FpGemvParams p)
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
             const float t = wave_sum(acc[i][r]);
-            if (lane == 0 && i < mr && row0 + r < p.n) Elt<XT>::store(y, i * p.n + row0 + r, t * gsc);
+            if (lane == 0 && i < mr && row0 + r < p.n) Elt<XT>::store(y, vec[i] * p.n + row0 + r, t * gsc);
         }
+}
+
+// One bf16 activation row (decode), K at most 64 U lane chunks: persistent
+// waves.  Lane L keeps its x chunks L + 64 u in registers; wave w of W takes
+// the weight rows w, w + W, ... and issues the next row's code and scale
+// loads before the current row's arithmetic.  Per row the arithmetic is
+// fp_gemv_kernel's (chunks in increasing order, the same dot products,
+// scaling and butterfly), so the bits are the same.
+template <int MODE, int U>
+__global__ void __launch_bounds__(256) fp_gemv_stream_kernel(FpGemvParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    // x goes through LDS once per workgroup (16-byte pieces), then each
+    // lane keeps its chunks in registers
+    __shared__ uint4 xl[64 * U * 4];
+    const int lane = threadIdx.x & 63;
+    const int64_t W = (int64_t)gridDim.x * 4;
+    int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS, chunks = p.k / 32;
+    const uint4 *xg = static_cast<const uint4 *>(p.x);
+    for (int i = threadIdx.x; i < (int)chunks * 4; i += 256) xl[i] = xg[i];
+    __syncthreads();
+    if (row >= p.n) return;
+    uint32_t xw[U][16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (int)min((int64_t)lane + 64 * u, chunks - 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 v = xl[c * 4 + t];
+            xw[u][4 * t] = v.x, xw[u][4 * t + 1] = v.y, xw[u][4 * t + 2] = v.z, xw[u][4 * t + 3] = v.w;
+        }
+    }
+    struct RowLd {
+        uint32_t wd[U][BITS];
+        uint32_t sc[U][NG];
+    };
+    auto load = [&](int64_t r, RowLd &l) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = min((int64_t)lane + 64 * u, chunks - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(p.codes + r * wpr + c * BITS);
+#pragma unroll
+            for (int i = 0; i < BITS / 4; ++i) {
+                const uint4 t = src[i];
+                l.wd[u][4 * i] = t.x, l.wd[u][4 * i + 1] = t.y, l.wd[u][4 * i + 2] = t.z, l.wd[u][4 * i + 3] = t.w;
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) l.sc[u][g] = p.scales[r * gpr + c * NG + g];
+        }
+    };
+    const float gsc = p.gscale ? p.gscale[0] : 1.0f;
+    bf16_bits *y = static_cast<bf16_bits *>(p.y);
+    // The next row's loads are unconditional (past the last row they re-read
+    // it), so the loop is straight-line and the wait before a row's
+    // arithmetic leaves the next row's loads in flight.  Results wait in
+    // lane j (iteration j mod 64) and are stored 64 at a time, so no store
+    // sits between a row's loads and their wait.
+    RowLd cur, nxt;
+    load(row, cur);
+    const int64_t row0 = row;
+    float res = 0.0f;
+    for (int j = 0; row < p.n; row += W, ++j) {
+        load(min(row + W, p.n - 1), nxt);
+        float acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if ((int64_t)lane + 64 * u >= chunks) break;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                float s = 0.0f;
+#pragma unroll
+                for (int q = 0; q < GS / 2; ++q) {
+                    const int pi = g * (GS / 2) + q;
+                    s = __builtin_amdgcn_fdot2_f32_bf16(pair_bf16<MODE>(cur.wd[u], pi),
+                                                        __builtin_bit_cast(bf16x2_t, xw[u][pi]), s, false);
+                }
+                acc = fmaf(scale_value<MODE>(cur.sc[u][g]), s, acc);
+            }
+        }
+        const float t = wave_sum(acc) * gsc;
+        res = lane == (j & 63) ? t : res;
+        if ((j & 63) == 63 || row + W >= p.n) {   // uniform over the wave
+            const int64_t r = row0 + ((int64_t)(j & ~63) + lane) * W;
+            if (lane <= (j & 63)) Elt<bf16_bits>::store(y, r, res);
+        }
+        cur = nxt;
+    }
 }
 
 // ---------------------------------------------------------------- tiled (bf16 MFMA)
@@ -521,7 +675,7 @@ template <int MODE> struct DequantRun {
     static hipError_t run(const uint32_t *codes, const uint8_t *scales, int64_t chunks, void *out,
                           int out_dt, hipStream_t stream)
     {
-        const dim3 grid((unsigned)((chunks + 255) / 256));
+        const dim3 grid((unsigned)((chunks + 255) / 256));   // 4 waves of 64 chunks
         if (out_dt == DT_BF16)
             fp_dequantize_kernel<MODE, bf16_bits><<<grid, 256, 0, stream>>>(codes, scales, chunks,
                                                                              static_cast<bf16_bits *>(out));
@@ -532,15 +686,15 @@ template <int MODE> struct DequantRun {
     }
 };
 
-template <int MODE, typename XT, int MR>
-hipError_t gemv_mr(const FpQmmLaunch &a, hipStream_t stream)
+template <int MODE, typename XT, int MR, int RW>
+hipError_t gemv_mr_rw(const FpQmmLaunch &a, hipStream_t stream)
 {
-    constexpr int RW = MR <= 2 ? 4 : MR == 4 ? 2 : 1;
     FpGemvParams p;
     p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale, p.idx = a.idx;
     p.vpi = a.vpi, p.cpi = (a.vpi + MR - 1) / MR;
-    p.n = a.n, p.k = a.k, p.e = a.idx ? a.e : 1;
-    const int64_t total = a.items * p.cpi;
+    p.n = a.n, p.k = a.k, p.e = a.idx || a.chunks ? a.e : 1;
+    p.chunks = a.chunks, p.perm = a.perm, p.nchunks = a.nchunks;
+    const int64_t total = a.chunks ? a.max_chunks : a.items * p.cpi;
     for (p.y0 = 0; p.y0 < total; p.y0 += 65535) {   // grid.y is at most 65535
         const dim3 grid((unsigned)((a.n + 4 * RW - 1) / (4 * RW)), (unsigned)std::min<int64_t>(65535, total - p.y0));
         fp_gemv_kernel<MODE, XT, MR, RW><<<grid, 256, 0, stream>>>(p);
@@ -550,9 +704,56 @@ hipError_t gemv_mr(const FpQmmLaunch &a, hipStream_t stream)
     return hipSuccess;
 }
 
+// Weight rows per wave: the most of 4, 2, 1 whose workgroup count along n
+// fills its last round of 256 compute units best (a whole number of
+// workgroups per CU; an uneven count leaves some CUs a round longer).  One
+// x load serves RW rows; RW never changes a row's arithmetic.
+inline int fp_gemv_rows_per_wave(int64_t n)
+{
+    int best = 4;
+    double best_fill = 0.0;
+    for (int rw : {4, 2, 1}) {
+        const int64_t g = (n + 4 * rw - 1) / (4 * rw);
+        const double fill = (double)g / (double)(((g + 255) / 256) * 256);
+        if (fill > best_fill + 1e-9) best = rw, best_fill = fill;
+    }
+    return best;
+}
+
+template <int MODE, typename XT, int MR>
+hipError_t gemv_mr(const FpQmmLaunch &a, hipStream_t stream)
+{
+    switch (fp_gemv_rows_per_wave(a.n)) {
+    case 1: return gemv_mr_rw<MODE, XT, MR, 1>(a, stream);
+    case 2: return gemv_mr_rw<MODE, XT, MR, 2>(a, stream);
+    default: return gemv_mr_rw<MODE, XT, MR, 4>(a, stream);
+    }
+}
+
+// One bf16 row, one weight matrix, K at most 256 lane chunks: the
+// streaming kernel on a whole number of workgroups per CU that stay
+// resident together (4, or 2 with the x registers of 4 chunks a lane).
+template <int MODE, int U>
+hipError_t gemv_stream(const FpQmmLaunch &a, hipStream_t stream)
+{
+    FpGemvParams p = {};
+    p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
+    p.n = a.n, p.k = a.k, p.e = 1;
+    const int64_t wgs = std::min<int64_t>((a.n + 3) / 4, (U >= 4 ? 2 : 4) * 256);
+    fp_gemv_stream_kernel<MODE, U><<<dim3((unsigned)wgs), 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
 template <int MODE> struct QmmRun {
     static hipError_t run(const FpQmmLaunch &a, hipStream_t stream)
     {
+        if (!a.tiled && !a.idx && !a.chunks && a.vpi == 1 && a.items == 1 && a.x_dt == DT_BF16 && a.k > 0 &&
+            a.k <= 256 * 32) {
+            const int64_t c = a.k / 32;
+            if (c <= 64) return gemv_stream<MODE, 1>(a, stream);
+            if (c <= 128) return gemv_stream<MODE, 2>(a, stream);
+            return gemv_stream<MODE, 4>(a, stream);
+        }
         if (a.tiled) {
             FpTiledParams p;
             p.x = static_cast<const bf16_bits *>(a.x), p.y = static_cast<bf16_bits *>(a.y);
@@ -562,7 +763,7 @@ template <int MODE> struct QmmRun {
             fp_tiled_kernel<MODE><<<grid, 256, 0, stream>>>(p);
             return hipGetLastError();
         }
-        const int64_t v = a.vpi;
+        const int64_t v = a.chunks ? kGroupChunk : a.vpi;
         if (a.x_dt == DT_BF16) {
             if (v <= 1) return gemv_mr<MODE, bf16_bits, 1>(a, stream);
             if (v <= 2) return gemv_mr<MODE, bf16_bits, 2>(a, stream);

@@ -838,7 +838,7 @@ nq_status nq_fp_dequantize(const uint32_t *codes, const uint8_t *scales, int64_t
 static nq_status fp_qmm_impl(const char *op, const void *x, nq_dtype x_dt, int64_t items, int64_t vpi,
                              int64_t k, const uint32_t *codes, const uint8_t *scales, const float *gscale,
                              int64_t e, int64_t n, int32_t mode, const uint32_t *idx, int32_t row_exact,
-                             void *y, hipStream_t stream)
+                             void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     g_last_error.clear();
     if (!dtype_ok(x_dt)) return fail(NQ_ERR_DTYPE, "%s: unknown dtype x_dt=%d", op, (int)x_dt);
@@ -863,12 +863,37 @@ static nq_status fp_qmm_impl(const char *op, const void *x, nq_dtype x_dt, int64
         overlap(sy, Span{scales, e * fp_scale_bytes(mode, n, k)}) ||
         overlap(sy, Span{gscale, gscale ? (idx ? e : 1) * 4 : 0}) || overlap(sy, Span{idx, idx ? items * 4 : 0}))
         return fail(NQ_ERR_ALIAS, "%s: y overlaps an input", op);
+    // gathered rows that share experts are grouped on the device, so that
+    // each expert's weights are read once per chunk of vectors
+    const bool grouped = idx && gather_shared(items, vpi, k, e, n);
+    if (grouped) {
+        const size_t need = nqk::gather_group_ws_bytes(items * vpi, e, nqk::kGroupChunk);
+        if (!workspace || workspace_bytes < need)
+            return fail(NQ_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", op, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(NQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", op);
+        const Span sw{workspace, (int64_t)need};
+        if (overlap(sw, sy) || overlap(sw, Span{x, items * vpi * k * xb}) ||
+            overlap(sw, Span{codes, e * fp_code_bytes(mode, n, k)}) ||
+            overlap(sw, Span{scales, e * fp_scale_bytes(mode, n, k)}) || overlap(sw, Span{idx, items * 4}))
+            return fail(NQ_ERR_ALIAS, "%s: the workspace overlaps an argument", op);
+    }
     nqk::FpQmmLaunch a;
     a.x = x, a.y = y, a.codes = codes, a.scales = scales, a.gscale = gscale, a.idx = idx;
     a.x_dt = x_dt, a.mode = mode;
     a.items = items, a.vpi = vpi, a.n = n, a.k = k, a.e = e;
     a.tiled = idx == nullptr && !row_exact && vpi > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && k % 64 == 0 &&
               vpi <= (int64_t)65535 * 128;   // row tiles along grid.y
+    if (grouped) {
+        hipError_t err = nqk::launch_gather_groups(idx, nullptr, items, items, vpi, e, nqk::kGroupChunk,
+                                                   workspace, stream);
+        if (err != hipSuccess) return check_launch(op, err);
+        const int64_t v = items * vpi;
+        uint32_t *ws = static_cast<uint32_t *>(workspace);
+        a.perm = ws, a.nchunks = ws + v;
+        a.chunks = reinterpret_cast<const uint4 *>(ws + ((v + 1 + 3) & ~(int64_t)3));
+        a.max_chunks = nqk::gather_group_max_chunks(v, e, nqk::kGroupChunk);
+    }
     return check_launch(op, nqk::launch_fp_qmm(a, stream));
 }
 
@@ -881,20 +906,26 @@ nq_status nq_fp_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const ui
         return fail(NQ_ERR_SHAPE, "nq_fp_qmm: negative m=%lld", (long long)m);
     }
     return fp_qmm_impl("nq_fp_qmm", x, x_dt, 1, m, k, codes, scales, global_scale, 1, n, mode, nullptr,
-                       row_exact, y, stream);
+                       row_exact, y, nullptr, 0, stream);
+}
+
+size_t nq_fp_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n)
+{
+    if (rows < 0 || l < 0 || e < 0 || k < 0 || n < 0 || !gather_shared(rows, l, k, e, n)) return 0;
+    return nqk::gather_group_ws_bytes(rows * l, e, nqk::kGroupChunk);
 }
 
 nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
                            const uint32_t *codes, const uint8_t *scales, const float *global_scales,
                            int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, void *y,
-                           hipStream_t stream)
+                           void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!rhs_idx && rows > 0 && l > 0 && n > 0) {
         g_last_error.clear();
         return fail(NQ_ERR_NULL, "nq_fp_gather_qmm: rhs_idx must be non-null");
     }
     return fp_qmm_impl("nq_fp_gather_qmm", x, x_dt, rows, l, k, codes, scales, global_scales, e, n, mode,
-                       rhs_idx, 1, y, stream);
+                       rhs_idx, 1, y, workspace, workspace_bytes, stream);
 }
 
 const char *nq_status_string(nq_status s)

@@ -160,7 +160,9 @@ hipError_t launch_fp_dequantize(const uint32_t *codes, const uint8_t *scales, in
 // expert idx[i]'s weights (idx null: the only weight matrix; idx[i] >= e:
 // zero rows) and the expert's global scale (gscale null: 1).  tiled: one
 // item, bf16 x, k a multiple of 64 (128 x 128 MFMA tiles); otherwise the
-// matrix-vector kernel in chunks of up to 8 vectors.
+// matrix-vector kernel in chunks of up to 8 vectors.  chunks set: the
+// matrix-vector kernel runs the grouping pass's chunk table instead
+// (launch_gather_groups, kGroupChunk vectors per chunk, max_chunks rows).
 struct FpQmmLaunch {
     const void *x;
     void *y;
@@ -171,6 +173,9 @@ struct FpQmmLaunch {
     int x_dt, mode;
     int64_t items, vpi, n, k, e;
     bool tiled;
+    const uint32_t *perm = nullptr, *nchunks = nullptr;
+    const uint4 *chunks = nullptr;
+    int64_t max_chunks = 0;
 };
 hipError_t launch_fp_qmm(const FpQmmLaunch &a, hipStream_t stream);
 

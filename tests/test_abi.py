@@ -465,11 +465,19 @@ def test_fp_storage_and_gather_argument_errors(lib):
     assert d(out=FAKE2) == NQ_ERR_ALIAS
     assert d(out=FAKE + 2) == NQ_ERR_ALIGN
     assert d(scales=0) == NQ_ERR_NULL
-    gq = lambda **kw: lib.nq_fp_gather_qmm(FAKE, BF16, 4, 1, 64, FAKE2, FAKE2 + 0x100000, kw.get("g", 0),
-                                           kw.get("e", 8), 32, kw.get("mode", 3), kw.get("idx", FAKE2 + 0x200000),
-                                           FAKE2 + 0x300000, None)
+    gq = lambda **kw: lib.nq_fp_gather_qmm(FAKE, BF16, kw.get("rows", 4), 1, 64, FAKE2, FAKE2 + 0x100000,
+                                           kw.get("g", 0), kw.get("e", 8), 32, kw.get("mode", 3),
+                                           kw.get("idx", FAKE2 + 0x200000), FAKE2 + 0x300000,
+                                           kw.get("ws", 0), kw.get("ws_bytes", 0), None)
     assert gq(idx=0) == NQ_ERR_NULL and b"rhs_idx" in lib.nq_last_error()
     assert gq(idx=FAKE2 + 0x200002) == NQ_ERR_ALIGN
     assert gq(e=0) == NQ_ERR_SHAPE
     assert gq(mode=1, g=FAKE2 + 0x400000) == NQ_ERR_QUANT
     assert gq(g=FAKE2 + 0x300000) == NQ_ERR_ALIAS
+    # shared experts are grouped on the device: a workspace is required
+    need = lib.nq_fp_gather_qmm_workspace_bytes(64, 1, 64, 8, 32)
+    assert need > 0 and lib.nq_fp_gather_qmm_workspace_bytes(4, 1, 64, 8, 32) == 0
+    assert gq(rows=64) == NQ_ERR_WORKSPACE and b"workspace" in lib.nq_last_error()
+    assert gq(rows=64, ws=FAKE2 + 0x800000, ws_bytes=need - 1) == NQ_ERR_WORKSPACE
+    assert gq(rows=64, ws=FAKE2 + 0x800008, ws_bytes=need) == NQ_ERR_ALIGN
+    assert gq(rows=64, ws=FAKE2 + 0x300000, ws_bytes=need) == NQ_ERR_ALIAS

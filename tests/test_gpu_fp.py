@@ -192,3 +192,30 @@ def test_prefill_size_sampled_rows():
     rows = np.random.default_rng(15).choice(2048, 16, replace=False)
     ref = F.qmm_f64(x[rows], words, scales, mode)
     assert_rows_close(values(host(y[torch.from_numpy(rows).cuda()])), ref, tolerance(y.dtype), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("l", [1, 3])
+def test_grouped_gather_rows_keep_their_bits(mode, l):
+    # enough rows per expert for the device grouping (workspace in use)
+    e, n, k, rows = 8, 96, 320, 48
+    assert B.nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n) > 0
+    words, scales = codes_case(16, (e, n), k, mode)
+    _, x = synthetic.random_case(16, (1, k), (rows, l, k), 1.0, "bf16")
+    idx = np.random.default_rng(16).integers(0, e + 2, size=rows).astype(np.uint32)   # some past e
+    gsc = np.linspace(0.5, 2.0, e).astype(np.float32) if mode == "nvfp4" else None
+    gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
+    yv = values(host(y))
+    for r in range(rows):
+        if idx[r] >= e:
+            assert not yv[r].any(), r
+    keep = [r for r in range(rows) if idx[r] < e]
+    assert_rows_close(yv[keep], ref[keep], tolerance(y.dtype), mode)
+    xs, ws, ss = dev(x), dev(words), u8(scales)
+    for r in keep:
+        ex = int(idx[r])
+        one = B.nq_fp_qmm(xs[r], ws[ex], ss[ex], mode,
+                          global_scale=None if gt is None else gt[ex:ex + 1], row_exact=True)
+        assert bits_equal(y[r], one), (mode, r)
