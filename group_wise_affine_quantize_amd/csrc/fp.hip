@@ -311,10 +311,14 @@ struct FpGemvParams {
     const uint32_t *perm, *nchunks;
 };
 
-__device__ __forceinline__ float wave_sum(float v)
+__device__ __forceinline__ float wave_sum(float v, int lane)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    v += xor_lane<32>(v, lane);
+    v += xor_lane<16>(v, lane);
+    v += xor_lane<8>(v, lane);
+    v += xor_lane<4>(v, lane);
+    v += xor_lane<2>(v, lane);
+    v += xor_lane<1>(v, lane);
     return v;
 }
 
@@ -425,7 +429,7 @@ __global__ void __launch_bounds__(256) fp_gemv_kernel(FpGemvParams p)
     for (int i = 0; i < MR; ++i)
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            const float t = wave_sum(acc[i][r]);
+            const float t = wave_sum(acc[i][r], lane);
             if (lane == 0 && i < mr && row0 + r < p.n) Elt<XT>::store(y, vec[i] * p.n + row0 + r, t * gsc);
         }
 }
@@ -508,11 +512,138 @@ __global__ void __launch_bounds__(256) fp_gemv_stream_kernel(FpGemvParams p)
                 acc = fmaf(scale_value<MODE>(cur.sc[u][g]), s, acc);
             }
         }
-        const float t = wave_sum(acc) * gsc;
+        const float t = wave_sum(acc, lane) * gsc;
         res = lane == (j & 63) ? t : res;
         if ((j & 63) == 63 || row + W >= p.n) {   // uniform over the wave
             const int64_t r = row0 + ((int64_t)(j & ~63) + lane) * W;
             if (lane <= (j & 63)) Elt<bf16_bits>::store(y, r, res);
+        }
+        cur = nxt;
+    }
+}
+
+// Sum of V values over the 64 lanes, every value through the same pairwise
+// tree as wave_sum (xor 32, 16, ..., 1; own value plus the partner's): at
+// each step a lane keeps half of its values and sends the other half.
+// Afterwards lane L holds value L >> (6 - log2 V).
+template <int V, int OFF = 32>
+__device__ __forceinline__ float wave_sum_many(float (&v)[V], int lane)
+{
+    if constexpr (OFF == 0) {
+        return v[0];
+    } else if constexpr (V > 1) {
+        const bool upper = (lane & OFF) != 0;
+        float h[V / 2];
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) {
+            const float send = pick(upper, v[i], v[i + V / 2]);
+            const float keep = pick(upper, v[i + V / 2], v[i]);
+            h[i] = keep + xor_lane<OFF>(send, lane);
+        }
+        return wave_sum_many<V / 2, OFF / 2>(h, lane);
+    } else {
+        float one[1] = {v[0] + xor_lane<OFF>(v[0], lane)};
+        return wave_sum_many<1, OFF / 2>(one, lane);
+    }
+}
+
+// Grouped gather, bf16 x, K = 2048 (one lane chunk per lane): workgroup row
+// c runs chunk c of the grouping table (up to 8 vectors of one expert).
+// Each wave keeps the chunk's 8 activation chunks in registers and streams
+// weight rows w, w + W, ... of the expert (the next row's loads issued
+// before the current row's arithmetic); the 8 sums of a row go through
+// wave_sum_many, and lane L keeps (vector L / 8, row slot L % 8) so that
+// eight rows leave in one store instruction.  Per vector the arithmetic is
+// fp_gemv_kernel's, so every row keeps its one-row bits.
+template <int MODE>
+__global__ void __launch_bounds__(256) fp_gather_stream_kernel(FpGemvParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS, MR = 8;
+    __shared__ uint4 xl[MR * 256];   // the chunk's 8 activation rows (2048 bf16 each)
+    const int lane = threadIdx.x & 63;
+    const int64_t cidx = blockIdx.y;
+    if (cidx >= *p.nchunks) return;   // uniform over the workgroup
+    const uint4 ch = p.chunks[cidx];
+    const uint32_t ex = ch.x;
+    const int cnt = max((int)ch.z, 1);   // chunks hold at least one vector
+    const int64_t W = (int64_t)gridDim.x * 4;
+    int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    {
+        // x rows of the chunk through LDS, once per workgroup
+        const bf16_bits *xg = static_cast<const bf16_bits *>(p.x);
+        for (int t = threadIdx.x; t < MR * 256; t += 256) {
+            const int i = t >> 8;
+            xl[t] = reinterpret_cast<const uint4 *>(xg + (int64_t)p.perm[ch.y + min(i, cnt - 1)] * 2048)[t & 255];
+        }
+        __syncthreads();
+    }
+    if (row >= p.n) return;
+    bf16_bits *y = static_cast<bf16_bits *>(p.y);
+    const int myv = lane >> 3;                         // the vector this lane stores
+    const int64_t yrow = (int64_t)p.perm[ch.y + min(myv, cnt - 1)];
+    if ((int64_t)ex >= p.e) {                          // no such expert: zero rows
+        for (int64_t r = row + (lane & 7) * W; r < p.n; r += 8 * W)
+            if (myv < cnt) Elt<bf16_bits>::store(y, yrow * p.n + r, 0.0f);
+        return;
+    }
+    const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS;
+    const uint32_t *codes = p.codes + (int64_t)ex * p.n * wpr;
+    const uint8_t *scales = p.scales + (int64_t)ex * p.n * gpr;
+    uint32_t xw[MR][16];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 v = xl[i * 256 + lane * 4 + t];
+            xw[i][4 * t] = v.x, xw[i][4 * t + 1] = v.y, xw[i][4 * t + 2] = v.z, xw[i][4 * t + 3] = v.w;
+        }
+    }
+    struct RowLd {
+        uint32_t wd[BITS];
+        uint32_t sc[NG];
+    };
+    auto load = [&](int64_t r, RowLd &l) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(codes + r * wpr + lane * BITS);
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i) {
+            const uint4 t = src[i];
+            l.wd[4 * i] = t.x, l.wd[4 * i + 1] = t.y, l.wd[4 * i + 2] = t.z, l.wd[4 * i + 3] = t.w;
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) l.sc[g] = scales[r * gpr + lane * NG + g];
+    };
+    const float gsc = p.gscale ? p.gscale[ex] : 1.0f;
+    RowLd cur, nxt;
+    load(row, cur);
+    const int64_t row0 = row;
+    float res = 0.0f;
+    for (int j = 0; row < p.n; row += W, ++j) {
+        load(min(row + W, p.n - 1), nxt);
+        float acc[MR];
+#pragma unroll
+        for (int i = 0; i < MR; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float S = scale_value<MODE>(cur.sc[g]);
+            float sg[MR];
+#pragma unroll
+            for (int i = 0; i < MR; ++i) sg[i] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < GS / 2; ++q) {
+                const int pi = g * (GS / 2) + q;
+                const bf16x2_t e = pair_bf16<MODE>(cur.wd, pi);
+#pragma unroll
+                for (int i = 0; i < MR; ++i)
+                    sg[i] = __builtin_amdgcn_fdot2_f32_bf16(e, __builtin_bit_cast(bf16x2_t, xw[i][pi]), sg[i], false);
+            }
+#pragma unroll
+            for (int i = 0; i < MR; ++i) acc[i] = fmaf(S, sg[i], acc[i]);
+        }
+        const float t = wave_sum_many<MR>(acc, lane) * gsc;   // lane L: vector L / 8
+        res = (lane & 7) == (j & 7) ? t : res;
+        if ((j & 7) == 7 || row + W >= p.n) {              // uniform over the wave
+            const int64_t r = row0 + (int64_t)((j & ~7) + (lane & 7)) * W;
+            if ((lane & 7) <= (j & 7) && myv < cnt) Elt<bf16_bits>::store(y, yrow * p.n + r, res);
         }
         cur = nxt;
     }
@@ -730,23 +861,54 @@ hipError_t gemv_mr(const FpQmmLaunch &a, hipStream_t stream)
     }
 }
 
+// Workgroups of a kernel that stay resident together on one CU (at most
+// `cap`), and the device's CU count; asked once per kernel.
+template <typename K>
+int64_t resident_grid(K kernel, int cap)
+{
+    static const int64_t total = [&] {
+        int per = 1, dev = 0, cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, 0) != hipSuccess || per < 1) per = 1;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        return (int64_t)std::min(per, cap) * cus;
+    }();
+    return total;
+}
+
 // One bf16 row, one weight matrix, K at most 256 lane chunks: the
 // streaming kernel on a whole number of workgroups per CU that stay
-// resident together (4, or 2 with the x registers of 4 chunks a lane).
+// resident together (at most 4).
 template <int MODE, int U>
 hipError_t gemv_stream(const FpQmmLaunch &a, hipStream_t stream)
 {
     FpGemvParams p = {};
     p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
     p.n = a.n, p.k = a.k, p.e = 1;
-    const int64_t wgs = std::min<int64_t>((a.n + 3) / 4, (U >= 4 ? 2 : 4) * 256);
+    const int64_t wgs = std::min<int64_t>((a.n + 3) / 4, resident_grid(fp_gemv_stream_kernel<MODE, U>, 4));
     fp_gemv_stream_kernel<MODE, U><<<dim3((unsigned)wgs), 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+// Grouped gather with bf16 x and K = 2048: the streaming gather kernel,
+// about 32 weight rows per wave.
+template <int MODE>
+hipError_t gather_stream(const FpQmmLaunch &a, hipStream_t stream)
+{
+    FpGemvParams p = {};
+    p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
+    p.n = a.n, p.k = a.k, p.e = a.e;
+    p.chunks = a.chunks, p.perm = a.perm, p.nchunks = a.nchunks;
+    const dim3 grid((unsigned)((a.n + 127) / 128), (unsigned)a.max_chunks);
+    fp_gather_stream_kernel<MODE><<<grid, 256, 0, stream>>>(p);
     return hipGetLastError();
 }
 
 template <int MODE> struct QmmRun {
     static hipError_t run(const FpQmmLaunch &a, hipStream_t stream)
     {
+        if (a.chunks && a.x_dt == DT_BF16 && a.k == 2048 && a.max_chunks <= 65535)
+            return gather_stream<MODE>(a, stream);
         if (!a.tiled && !a.idx && !a.chunks && a.vpi == 1 && a.items == 1 && a.x_dt == DT_BF16 && a.k > 0 &&
             a.k <= 256 * 32) {
             const int64_t c = a.k / 32;

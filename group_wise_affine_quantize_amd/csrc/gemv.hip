@@ -125,28 +125,6 @@ __device__ __forceinline__ float raw_to_f32(uint32_t v)
     else return __uint_as_float(v);
 }
 
-// v from lane (lane ^ OFF) of the wave: DPP quad permutes for 1 and 2,
-// ds_swizzle (xor mode, within 32 lanes) for 4, 8 and 16, ds_bpermute for 32.
-template <int OFF>
-__device__ __forceinline__ float xor_lane(float v, int lane)
-{
-    const int iv = __float_as_int(v);
-    int r;
-    if constexpr (OFF == 1) r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);   // [1,0,3,2]
-    else if constexpr (OFF == 2) r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
-    else if constexpr (OFF == 4 || OFF == 8 || OFF == 16)
-        r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (OFF << 10));
-    else r = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, iv);
-    return __int_as_float(r);
-}
-
-__device__ __forceinline__ float pick(bool c, float a, float b)
-{
-    // c ? a : b, written with integer masks so that it stays a register select
-    const int m = -(int)c;
-    return __int_as_float((__float_as_int(a) & m) | (__float_as_int(b) & ~m));
-}
-
 // Sum of V values over the 64 lanes (V a power of two <= 64).  At each xor
 // step a lane keeps half of its values and sends the other half, so every
 // value goes through the same pairwise tree (xor 32, 16, ..., 1) as a plain

@@ -219,3 +219,27 @@ def test_grouped_gather_rows_keep_their_bits(mode, l):
         one = B.nq_fp_qmm(xs[r], ws[ex], ss[ex], mode,
                           global_scale=None if gt is None else gt[ex:ex + 1], row_exact=True)
         assert bits_equal(y[r], one), (mode, r)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_grouped_gather_moe_shape_streams(mode):
+    # K = 2048 takes the streaming grouped kernel: 64 rows over 8 experts
+    # (some past the last), every row bit-equal to its one-row product
+    e, n, k, rows = 8, 200, 2048, 64
+    words, scales = codes_case(17, (e, n), k, mode)
+    _, x = synthetic.random_case(17, (1, k), (rows, 1, k), 1.0, "bf16")
+    idx = np.random.default_rng(17).integers(0, e + 1, size=rows).astype(np.uint32)
+    gsc = np.linspace(0.25, 4.0, e).astype(np.float32) if mode == "nvfp4" else None
+    gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
+    yv = values(host(y))
+    keep = [r for r in range(rows) if idx[r] < e]
+    assert all(not yv[r].any() for r in range(rows) if idx[r] >= e)
+    assert_rows_close(yv[keep], ref[keep], tolerance(y.dtype), mode)
+    xs, ws, ss = dev(x), dev(words), u8(scales)
+    for r in keep:
+        ex = int(idx[r])
+        one = B.nq_fp_qmm(xs[r], ws[ex], ss[ex], mode,
+                          global_scale=None if gt is None else gt[ex:ex + 1], row_exact=True)
+        assert bits_equal(y[r], one), (mode, r)
