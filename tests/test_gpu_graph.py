@@ -1,5 +1,5 @@
-"""Captured HIP graphs of the product kernels replay the eager results bit
-for bit, replay after replay, with other eager work and synchronisations in
+"""Captured HIP graphs of the product kernels (affine and floating-point
+modes) replay the eager results bit for bit, replay after replay, with other eager work and synchronisations in
 between (the benchmark times graph replays)."""
 import numpy as np
 import pytest
@@ -38,6 +38,10 @@ def test_graph_replays_match_eager():
                                                        torch.bfloat16), dtype=torch.uint8, device="cuda")
     ws_nt = torch.empty(max(1, B.nq_qmm_notrans_workspace_bytes(1, 512, 2048 * 3, gs, bits, torch.bfloat16)),
                         dtype=torch.uint8, device="cuda")
+    wf, sfp = synthetic.random_fp_matrix(18, (1024,), 2048, 4, 16, (0x20, 0x50))
+    wf, sfp = dev(wf), torch.from_numpy(sfp).cuda()
+    gfp = torch.tensor([0.75], dtype=torch.float32, device="cuda")
+    xf = xs[:, :2048].contiguous()
     dy = xs[:1, :512].contiguous()
     dy3 = xs[:3, :512].contiguous()
 
@@ -54,6 +58,10 @@ def test_graph_replays_match_eager():
         "dscales": torch.empty((512, 2048 * 3 // gs), dtype=torch.float32, device="cuda"),
         "dbiases": torch.empty((512, 2048 * 3 // gs), dtype=torch.float32, device="cuda"),
         "dequant": torch.empty((512, 2048 * 3), dtype=torch.bfloat16, device="cuda"),
+        "fp_decode": torch.empty((1, 1024), dtype=torch.bfloat16, device="cuda"),
+        "fp_few": torch.empty((5, 1024), dtype=torch.bfloat16, device="cuda"),
+        "fp_tiled": torch.empty((20, 1024), dtype=torch.bfloat16, device="cuda"),
+        "fp_dequant": torch.empty((1024, 2048), dtype=torch.bfloat16, device="cuda"),
     }
 
     def launch():
@@ -68,6 +76,10 @@ def test_graph_replays_match_eager():
         B.nq_qmm_notrans(dy, c, s, b, gs, bits, y=outs["notrans"], workspace=ws_nt)
         B.nq_qmm_grad_scales_biases(xs[:3], dy3, c, gs, bits, dscales=outs["dscales"], dbiases=outs["dbiases"])
         B.nq_dequantize(c, s, b, gs, bits, out=outs["dequant"])
+        B.nq_fp_qmm(xf[:1], wf, sfp, "nvfp4", global_scale=gfp, y=outs["fp_decode"])
+        B.nq_fp_qmm(xf[:5], wf, sfp, "nvfp4", y=outs["fp_few"])
+        B.nq_fp_qmm(xf, wf, sfp, "nvfp4", global_scale=gfp, y=outs["fp_tiled"])
+        B.nq_fp_dequantize(wf, sfp, "nvfp4", out=outs["fp_dequant"])
 
     launch()
     torch.cuda.synchronize()
