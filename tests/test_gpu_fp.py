@@ -243,3 +243,20 @@ def test_grouped_gather_moe_shape_streams(mode):
         one = B.nq_fp_qmm(xs[r], ws[ex], ss[ex], mode,
                           global_scale=None if gt is None else gt[ex:ex + 1], row_exact=True)
         assert bits_equal(y[r], one), (mode, r)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("n,k", [(8192 + 96, 2048 + 320), (9000, 1024)])
+def test_long_decode_rows_keep_their_bits(mode, n, k):
+    # long one-row products (the streaming decode kernel, several rows per
+    # wave) equal the few-row kernel's rows (row-exact) bit for bit, and the
+    # oracle
+    words, scales = codes_case(19, (n,), k, mode)
+    _, x = synthetic.random_case(19, (1, k), (3, k), 1.0, "bf16")
+    xs, cs, ss = dev(x), dev(words), u8(scales)
+    full = B.nq_fp_qmm(xs, cs, ss, mode, row_exact=True)
+    for i in range(3):
+        one = B.nq_fp_qmm(xs[i:i + 1], cs, ss, mode)
+        assert bits_equal(full[i:i + 1], one), (mode, i)
+    ref = F.qmm_f64(x[:1], words, scales, mode)
+    assert_rows_close(values(host(full[:1])), ref, tolerance(full.dtype), mode)
