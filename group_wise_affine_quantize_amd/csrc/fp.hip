@@ -445,26 +445,13 @@ __global__ void __launch_bounds__(256) fp_gemv_stream_kernel(FpGemvParams p)
 {
     constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
     // x goes through LDS once per workgroup (16-byte pieces), then each
-    // lane keeps its chunks in registers
+    // lane keeps its chunks in registers; the first row's loads are issued
+    // before, so that their latency covers the staging
     __shared__ uint4 xl[64 * U * 4];
     const int lane = threadIdx.x & 63;
     const int64_t W = (int64_t)gridDim.x * 4;
     int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS, chunks = p.k / 32;
-    const uint4 *xg = static_cast<const uint4 *>(p.x);
-    for (int i = threadIdx.x; i < (int)chunks * 4; i += 256) xl[i] = xg[i];
-    __syncthreads();
-    if (row >= p.n) return;
-    uint32_t xw[U][16];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = (int)min((int64_t)lane + 64 * u, chunks - 1);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint4 v = xl[c * 4 + t];
-            xw[u][4 * t] = v.x, xw[u][4 * t + 1] = v.y, xw[u][4 * t + 2] = v.z, xw[u][4 * t + 3] = v.w;
-        }
-    }
     struct RowLd {
         uint32_t wd[U][BITS];
         uint32_t sc[U][NG];
@@ -491,7 +478,21 @@ __global__ void __launch_bounds__(256) fp_gemv_stream_kernel(FpGemvParams p)
     // lane j (iteration j mod 64) and are stored 64 at a time, so no store
     // sits between a row's loads and their wait.
     RowLd cur, nxt;
-    load(row, cur);
+    load(min(row, p.n - 1), cur);
+    const uint4 *xg = static_cast<const uint4 *>(p.x);
+    for (int i = threadIdx.x; i < (int)chunks * 4; i += 256) xl[i] = xg[i];
+    __syncthreads();
+    if (row >= p.n) return;
+    uint32_t xw[U][16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (int)min((int64_t)lane + 64 * u, chunks - 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 v = xl[c * 4 + t];
+            xw[u][4 * t] = v.x, xw[u][4 * t + 1] = v.y, xw[u][4 * t + 2] = v.z, xw[u][4 * t + 3] = v.w;
+        }
+    }
     const int64_t row0 = row;
     float res = 0.0f;
     for (int j = 0; row < p.n; row += W, ++j) {
@@ -568,36 +569,10 @@ __global__ void __launch_bounds__(256) fp_gather_stream_kernel(FpGemvParams p)
     const int cnt = max((int)ch.z, 1);   // chunks hold at least one vector
     const int64_t W = (int64_t)gridDim.x * 4;
     int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    {
-        // x rows of the chunk through LDS, once per workgroup
-        const bf16_bits *xg = static_cast<const bf16_bits *>(p.x);
-        for (int t = threadIdx.x; t < MR * 256; t += 256) {
-            const int i = t >> 8;
-            xl[t] = reinterpret_cast<const uint4 *>(xg + (int64_t)p.perm[ch.y + min(i, cnt - 1)] * 2048)[t & 255];
-        }
-        __syncthreads();
-    }
-    if (row >= p.n) return;
-    bf16_bits *y = static_cast<bf16_bits *>(p.y);
-    const int myv = lane >> 3;                         // the vector this lane stores
-    const int64_t yrow = (int64_t)p.perm[ch.y + min(myv, cnt - 1)];
-    if ((int64_t)ex >= p.e) {                          // no such expert: zero rows
-        for (int64_t r = row + (lane & 7) * W; r < p.n; r += 8 * W)
-            if (myv < cnt) Elt<bf16_bits>::store(y, yrow * p.n + r, 0.0f);
-        return;
-    }
+    const bool live = (int64_t)ex < p.e;               // ex >= e: zero rows
     const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS;
-    const uint32_t *codes = p.codes + (int64_t)ex * p.n * wpr;
-    const uint8_t *scales = p.scales + (int64_t)ex * p.n * gpr;
-    uint32_t xw[MR][16];
-#pragma unroll
-    for (int i = 0; i < MR; ++i) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint4 v = xl[i * 256 + lane * 4 + t];
-            xw[i][4 * t] = v.x, xw[i][4 * t + 1] = v.y, xw[i][4 * t + 2] = v.z, xw[i][4 * t + 3] = v.w;
-        }
-    }
+    const uint32_t *codes = p.codes + (int64_t)(live ? ex : 0u) * p.n * wpr;
+    const uint8_t *scales = p.scales + (int64_t)(live ? ex : 0u) * p.n * gpr;
     struct RowLd {
         uint32_t wd[BITS];
         uint32_t sc[NG];
@@ -612,9 +587,38 @@ __global__ void __launch_bounds__(256) fp_gather_stream_kernel(FpGemvParams p)
 #pragma unroll
         for (int g = 0; g < NG; ++g) l.sc[g] = scales[r * gpr + lane * NG + g];
     };
-    const float gsc = p.gscale ? p.gscale[ex] : 1.0f;
+    // the first row's loads go out before the activation staging, whose
+    // latency they cover
     RowLd cur, nxt;
-    load(row, cur);
+    if (live) load(min(row, p.n - 1), cur);
+    {
+        // x rows of the chunk through LDS, once per workgroup
+        const bf16_bits *xg = static_cast<const bf16_bits *>(p.x);
+        for (int t = threadIdx.x; t < MR * 256; t += 256) {
+            const int i = t >> 8;
+            xl[t] = reinterpret_cast<const uint4 *>(xg + (int64_t)p.perm[ch.y + min(i, cnt - 1)] * 2048)[t & 255];
+        }
+        __syncthreads();
+    }
+    if (row >= p.n) return;
+    bf16_bits *y = static_cast<bf16_bits *>(p.y);
+    const int myv = lane >> 3;                         // the vector this lane stores
+    const int64_t yrow = (int64_t)p.perm[ch.y + min(myv, cnt - 1)];
+    if (!live) {
+        for (int64_t r = row + (lane & 7) * W; r < p.n; r += 8 * W)
+            if (myv < cnt) Elt<bf16_bits>::store(y, yrow * p.n + r, 0.0f);
+        return;
+    }
+    uint32_t xw[MR][16];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 v = xl[i * 256 + lane * 4 + t];
+            xw[i][4 * t] = v.x, xw[i][4 * t + 1] = v.y, xw[i][4 * t + 2] = v.z, xw[i][4 * t + 3] = v.w;
+        }
+    }
+    const float gsc = p.gscale ? p.gscale[ex] : 1.0f;
     const int64_t row0 = row;
     float res = 0.0f;
     for (int j = 0; row < p.n; row += W, ++j) {
