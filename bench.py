@@ -407,11 +407,16 @@ def main():
         gsc = torch.rand(32, dtype=torch.float32, device="cuda") + 0.5
         xg = dev(synthetic.generate("moe_gather")["x"])
         idg = dev(synthetic.generate("moe_gather")["ids"])
-        t = timer.run(lambda i: B.nq_fp_gather_qmm(xg, cg, sg, "nvfp4", idg, global_scales=gsc, y=yg),
-                      steps, 10)
-        put("fp_gather_nvfp4", t, steps, nbytes(cg, sg), "GB/s",
-            {"workload": "x bf16 [512,1,2048], 32 NVFP4 experts W[1408,2048] with global scales, "
-                         "one matrix-vector product per row"})
+        wsf = torch.empty(B.nq_fp_gather_qmm_workspace_bytes(512, 1, 2048, 32, 1408), dtype=torch.uint8,
+                          device="cuda")
+        for tag, rx in (("fp_gather_nvfp4", False), ("fp_gather_nvfp4_row_exact", True)):
+            t = timer.run(lambda i: B.nq_fp_gather_qmm(xg, cg, sg, "nvfp4", idg, global_scales=gsc,
+                                                       row_exact=rx, y=yg, workspace=wsf), steps, 10)
+            put(tag, t, steps, nbytes(cg, sg), "GB/s",
+                {"workload": "x bf16 [512,1,2048], 32 NVFP4 experts W[1408,2048] with global scales, "
+                             "unsorted ids grouped by expert on the device" +
+                             (" (row-exact matrix-vector route)" if rx else " (matrix-core route)"),
+                 "tflops": round(2 * 512 * 1408 * 2048 / (t / steps) / 1e12, 3)})
     out["rows"] = rows
 
     # ---------------------------------------------------------------- measured ceilings

@@ -76,8 +76,8 @@ _SIGNATURES = {
     "nq_fp_dequantize": [_P, _P, _I64, _I64, _I32, _P, _I32, _P],
     "nq_fp_qmm": [_P, _I32, _I64, _I64, _P, _P, _P, _I64, _I32, _I32, _P, _P],
     "nq_fp_gather_qmm_workspace_bytes": [_I64, _I64, _I64, _I64, _I64],
-    "nq_fp_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P, _P, _SZ,
-                         _P],
+    "nq_fp_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _I32, _P, _P,
+                         _SZ, _P],
     "nq_status_string": [_I32],
     "nq_last_error": [],
     "nq_version": [],
@@ -488,12 +488,13 @@ def nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n):
     return load_library().nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n)
 
 
-def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, y=None, workspace=None,
-                     stream=None):
+def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, row_exact=False, y=None,
+                     workspace=None, stream=None):
     """x [rows, l, k], stacked experts codes [e, n, words] and scales [e, n,
     groups], rhs_idx [rows] (uint32 as int32), optional per-expert fp32 global
-    scales [e] (NVFP4) -> y [rows, l, n].  The workspace (bytes from
-    nq_fp_gather_qmm_workspace_bytes) is allocated here when not given."""
+    scales [e] (NVFP4) -> y [rows, l, n]; row_exact keeps every row's
+    one-row bits.  The workspace (bytes from nq_fp_gather_qmm_workspace_bytes)
+    is allocated here when not given."""
     torch = _torch()
     lib = load_library()
     mid, bits, gs = _fp(mode)
@@ -512,6 +513,6 @@ def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, y=None
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_fp_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
-                                _ptr(global_scales), e, n, mid, _ptr(rhs_idx), _ptr(y), _ptr(workspace),
-                                ws_bytes, _stream(stream)))
+                                _ptr(global_scales), e, n, mid, _ptr(rhs_idx), int(bool(row_exact)), _ptr(y),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
     return y

@@ -654,6 +654,117 @@ __global__ void __launch_bounds__(256) fp_gather_stream_kernel(FpGemvParams p)
 }
 
 // ---------------------------------------------------------------- tiled (bf16 MFMA)
+constexpr int kFpLdG = 72;   // LDS row stride (elements) of the gather tiles
+
+// Grouped gather on matrix cores (bf16 x, K a multiple of 64): workgroup
+// (b, c) multiplies chunk c of the grouping table (up to 32 activation
+// vectors of one expert, gathered through perm) by the expert's weight rows
+// [128 b, 128 b + 128).  Per K step of 64 the 32 x rows and the 128 weight
+// rows (as bf16(S * E), exact) are staged in LDS -- thread t stages 8
+// elements of x row t / 8 and 32 weights of row t / 2 -- and wave w runs
+// one 32 x 32 block (its 32 weight rows) with v_mfma_f32_32x32x16_bf16; the
+// next step's loads are issued before the MFMAs.  Each weight tile is
+// converted once for all the chunk's vectors.
+template <int MODE>
+__global__ void __launch_bounds__(256) fp_gather_mfma_kernel(FpGemvParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    __shared__ __attribute__((aligned(16))) bf16_bits xs[32 * kFpLdG];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[128 * kFpLdG];
+    const int64_t cidx = blockIdx.y;
+    if (cidx >= *p.nchunks) return;   // uniform over the workgroup
+    const uint4 ch = p.chunks[cidx];
+    const uint32_t ex = ch.x;
+    const int cnt = max((int)ch.z, 1);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * 128;
+    bf16_bits *y = static_cast<bf16_bits *>(p.y);
+    if ((int64_t)ex >= p.e) {   // no such expert: zero rows
+        for (int t = tid; t < 32 * 128; t += 256) {
+            const int i = t >> 7;
+            const int64_t col = n0 + (t & 127);
+            if (i < (int)ch.z && col < p.n) y[(int64_t)p.perm[ch.y + i] * p.n + col] = 0;
+        }
+        return;
+    }
+    const int64_t wpr = p.k * BITS / 32, gpr = p.k / GS;
+    const uint32_t *codes = p.codes + (int64_t)ex * p.n * wpr;
+    const uint8_t *scales = p.scales + (int64_t)ex * p.n * gpr;
+    const bf16_bits *x = static_cast<const bf16_bits *>(p.x);
+    const int xr = tid >> 3, xq = tid & 7;                   // x loader: row, 8-element piece
+    const int64_t xrow = (int64_t)p.perm[ch.y + min(xr, cnt - 1)];
+    const int wrl = tid >> 1, whalf = tid & 1;               // weight loader: row, 32-element half
+    const int64_t wr = n0 + wrl, wrc = min(wr, p.n - 1);
+    const int nsteps = (int)(p.k / 64);
+    struct Ld {
+        uint4 x;
+        uint4 c[BITS / 4];
+        uint32_t s[NG];
+    };
+    auto load = [&](int step, Ld &l) {
+        const int64_t k0 = (int64_t)step * 64;
+        l.x = *reinterpret_cast<const uint4 *>(x + xrow * p.k + k0 + 8 * xq);
+        const int64_t e0 = k0 + 32 * whalf;
+        const uint4 *csrc = reinterpret_cast<const uint4 *>(codes + wrc * wpr + e0 * BITS / 32);
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u) l.c[u] = csrc[u];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) l.s[g] = scales[wrc * gpr + e0 / GS + g];
+    };
+    auto store = [&](const Ld &l) {
+        *reinterpret_cast<uint4 *>(xs + xr * kFpLdG + 8 * xq) = l.x;
+        uint32_t wd[BITS];
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u)
+            wd[4 * u] = l.c[u].x, wd[4 * u + 1] = l.c[u].y, wd[4 * u + 2] = l.c[u].z, wd[4 * u + 3] = l.c[u].w;
+        uint32_t o[16];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float S = scale_value<MODE>(l.s[g]);
+#pragma unroll
+            for (int q = 0; q < GS / 2; ++q) {
+                const int pi = g * (GS / 2) + q;
+                const f32x2_t e = pair_f32<MODE>(wd, pi);
+                const f32x2_t v = {S * e[0], S * e[1]};
+                o[pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+            }
+        }
+        uint4 *wdst = reinterpret_cast<uint4 *>(ws + wrl * kFpLdG + 32 * whalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            wdst[u] = wr < p.n ? make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3])
+                               : make_uint4(0u, 0u, 0u, 0u);
+    };
+
+    f32x16_t acc = {};
+    Ld cur, nxt;
+    if (nsteps > 0) load(0, cur);
+    for (int step = 0; step < nsteps; ++step) {
+        store(cur);
+        __syncthreads();
+        if (step + 1 < nsteps) load(step + 1, nxt);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = ks * 16 + 8 * (lane >> 5);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(xs + (lane & 31) * kFpLdG + kk);
+            const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(ws + (wave * 32 + (lane & 31)) * kFpLdG + kk);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
+        __syncthreads();
+        cur = nxt;
+    }
+    // lane l holds weight row (column of y) l % 32 of the wave's block and
+    // vectors 8 (v / 4) + 4 (l / 32) + v % 4
+    const float gsc = p.gscale ? p.gscale[ex] : 1.0f;
+    const int64_t col = n0 + wave * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (i < (int)ch.z && col < p.n)
+            y[(int64_t)p.perm[ch.y + i] * p.n + col] = (bf16_bits)f32_to_bf16(acc[v] * gsc);
+    }
+}
+
 // 128 x 128 tiles of y, four waves of 64 x 64 (2 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16), K steps of 64.  Thread t stages row t / 2 of
 // the x tile and of the weight tile, 32 elements at k = 32 (t % 2): x as it
@@ -908,9 +1019,23 @@ hipError_t gather_stream(const FpQmmLaunch &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Grouped gather on matrix cores: 128 weight rows per workgroup, one
+// workgroup row per chunk of up to 32 vectors.
+template <int MODE>
+hipError_t gather_mfma(const FpQmmLaunch &a, hipStream_t stream)
+{
+    FpGemvParams p = {};
+    p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
+    p.n = a.n, p.k = a.k, p.e = a.e;
+    p.chunks = a.chunks, p.perm = a.perm, p.nchunks = a.nchunks;
+    fp_gather_mfma_kernel<MODE><<<dim3((unsigned)((a.n + 127) / 128), (unsigned)a.max_chunks), 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
 template <int MODE> struct QmmRun {
     static hipError_t run(const FpQmmLaunch &a, hipStream_t stream)
     {
+        if (a.chunks && a.mfma) return gather_mfma<MODE>(a, stream);
         if (a.chunks && a.x_dt == DT_BF16 && a.k == 2048 && a.max_chunks <= 65535)
             return gather_stream<MODE>(a, stream);
         if (!a.tiled && !a.idx && !a.chunks && a.vpi == 1 && a.items == 1 && a.x_dt == DT_BF16 && a.k > 0 &&

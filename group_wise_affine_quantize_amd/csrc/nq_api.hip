@@ -885,14 +885,16 @@ static nq_status fp_qmm_impl(const char *op, const void *x, nq_dtype x_dt, int64
     a.tiled = idx == nullptr && !row_exact && vpi > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && k % 64 == 0 &&
               vpi <= (int64_t)65535 * 128;   // row tiles along grid.y
     if (grouped) {
-        hipError_t err = nqk::launch_gather_groups(idx, nullptr, items, items, vpi, e, nqk::kGroupChunk,
-                                                   workspace, stream);
+        // matrix cores unless every row must keep its one-row bits
+        a.mfma = !row_exact && x_dt == NQ_BF16 && k % 64 == 0;
+        const int chunk = a.mfma ? nqk::kGroupChunkMfma : nqk::kGroupChunk;
+        hipError_t err = nqk::launch_gather_groups(idx, nullptr, items, items, vpi, e, chunk, workspace, stream);
         if (err != hipSuccess) return check_launch(op, err);
         const int64_t v = items * vpi;
         uint32_t *ws = static_cast<uint32_t *>(workspace);
         a.perm = ws, a.nchunks = ws + v;
         a.chunks = reinterpret_cast<const uint4 *>(ws + ((v + 1 + 3) & ~(int64_t)3));
-        a.max_chunks = nqk::gather_group_max_chunks(v, e, nqk::kGroupChunk);
+        a.max_chunks = nqk::gather_group_max_chunks(v, e, chunk);
     }
     return check_launch(op, nqk::launch_fp_qmm(a, stream));
 }
@@ -917,15 +919,15 @@ size_t nq_fp_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int6
 
 nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
                            const uint32_t *codes, const uint8_t *scales, const float *global_scales,
-                           int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, void *y,
-                           void *workspace, size_t workspace_bytes, hipStream_t stream)
+                           int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, int32_t row_exact,
+                           void *y, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!rhs_idx && rows > 0 && l > 0 && n > 0) {
         g_last_error.clear();
         return fail(NQ_ERR_NULL, "nq_fp_gather_qmm: rhs_idx must be non-null");
     }
     return fp_qmm_impl("nq_fp_gather_qmm", x, x_dt, rows, l, k, codes, scales, global_scales, e, n, mode,
-                       rhs_idx, 1, y, workspace, workspace_bytes, stream);
+                       rhs_idx, row_exact, y, workspace, workspace_bytes, stream);
 }
 
 const char *nq_status_string(nq_status s)

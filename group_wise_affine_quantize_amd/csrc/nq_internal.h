@@ -176,6 +176,7 @@ struct FpQmmLaunch {
     const uint32_t *perm = nullptr, *nchunks = nullptr;
     const uint4 *chunks = nullptr;
     int64_t max_chunks = 0;
+    bool mfma = false;   // chunks of up to kGroupChunkMfma vectors on matrix cores (bf16 x, k % 64 == 0)
 };
 hipError_t launch_fp_qmm(const FpQmmLaunch &a, hipStream_t stream);
 

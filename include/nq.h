@@ -355,22 +355,27 @@ nq_status nq_fp_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const ui
  * several vectors (rows * l >= 16 and >= 4 * e, e <= 4096 -- the thresholds
  * of the "Mixture of experts" section), when the vectors are grouped by
  * expert on the device and each expert's weights are read once per chunk of
- * up to 8 vectors. */
+ * vectors (either route). */
 size_t nq_fp_gather_qmm_workspace_bytes(int64_t rows, int64_t l, int64_t k, int64_t e, int64_t n);
 
 /* gather_qmm in a floating-point mode ("Mixture of experts" section): x
  * [rows, l, k]; experts codes [e, n, k*bits/32] and scales [e, n, k/group];
  * global_scales [e] fp32 (NVFP4 only; null: 1); rhs_idx [rows] uint32.
  * y [rows, l, n]: y[r, j, :] = x[r, j, :] . (g[i] * w_hat[i])^T with i =
- * rhs_idx[r]; rhs_idx[r] >= e gives an all-zero row.  Grouped or not,
- * every row is bit-equal to nq_fp_qmm(row_exact = 1) of x[r] with expert
- * i's weights and global scale.  workspace: at least
+ * rhs_idx[r]; rhs_idx[r] >= e gives an all-zero row.  Routes: few vectors,
+ * matrix-vector products per row; shared experts (see the workspace
+ * function), the vectors grouped by expert on the device, then with
+ * row_exact = 0, bf16 x and k a multiple of 64 bf16-MFMA tiles over chunks
+ * of up to 32 vectors (the affine products' tolerance), otherwise the
+ * matrix-vector kernel over chunks of up to 8.  With row_exact = 1 every
+ * row is bit-equal to nq_fp_qmm(row_exact = 1) of x[r] with expert i's
+ * weights and global scale.  workspace: at least
  * nq_fp_gather_qmm_workspace_bytes (16-byte aligned; NQ_ERR_WORKSPACE if
  * short). */
 nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
                            const uint32_t *codes, const uint8_t *scales, const float *global_scales,
-                           int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, void *y,
-                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+                           int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, int32_t row_exact,
+                           void *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- errors */
 

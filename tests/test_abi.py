@@ -467,7 +467,7 @@ def test_fp_storage_and_gather_argument_errors(lib):
     assert d(scales=0) == NQ_ERR_NULL
     gq = lambda **kw: lib.nq_fp_gather_qmm(FAKE, BF16, kw.get("rows", 4), 1, 64, FAKE2, FAKE2 + 0x100000,
                                            kw.get("g", 0), kw.get("e", 8), 32, kw.get("mode", 3),
-                                           kw.get("idx", FAKE2 + 0x200000), FAKE2 + 0x300000,
+                                           kw.get("idx", FAKE2 + 0x200000), 0, FAKE2 + 0x300000,
                                            kw.get("ws", 0), kw.get("ws_bytes", 0), None)
     assert gq(idx=0) == NQ_ERR_NULL and b"rhs_idx" in lib.nq_last_error()
     assert gq(idx=FAKE2 + 0x200002) == NQ_ERR_ALIGN

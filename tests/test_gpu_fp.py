@@ -147,7 +147,8 @@ def test_gather_rows_match_their_expert(mode):
     idx = np.array([3, 0, 0, 1, 9, 2, 3, 3, 1, 0], np.uint32)          # 9: no such expert
     gsc = np.array([0.5, 1.25, 2.0, 0.75], np.float32) if mode == "nvfp4" else None
     gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
-    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt,
+                           row_exact=True)
     ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
     assert not values(host(y[4])).any()
     keep = [r for r in range(rows) if idx[r] < e]
@@ -205,7 +206,8 @@ def test_grouped_gather_rows_keep_their_bits(mode, l):
     idx = np.random.default_rng(16).integers(0, e + 2, size=rows).astype(np.uint32)   # some past e
     gsc = np.linspace(0.5, 2.0, e).astype(np.float32) if mode == "nvfp4" else None
     gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
-    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt,
+                           row_exact=True)
     ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
     yv = values(host(y))
     for r in range(rows):
@@ -231,7 +233,8 @@ def test_grouped_gather_moe_shape_streams(mode):
     idx = np.random.default_rng(17).integers(0, e + 1, size=rows).astype(np.uint32)
     gsc = np.linspace(0.25, 4.0, e).astype(np.float32) if mode == "nvfp4" else None
     gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
-    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt,
+                           row_exact=True)
     ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
     yv = values(host(y))
     keep = [r for r in range(rows) if idx[r] < e]
@@ -260,3 +263,37 @@ def test_long_decode_rows_keep_their_bits(mode, n, k):
         assert bits_equal(full[i:i + 1], one), (mode, i)
     ref = F.qmm_f64(x[:1], words, scales, mode)
     assert_rows_close(values(host(full[:1])), ref, tolerance(full.dtype), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("l,k", [(1, 320), (2, 448)])
+def test_gather_matrix_core_route(mode, l, k):
+    # shared experts, bf16 x, k % 64 == 0, row_exact off: MFMA tiles over
+    # chunks of up to 32 vectors (ragged n, ids past the last expert)
+    e, n, rows = 8, 200, 80
+    words, scales = codes_case(20 + l, (e, n), k, mode)
+    _, x = synthetic.random_case(20 + l, (1, k), (rows, l, k), 1.0, "bf16")
+    idx = np.random.default_rng(20 + l).integers(0, e + 1, size=rows).astype(np.uint32)
+    gsc = np.linspace(0.5, 3.0, e).astype(np.float32) if mode == "nvfp4" else None
+    gt = torch.from_numpy(gsc).cuda() if gsc is not None else None
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx), global_scales=gt)
+    ref = F.gather_qmm_f64(x, words, scales, mode, idx, gsc)
+    yv = values(host(y))
+    assert all(not yv[r].any() for r in range(rows) if idx[r] >= e)
+    keep = [r for r in range(rows) if idx[r] < e]
+    assert_rows_close(yv[keep], ref[keep], tolerance(y.dtype), mode)
+
+
+def test_gather_matrix_core_moe_shape():
+    # 512 rows over 32 NVFP4 experts [1408, 2048] with global scales; 24
+    # sampled rows against the oracle
+    mode, e, n, k, rows = "nvfp4", 32, 1408, 2048, 512
+    words, scales = codes_case(22, (e, n), k, mode)
+    _, x = synthetic.random_case(22, (1, k), (rows, 1, k), 1.0, "bf16")
+    idx = np.random.default_rng(22).integers(0, e, size=rows).astype(np.uint32)
+    gsc = np.linspace(0.5, 2.0, e).astype(np.float32)
+    y = B.nq_fp_gather_qmm(dev(x), dev(words), u8(scales), mode, dev(idx),
+                           global_scales=torch.from_numpy(gsc).cuda())
+    pick = np.random.default_rng(22).choice(rows, 24, replace=False)
+    ref = F.gather_qmm_f64(x[pick], words, scales, mode, idx[pick], gsc)
+    assert_rows_close(values(host(y[torch.from_numpy(pick).cuda()])), ref, tolerance(y.dtype), mode)
