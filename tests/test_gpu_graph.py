@@ -42,6 +42,14 @@ def test_graph_replays_match_eager():
     wf, sfp = dev(wf), torch.from_numpy(sfp).cuda()
     gfp = torch.tensor([0.75], dtype=torch.float32, device="cuda")
     xf = xs[:, :2048].contiguous()
+    # floating-point gathers with shared experts: matrix-core and row-exact
+    # routes behind the device grouping pass
+    wfe, sfe = synthetic.random_fp_matrix(19, (4, 256), 2048, 4, 32, (120, 134))
+    wfe, sfe = dev(wfe), torch.from_numpy(sfe).cuda()
+    idf = dev(np.random.default_rng(19).integers(0, 5, size=20).astype(np.uint32))
+    xfg = xf.view(20, 1, 2048)
+    ws_f = torch.empty(B.nq_fp_gather_qmm_workspace_bytes(20, 1, 2048, 4, 256), dtype=torch.uint8,
+                       device="cuda")
     dy = xs[:1, :512].contiguous()
     dy3 = xs[:3, :512].contiguous()
 
@@ -62,6 +70,8 @@ def test_graph_replays_match_eager():
         "fp_few": torch.empty((5, 1024), dtype=torch.bfloat16, device="cuda"),
         "fp_tiled": torch.empty((20, 1024), dtype=torch.bfloat16, device="cuda"),
         "fp_dequant": torch.empty((1024, 2048), dtype=torch.bfloat16, device="cuda"),
+        "fp_gather": torch.empty((20, 1, 256), dtype=torch.bfloat16, device="cuda"),
+        "fp_gather_exact": torch.empty((20, 1, 256), dtype=torch.bfloat16, device="cuda"),
     }
 
     def launch():
@@ -80,6 +90,9 @@ def test_graph_replays_match_eager():
         B.nq_fp_qmm(xf[:5], wf, sfp, "nvfp4", y=outs["fp_few"])
         B.nq_fp_qmm(xf, wf, sfp, "nvfp4", global_scale=gfp, y=outs["fp_tiled"])
         B.nq_fp_dequantize(wf, sfp, "nvfp4", out=outs["fp_dequant"])
+        B.nq_fp_gather_qmm(xfg, wfe, sfe, "mxfp4", idf, y=outs["fp_gather"], workspace=ws_f)
+        B.nq_fp_gather_qmm(xfg, wfe, sfe, "mxfp4", idf, row_exact=True, y=outs["fp_gather_exact"],
+                           workspace=ws_f)
 
     launch()
     torch.cuda.synchronize()
