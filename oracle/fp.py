@@ -236,3 +236,14 @@ def gather_qmm_f64(x, codes, scales, mode, idx, global_scales=None):
         g = None if global_scales is None else global_scales[ex]
         y[r] = xv[r] @ dequantize_f64(codes[ex], scales[ex], mode, k, g).T
     return y
+
+
+def qmm_nt_f64(x, codes, scales, mode, global_scale=None):
+    """Product with the weights as stored ("transpose = false"): y = x .
+    w_hat for a quantized matrix w_hat [ni, nc] whose groups run along nc
+    (codes [ni, nc * bits / 32], scales [ni, nc / group]); x [m, ni].  With
+    the forward weights this is the derivative for the activations."""
+    xv = _as_f32(x).astype(np.float64)
+    nc = scales.shape[-1] * mode_info(mode)[2]
+    return xv @ dequantize_f64(codes, scales, mode, nc, global_scale)
+

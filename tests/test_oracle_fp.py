@@ -281,3 +281,26 @@ def test_dequantize_nan_is_canonical_in_both_outputs():
         assert b[0, 0] == 0x7FC0
     f = F.dequantize(cq, np.array([[127]], np.uint8), "mxfp8", 32, "f32")
     assert f[0, 1] == -1.0
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8", "nvfp4"])
+def test_weights_as_stored_adjoint_of_the_product(mode):
+    # <dy, x . w_hat^T> = <dy . w_hat, x> for the same quantized matrix: a
+    # transposed operand or a group axis along the wrong dimension fails it;
+    # plus a brute-force entry
+    _, bits, gs, _ = F.mode_info(mode)
+    rng = np.random.default_rng(13)
+    n, k, m = 6, 2 * gs, 3
+    cq, sq = F.quantize(rng.standard_normal((n, k)).astype(np.float32), mode)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    dy = rng.standard_normal((m, n)).astype(np.float32)
+    fwd = F.qmm_f64(x, cq, sq, mode, 0.5)
+    dx = F.qmm_nt_f64(dy, cq, sq, mode, 0.5)
+    assert dx.shape == (m, k)
+    lhs = float(np.sum(dy.astype(np.float64) * fwd))
+    rhs = float(np.sum(dx * x.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    E = F.decode(F.unpack(cq, bits, k), "e2m1" if bits == 4 else "e4m3")
+    S = F.decode(sq, "e8m0" if mode != "nvfp4" else "e4m3")
+    want = sum(float(dy[1, i]) * 0.5 * float(S[i, 5 // gs]) * float(E[i, 5]) for i in range(n))
+    assert abs(dx[1, 5] - want) <= 1e-12 * max(1.0, abs(want))
