@@ -393,6 +393,21 @@ def main():
             put(f"fp_decode_{mode}", t, steps, nbytes(*qm), "GB/s",
                 {"workload": f"x bf16 [1,4096] . W[14336,4096]^T {mode}"})
             if mode == "mxfp4":
+                # the derivative for the activations through these weights (as stored)
+                dyf = dev(synthetic.random_case(7, (1, 1), (1, 14336), 1.0, "f32", "bf16")[1])
+                dxf = torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda")
+                wsf = torch.empty(B.nq_fp_qmm_notrans_workspace_bytes(1, 14336, 4096, mode, torch.bfloat16),
+                                  dtype=torch.uint8, device="cuda")
+                t = timer.run(lambda i: B.nq_fp_qmm_notrans(dyf, *cps[i % len(cps)], mode, y=dxf, workspace=wsf),
+                              steps, 10)
+                put("fp_dx_decode_mxfp4", t, steps, nbytes(*qm), "GB/s",
+                    {"workload": "dx bf16 [1,4096] = dy [1,14336] . W[14336,4096] mxfp4 (weights as stored)"})
+                dyp = dev(synthetic.random_case(8, (1, 1), (2048, 14336), 1.0, "f32", "bf16")[1])
+                dxp = torch.empty((2048, 4096), dtype=torch.bfloat16, device="cuda")
+                tp = timer.run(lambda i: B.nq_fp_qmm_notrans(dyp, *qm, mode, y=dxp), max(2, steps // 20), 2)
+                put("fp_dx_prefill_mxfp4", tp, max(2, steps // 20), 2 * 2048 * 14336 * 4096, "TFLOP/s",
+                    {"workload": "dx bf16 [2048,4096] = dy [2048,14336] . W[14336,4096] mxfp4 (128x128 tiles)"})
+                del dyp, dxp
                 t = timer.run(lambda i: B.nq_fp_dequantize(*cps[i % len(cps)], mode, out=wout), steps, 10)
                 put("fp_dequantize_mxfp4", t, steps, nbytes(wout) + nbytes(*qm), "GB/s",
                     {"workload": "MXFP4 [14336,4096] -> bf16"})

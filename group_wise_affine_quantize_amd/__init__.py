@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     nq_fp_gather_qmm,
     nq_fp_gather_qmm_workspace_bytes,
     nq_fp_qmm,
+    nq_fp_qmm_notrans,
+    nq_fp_qmm_notrans_workspace_bytes,
     nq_fp_quantize,
     nq_gather_qmm,
     nq_gather_qmm_row_exact,

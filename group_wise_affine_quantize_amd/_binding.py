@@ -78,12 +78,15 @@ _SIGNATURES = {
     "nq_fp_gather_qmm_workspace_bytes": [_I64, _I64, _I64, _I64, _I64],
     "nq_fp_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _I32, _P, _P,
                          _SZ, _P],
+    "nq_fp_qmm_notrans_workspace_bytes": [_I64, _I64, _I64, _I32, _I32, _I32],
+    "nq_fp_qmm_notrans": [_P, _I32, _I64, _I64, _P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P],
     "nq_status_string": [_I32],
     "nq_last_error": [],
     "nq_version": [],
 }
 _RESTYPES = {"nq_qmm_workspace_bytes": _SZ, "nq_gather_qmm_workspace_bytes": _SZ,
              "nq_qmm_notrans_workspace_bytes": _SZ, "nq_fp_gather_qmm_workspace_bytes": _SZ,
+             "nq_fp_qmm_notrans_workspace_bytes": _SZ,
              "nq_status_string": ctypes.c_char_p, "nq_last_error": ctypes.c_char_p,
              "nq_version": ctypes.c_char_p}
 
@@ -516,3 +519,38 @@ def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, row_ex
                                 _ptr(global_scales), e, n, mid, _ptr(rhs_idx), int(bool(row_exact)), _ptr(y),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
     return y
+
+
+def nq_fp_qmm_notrans_workspace_bytes(m, ni, nc, mode, x_dtype, row_exact=False):
+    torch = _torch()
+    xd = NQ_F32 if x_dtype == torch.float32 else NQ_BF16
+    return load_library().nq_fp_qmm_notrans_workspace_bytes(m, ni, nc, _fp(mode)[0], xd,
+                                                            int(bool(row_exact)))
+
+
+def nq_fp_qmm_notrans(x, codes, scales, mode, global_scale=None, row_exact=False, y=None, workspace=None,
+                      stream=None):
+    """y [m, nc] = x [m, ni] times the quantized matrix [ni, nc] as stored
+    (codes [ni, nc*bits/32], scales [ni, nc/group]); with the forward weights
+    this is the derivative for the activations.  The workspace is allocated
+    here when not given."""
+    torch = _torch()
+    lib = load_library()
+    mid, bits, gs = _fp(mode)
+    for name, t in (("x", x), ("codes", codes), ("scales", scales)):
+        _contig(name, t)
+    m, ni = x.shape
+    nc = scales.shape[1] * gs
+    if scales.shape[0] != ni or codes.shape != (ni, words_per_row(nc, bits)):
+        raise ValueError("codes/scales shapes do not match x and the mode")
+    if y is None:
+        y = torch.empty((m, nc), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        need = lib.nq_fp_qmm_notrans_workspace_bytes(m, ni, nc, mid, _dt(x), int(bool(row_exact)))
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.nq_fp_qmm_notrans(_ptr(x), _dt(x), m, ni, _ptr(codes), _ptr(scales), _ptr(global_scale), nc,
+                                 mid, int(bool(row_exact)), _ptr(y), _ptr(workspace), ws_bytes,
+                                 _stream(stream)))
+    return y
+

@@ -899,6 +899,244 @@ __global__ void __launch_bounds__(256) fp_tiled_kernel(FpTiledParams p)
         }
 }
 
+// ---------------------------------------------------------------- weights as stored
+// y[m, c] = x[m, i] . (g w_hat)[i, c] for a quantized matrix w_hat [ni, nc]
+// whose groups run along c (the derivative for the activations with the
+// forward weights).  Few rows: the rows of w_hat are cut into ranges that
+// depend only on (ni, nc); workgroup (b, r) covers the 64 lane chunks
+// [64 b, 64 b + 64) of a row (32 columns each) over range r, wave w taking
+// the range's rows w, w + 4, ... in increasing order; per row a lane forms
+// x[m, i] * S once and adds it times each element to its 32 column sums.
+// The waves' sums are added in LDS in wave order, and a second kernel adds
+// the ranges in order, so a row's bits do not depend on the other rows.
+struct FpNtParams {
+    const void *x;
+    void *y;
+    float *part;
+    const uint32_t *codes;
+    const uint8_t *scales;
+    const float *gscale;
+    int64_t m0, mr, ni, nc, rows_per_range;
+    int ranges;
+};
+
+template <int MODE, typename XT>
+__global__ void __launch_bounds__(256) fp_nt_partial_kernel(FpNtParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS, MR = kFpNtRows, U = 4;
+    __shared__ float red[3][MR][64 * 33];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t chunks = p.nc / 32, chunk = (int64_t)blockIdx.x * 64 + lane;
+    const bool ok = chunk < chunks;
+    const int64_t cc = ok ? chunk : 0;
+    const int64_t i0 = (int64_t)blockIdx.y * p.rows_per_range, i1 = min(i0 + p.rows_per_range, p.ni);
+    const int64_t wpr = p.nc * BITS / 32, gpr = p.nc / GS;
+    const XT *x = static_cast<const XT *>(p.x);
+    float acc[MR][32];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < 32; ++j) acc[m][j] = 0.0f;
+    for (int64_t ib = i0 + wave; ib < i1; ib += 4 * U) {
+        // U rows' loads first (rows past the range re-read its last row and
+        // are not added)
+        uint32_t wd[U][BITS];
+        uint32_t sc[U][NG];
+        float xv[U][MR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = min(ib + 4 * u, i1 - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(p.codes + i * wpr + cc * BITS);
+#pragma unroll
+            for (int q = 0; q < BITS / 4; ++q) {
+                const uint4 t = src[q];
+                wd[u][4 * q] = t.x, wd[u][4 * q + 1] = t.y, wd[u][4 * q + 2] = t.z, wd[u][4 * q + 3] = t.w;
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) sc[u][g] = p.scales[i * gpr + cc * NG + g];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) xv[u][m] = Elt<XT>::load(x, (p.m0 + min((int64_t)m, p.mr - 1)) * p.ni + i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (ib + 4 * u >= i1) break;   // uniform over the wave
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const float S = scale_value<MODE>(sc[u][g]);
+                float xs[MR];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) xs[m] = xv[u][m] * S;
+#pragma unroll
+                for (int q = 0; q < GS / 2; ++q) {
+                    const int pi = g * (GS / 2) + q;
+                    const f32x2_t e = pair_f32<MODE>(wd[u], pi);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        acc[m][2 * pi] = fmaf(xs[m], e[0], acc[m][2 * pi]);
+                        acc[m][2 * pi + 1] = fmaf(xs[m], e[1], acc[m][2 * pi + 1]);
+                    }
+                }
+            }
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int j = 0; j < 32; ++j) red[wave - 1][m][lane * 33 + j] = acc[m][j];
+    }
+    __syncthreads();
+    if (wave == 0 && ok) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= p.mr) break;
+            float o[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                o[j] = ((acc[m][j] + red[0][m][lane * 33 + j]) + red[1][m][lane * 33 + j]) + red[2][m][lane * 33 + j];
+            uint4 *dst = reinterpret_cast<uint4 *>(p.part + ((int64_t)blockIdx.y * MR + m) * p.nc + chunk * 32);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dst[t] = make_uint4(__float_as_uint(o[4 * t]), __float_as_uint(o[4 * t + 1]),
+                                    __float_as_uint(o[4 * t + 2]), __float_as_uint(o[4 * t + 3]));
+        }
+    }
+}
+
+// y[m0 + m, c] = g * (sum over ranges r in increasing order of part[r][m][c])
+template <typename XT>
+__global__ void __launch_bounds__(256) fp_nt_reduce_kernel(FpNtParams p)
+{
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y;
+    if (col >= p.nc) return;
+    const float *src = p.part + (int64_t)m * p.nc + col;
+    const int64_t stride = (int64_t)kFpNtRows * p.nc;
+    float s = 0.0f;
+    int r = 0;
+    for (; r + 8 <= p.ranges; r += 8) {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = src[(int64_t)(r + t) * stride];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s += v[t];
+    }
+    for (; r < p.ranges; ++r) s += src[(int64_t)r * stride];
+    const float g = p.gscale ? *p.gscale : 1.0f;
+    Elt<XT>::store(static_cast<XT *>(p.y), (p.m0 + m) * p.nc + col, s * g);
+}
+
+// Many bf16 rows: 128 x 128 tiles of y with bf16 MFMA, K steps of 64 rows i
+// of w_hat; thread t stages 32 elements of x row t / 2 and the 32 columns
+// 32 (t % 4) .. + 31 of w_hat row t / 4 (one lane chunk), converted to
+// bf16(S * E) and written down LDS columns, so that a B operand reads 8
+// consecutive i of one column.  Column c starts at c * 72 + 16 ((c / 32) % 4)
+// elements, which keeps the 2-byte writes of 16 rows x 4 column groups on
+// distinct banks.  ni is a multiple of 64.
+__device__ __forceinline__ int fp_nt_wcol(int c) { return c * 72 + 16 * ((c >> 5) & 3); }
+
+template <int MODE>
+__global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
+{
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    __shared__ __attribute__((aligned(16))) bf16_bits xs[128 * 72];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[128 * 72 + 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+    const int lrow = tid >> 1, lhalf = tid & 1;
+    const int64_t xm = m0 + lrow, xmc = min(xm, p.mr - 1);
+    const int wrow = tid >> 2, wcol = 32 * (tid & 3);
+    const int64_t cb = c0 + wcol;
+    const bool wok = cb < p.nc;
+    const int64_t cbc = wok ? cb : 0;
+    const int64_t wpr = p.nc * BITS / 32, gpr = p.nc / GS;
+    const bf16_bits *x = static_cast<const bf16_bits *>(p.x);
+    const int nsteps = (int)(p.ni / 64);
+    struct Ld {
+        uint4 x[4];
+        uint4 c[BITS / 4];
+        uint32_t s[NG];
+    };
+    auto load = [&](int step, Ld &l) {
+        const int64_t i0 = (int64_t)step * 64;
+        const uint4 *xsrc = reinterpret_cast<const uint4 *>(x + xmc * p.ni + i0 + 32 * lhalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) l.x[u] = xsrc[u];
+        const int64_t i = i0 + wrow;
+        const uint4 *csrc = reinterpret_cast<const uint4 *>(p.codes + i * wpr + cbc * BITS / 32);
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u) l.c[u] = csrc[u];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) l.s[g] = p.scales[i * gpr + cbc / GS + g];
+    };
+    auto store = [&](const Ld &l) {
+        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * 72 + 32 * lhalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xd[u] = xm < p.mr ? l.x[u] : make_uint4(0u, 0u, 0u, 0u);
+        uint32_t wd[BITS];
+#pragma unroll
+        for (int u = 0; u < BITS / 4; ++u)
+            wd[4 * u] = l.c[u].x, wd[4 * u + 1] = l.c[u].y, wd[4 * u + 2] = l.c[u].z, wd[4 * u + 3] = l.c[u].w;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float S = scale_value<MODE>(l.s[g]);
+#pragma unroll
+            for (int q = 0; q < GS / 2; ++q) {
+                const int pi = g * (GS / 2) + q;
+                const f32x2_t e = pair_f32<MODE>(wd, pi);
+                const f32x2_t v = {wok ? S * e[0] : 0.0f, wok ? S * e[1] : 0.0f};
+                const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                ws[fp_nt_wcol(wcol + 2 * pi) + wrow] = (bf16_bits)(h & 0xffffu);
+                ws[fp_nt_wcol(wcol + 2 * pi + 1) + wrow] = (bf16_bits)(h >> 16);
+            }
+        }
+    };
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    Ld cur, nxt;
+    if (nsteps > 0) load(0, cur);
+    for (int step = 0; step < nsteps; ++step) {
+        store(cur);
+        __syncthreads();
+        if (step + 1 < nsteps) load(step + 1, nxt);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = ks * 16 + 8 * (lane >> 5);
+            bf16x8_t a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8_t *>(xs + (wm * 64 + i * 32 + (lane & 31)) * 72 + kk);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const bf16x8_t *>(ws + fp_nt_wcol(wn * 64 + j * 32 + (lane & 31)) + kk);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+        cur = nxt;
+    }
+    const float gsc = p.gscale ? *p.gscale : 1.0f;
+    bf16_bits *y = static_cast<bf16_bits *>(p.y);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = c0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < p.mr && col < p.nc) y[row * p.nc + col] = (bf16_bits)f32_to_bf16(acc[i][j][v] * gsc);
+            }
+        }
+}
+
 // ---------------------------------------------------------------- launchers
 namespace {
 
@@ -1092,6 +1330,59 @@ hipError_t launch_fp_dequantize(const uint32_t *codes, const uint8_t *scales, in
                                 void *out, int out_dt, hipStream_t stream)
 {
     return by_mode<DequantRun>(mode, codes, scales, n * (k / 32), out, out_dt, stream);
+}
+
+int fp_nt_ranges(int64_t ni, int64_t nc)
+{
+    if (ni <= 0) return 1;
+    const int64_t cblocks = (nc / 32 + 63) / 64;
+    int64_t r = std::max<int64_t>(1, std::min<int64_t>((512 + cblocks - 1) / std::max<int64_t>(cblocks, 1), (ni + 3) / 4));
+    r = std::min<int64_t>(r, 65535);
+    const int64_t per = (ni + r - 1) / r;
+    return (int)((ni + per - 1) / per);
+}
+
+size_t fp_nt_ws_bytes(int64_t ni, int64_t nc)
+{
+    return (size_t)fp_nt_ranges(ni, nc) * kFpNtRows * (size_t)nc * 4;
+}
+
+namespace {
+template <int MODE> struct NtRun {
+    static hipError_t run(const FpNtLaunch &a, hipStream_t stream)
+    {
+        FpNtParams p = {};
+        p.x = a.x, p.y = a.y, p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
+        p.ni = a.ni, p.nc = a.nc;
+        if (a.tiled) {
+            p.mr = a.m;
+            const dim3 grid((unsigned)((a.nc + 127) / 128), (unsigned)((a.m + 127) / 128));
+            fp_tiled_nt_kernel<MODE><<<grid, 256, 0, stream>>>(p);
+            return hipGetLastError();
+        }
+        p.part = static_cast<float *>(a.workspace);
+        p.ranges = fp_nt_ranges(a.ni, a.nc);
+        p.rows_per_range = (a.ni + p.ranges - 1) / p.ranges;
+        const dim3 pgrid((unsigned)((a.nc / 32 + 63) / 64), (unsigned)p.ranges);
+        for (int64_t m0 = 0; m0 < a.m; m0 += kFpNtRows) {
+            p.m0 = m0, p.mr = std::min<int64_t>(kFpNtRows, a.m - m0);
+            if (a.x_dt == DT_BF16) fp_nt_partial_kernel<MODE, bf16_bits><<<pgrid, 256, 0, stream>>>(p);
+            else fp_nt_partial_kernel<MODE, float><<<pgrid, 256, 0, stream>>>(p);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            const dim3 rgrid((unsigned)((a.nc + 255) / 256), (unsigned)p.mr);
+            if (a.x_dt == DT_BF16) fp_nt_reduce_kernel<bf16_bits><<<rgrid, 256, 0, stream>>>(p);
+            else fp_nt_reduce_kernel<float><<<rgrid, 256, 0, stream>>>(p);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        return hipSuccess;
+    }
+};
+}  // namespace
+
+hipError_t launch_fp_qmm_nt(const FpNtLaunch &a, hipStream_t stream)
+{
+    return by_mode<NtRun>(a.mode, a, stream);
 }
 
 hipError_t launch_fp_qmm(const FpQmmLaunch &a, hipStream_t stream)

@@ -930,6 +930,57 @@ nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l
                        rhs_idx, row_exact, y, workspace, workspace_bytes, stream);
 }
 
+size_t nq_fp_qmm_notrans_workspace_bytes(int64_t m, int64_t ni, int64_t nc, int32_t mode, nq_dtype x_dt,
+                                         int32_t row_exact)
+{
+    (void)mode;
+    if (m <= 0 || ni < 0 || nc <= 0 || nc % 32 != 0) return 0;
+    if (!row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && ni % 64 == 0) return 0;   // tiles
+    return nqk::fp_nt_ws_bytes(ni, nc);
+}
+
+nq_status nq_fp_qmm_notrans(const void *x, nq_dtype x_dt, int64_t m, int64_t ni, const uint32_t *codes,
+                            const uint8_t *scales, const float *global_scale, int64_t nc, int32_t mode,
+                            int32_t row_exact, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    const char *op = "nq_fp_qmm_notrans";
+    g_last_error.clear();
+    if (!dtype_ok(x_dt)) return fail(NQ_ERR_DTYPE, "%s: unknown dtype x_dt=%d", op, (int)x_dt);
+    nq_status st = check_fp(op, mode, ni, nc);   // nc (the grouped axis) a multiple of 32
+    if (st) return st;
+    if ((st = check_global_scale(op, mode, global_scale))) return st;
+    if (m < 0) return fail(NQ_ERR_SHAPE, "%s: negative m=%lld", op, (long long)m);
+    if (m >= kMaxDim || (ni > 0 && m > kMaxElems / ni) || (nc > 0 && m > kMaxElems / nc))
+        return fail(NQ_ERR_SHAPE, "%s: m=%lld is too large", op, (long long)m);
+    if (m == 0 || nc == 0) return NQ_OK;
+    if (!y || (ni > 0 && (!x || !codes || !scales)))
+        return fail(NQ_ERR_NULL, "%s: x, codes, scales and y must be non-null", op);
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(y))
+        return fail(NQ_ERR_ALIGN, "%s: x, codes and y must be 16-byte aligned", op);
+    const int64_t xb = dtype_bytes(x_dt);
+    const Span sy{y, m * nc * xb};
+    if (overlap(sy, Span{x, m * ni * xb}) || overlap(sy, Span{codes, fp_code_bytes(mode, ni, nc)}) ||
+        overlap(sy, Span{scales, fp_scale_bytes(mode, ni, nc)}) || overlap(sy, Span{global_scale, global_scale ? 4 : 0}))
+        return fail(NQ_ERR_ALIAS, "%s: y overlaps an input", op);
+    nqk::FpNtLaunch a;
+    a.x = x, a.y = y, a.codes = codes, a.scales = scales, a.gscale = global_scale, a.workspace = workspace;
+    a.x_dt = x_dt, a.mode = mode, a.m = m, a.ni = ni, a.nc = nc;
+    a.tiled = !row_exact && m > NQ_ROW_INDEPENDENT_ROWS && x_dt == NQ_BF16 && ni % 64 == 0;
+    if (!a.tiled) {
+        const size_t need = nqk::fp_nt_ws_bytes(ni, nc);
+        if (!workspace || workspace_bytes < need)
+            return fail(NQ_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", op, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(NQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", op);
+        const Span sw{workspace, (int64_t)need};
+        if (overlap(sw, sy) || overlap(sw, Span{x, m * ni * xb}) ||
+            overlap(sw, Span{codes, fp_code_bytes(mode, ni, nc)}) || overlap(sw, Span{scales, fp_scale_bytes(mode, ni, nc)}))
+            return fail(NQ_ERR_ALIAS, "%s: the workspace overlaps an argument", op);
+    }
+    return check_launch(op, nqk::launch_fp_qmm_nt(a, stream));
+}
+
 const char *nq_status_string(nq_status s)
 {
     switch (s) {

@@ -180,4 +180,25 @@ struct FpQmmLaunch {
 };
 hipError_t launch_fp_qmm(const FpQmmLaunch &a, hipStream_t stream);
 
+// Weights as stored in a floating-point mode: y[m, c] = x[m, i] . (g w_hat)[i, c],
+// w_hat [ni, nc] with groups along c (nc a multiple of 32).  tiled: bf16 x,
+// ni a multiple of 64 (128 x 128 MFMA tiles); otherwise row ranges fixed by
+// (ni, nc) write fp32 partial sums to the workspace (fp_nt_ws_bytes), added
+// in range order, kFpNtRows activation rows per launch pair.
+constexpr int kFpNtRows = 2;
+struct FpNtLaunch {
+    const void *x;
+    void *y;
+    const uint32_t *codes;
+    const uint8_t *scales;
+    const float *gscale;
+    void *workspace;
+    int x_dt, mode;
+    int64_t m, ni, nc;
+    bool tiled;
+};
+int fp_nt_ranges(int64_t ni, int64_t nc);
+size_t fp_nt_ws_bytes(int64_t ni, int64_t nc);
+hipError_t launch_fp_qmm_nt(const FpNtLaunch &a, hipStream_t stream);
+
 }  // namespace nqk

@@ -377,6 +377,25 @@ nq_status nq_fp_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l
                            int64_t e, int64_t n, int32_t mode, const uint32_t *rhs_idx, int32_t row_exact,
                            void *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Product with the weights as stored in a floating-point mode (the
+ * "transpose = false" product; with the forward weights, dy . w_hat is the
+ * derivative for the activations, "Training through quantized weights"):
+ * y[m, c] = x[m, i] . (g * w_hat)[i, c] for a quantized matrix w_hat
+ * [ni, nc] laid out as above with groups along nc (nc a multiple of 32);
+ * g = *global_scale (NVFP4 only; null: 1); y in x's dtype.  Routes: with
+ * row_exact = 0, m > 8, bf16 x and ni a multiple of 64, 128 x 128 bf16-MFMA
+ * tiles (no workspace); otherwise row ranges of w_hat fixed by (ni, nc)
+ * write fp32 partial sums to the workspace, added in range order, so every
+ * row is bit-equal to its one-row product.  workspace: at least
+ * nq_fp_qmm_notrans_workspace_bytes bytes (16-byte aligned; NQ_ERR_WORKSPACE
+ * if short). */
+size_t nq_fp_qmm_notrans_workspace_bytes(int64_t m, int64_t ni, int64_t nc, int32_t mode, nq_dtype x_dt,
+                                         int32_t row_exact);
+nq_status nq_fp_qmm_notrans(const void *x, nq_dtype x_dt, int64_t m, int64_t ni, const uint32_t *codes,
+                            const uint8_t *scales, const float *global_scale, int64_t nc, int32_t mode,
+                            int32_t row_exact, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* ---------------------------------------------------------------- errors */
 
 /* A static description of a status code. */

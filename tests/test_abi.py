@@ -481,3 +481,25 @@ def test_fp_storage_and_gather_argument_errors(lib):
     assert gq(rows=64, ws=FAKE2 + 0x800000, ws_bytes=need - 1) == NQ_ERR_WORKSPACE
     assert gq(rows=64, ws=FAKE2 + 0x800008, ws_bytes=need) == NQ_ERR_ALIGN
     assert gq(rows=64, ws=FAKE2 + 0x300000, ws_bytes=need) == NQ_ERR_ALIAS
+
+
+def test_fp_notrans_argument_errors(lib):
+    def q(**kw):
+        return lib.nq_fp_qmm_notrans(kw.get("x", FAKE), kw.get("dt", BF16), kw.get("m", 2), kw.get("ni", 128),
+                                     FAKE2, FAKE2 + 0x100000, kw.get("g", 0), kw.get("nc", 64), kw.get("mode", 1),
+                                     kw.get("rx", 0), kw.get("y", FAKE2 + 0x300000), kw.get("ws", 0),
+                                     kw.get("ws_bytes", 0), None)
+    need = lib.nq_fp_qmm_notrans_workspace_bytes(2, 128, 64, 1, BF16, 0)
+    assert need > 0 and lib.nq_fp_qmm_notrans_workspace_bytes(64, 128, 64, 1, BF16, 0) == 0
+    assert lib.nq_fp_qmm_notrans_workspace_bytes(64, 128, 64, 1, BF16, 1) > 0
+    assert q() == NQ_ERR_WORKSPACE and b"nq_fp_qmm_notrans:" in lib.nq_last_error()
+    assert q(mode=7) == NQ_ERR_QUANT
+    assert q(nc=48) == NQ_ERR_SHAPE
+    assert q(m=-1) == NQ_ERR_SHAPE
+    assert q(g=FAKE2 + 0x400000) == NQ_ERR_QUANT
+    assert q(x=0) == NQ_ERR_NULL
+    assert q(x=FAKE + 4) == NQ_ERR_ALIGN
+    assert q(y=FAKE) == NQ_ERR_ALIAS
+    assert q(ws=FAKE2 + 0x800008, ws_bytes=need) == NQ_ERR_ALIGN
+    assert q(ws=FAKE2 + 0x300000, ws_bytes=need) == NQ_ERR_ALIAS
+    assert q(m=0, x=0, y=0) == NQ_OK

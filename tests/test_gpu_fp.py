@@ -297,3 +297,48 @@ def test_gather_matrix_core_moe_shape():
     pick = np.random.default_rng(22).choice(rows, 24, replace=False)
     ref = F.gather_qmm_f64(x[pick], words, scales, mode, idx[pick], gsc)
     assert_rows_close(values(host(y[torch.from_numpy(pick).cuda()])), ref, tolerance(y.dtype), mode)
+
+
+# ---------------------------------------------------------------- weights as stored
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("m,ni,nc,dtype,row_exact", [
+    (1, 320, 224, "bf16", False),
+    (3, 300, 96, "f32", False),                   # ragged row ranges
+    (5, 448, 256, "bf16", True),
+    (40, 320, 224, "bf16", False),                # tiles, ragged nc
+    (130, 448, 96, "bf16", False),                # several row tiles, nc < one tile
+])
+def test_notrans_matches_oracle(mode, m, ni, nc, dtype, row_exact):
+    words, scales = codes_case(30 + m, (ni,), nc, mode)
+    _, x = synthetic.random_case(30 + m, (1, ni), (m, ni), 1.0, dtype)
+    g = 0.625 if mode == "nvfp4" else None
+    gt = torch.tensor([g], dtype=torch.float32, device="cuda") if g else None
+    y = B.nq_fp_qmm_notrans(dev(x), dev(words), u8(scales), mode, global_scale=gt, row_exact=row_exact)
+    ref = F.qmm_nt_f64(x, words, scales, mode, g)
+    assert_rows_close(values(host(y)), ref, tolerance(y.dtype), (mode, m, ni, nc))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_notrans_rows_keep_their_bits(mode):
+    words, scales = codes_case(40, (1000,), 512, mode)
+    _, x = synthetic.random_case(40, (1, 1000), (7, 1000), 1.0, "bf16")
+    xs, cs, ss = dev(x), dev(words), u8(scales)
+    full = B.nq_fp_qmm_notrans(xs, cs, ss, mode, row_exact=True)
+    for i in range(7):
+        one = B.nq_fp_qmm_notrans(xs[i:i + 1], cs, ss, mode)
+        assert bits_equal(full[i:i + 1], one), (mode, i)
+
+
+def test_notrans_decode_size_and_empty_inner():
+    # dx = dy [1, 14336] . W [14336, 4096] as stored (the decode weights' derivative)
+    mode = "mxfp4"
+    words, scales = codes_case(41, (14336,), 4096, mode)
+    _, dy = synthetic.random_case(41, (1, 14336), (1, 14336), 1.0, "bf16")
+    y = B.nq_fp_qmm_notrans(dev(dy), dev(words), u8(scales), mode)
+    assert_rows_close(values(host(y)), F.qmm_nt_f64(dy, words, scales, mode), tolerance(y.dtype), mode)
+    x0 = torch.ones((3, 0), dtype=torch.bfloat16, device="cuda")
+    c0 = torch.zeros((0, 64 * 4 // 32), dtype=torch.int32, device="cuda")
+    s0 = torch.zeros((0, 2), dtype=torch.uint8, device="cuda")
+    y0 = B.nq_fp_qmm_notrans(x0, c0, s0, mode)
+    torch.cuda.synchronize()
+    assert y0.shape == (3, 64) and not y0.float().abs().sum().item()
