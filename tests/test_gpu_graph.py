@@ -50,6 +50,10 @@ def test_graph_replays_match_eager():
     xfg = xf.view(20, 1, 2048)
     ws_f = torch.empty(B.nq_fp_gather_qmm_workspace_bytes(20, 1, 2048, 4, 256), dtype=torch.uint8,
                        device="cuda")
+    # the weights as stored: dy [3, 1024] . W [1024, 2048] (row ranges, ordered adds)
+    dyf = xs[:3, :1024].contiguous()
+    ws_nf = torch.empty(B.nq_fp_qmm_notrans_workspace_bytes(3, 1024, 2048, "nvfp4", torch.bfloat16),
+                        dtype=torch.uint8, device="cuda")
     dy = xs[:1, :512].contiguous()
     dy3 = xs[:3, :512].contiguous()
 
@@ -72,6 +76,7 @@ def test_graph_replays_match_eager():
         "fp_dequant": torch.empty((1024, 2048), dtype=torch.bfloat16, device="cuda"),
         "fp_gather": torch.empty((20, 1, 256), dtype=torch.bfloat16, device="cuda"),
         "fp_gather_exact": torch.empty((20, 1, 256), dtype=torch.bfloat16, device="cuda"),
+        "fp_notrans": torch.empty((3, 2048), dtype=torch.bfloat16, device="cuda"),
     }
 
     def launch():
@@ -93,6 +98,7 @@ def test_graph_replays_match_eager():
         B.nq_fp_gather_qmm(xfg, wfe, sfe, "mxfp4", idf, y=outs["fp_gather"], workspace=ws_f)
         B.nq_fp_gather_qmm(xfg, wfe, sfe, "mxfp4", idf, row_exact=True, y=outs["fp_gather_exact"],
                            workspace=ws_f)
+        B.nq_fp_qmm_notrans(dyf, wf, sfp, "nvfp4", global_scale=gfp, y=outs["fp_notrans"], workspace=ws_nf)
 
     launch()
     torch.cuda.synchronize()
