@@ -1003,27 +1003,42 @@ __global__ void __launch_bounds__(256) fp_nt_partial_kernel(FpNtParams p)
     }
 }
 
-// y[m0 + m, c] = g * (sum over ranges r in increasing order of part[r][m][c])
+// y[m0 + m, c] = g * sum over the ranges of part[r][m][c]: workgroup (b, m)
+// takes 16 columns; thread (part q, column j) adds the ranges of part q
+// (consecutive, increasing) and the 16 part sums are added in part order in
+// LDS.  The order depends only on the number of ranges.
+constexpr int kFpNtRedParts = 16;
+
 template <typename XT>
 __global__ void __launch_bounds__(256) fp_nt_reduce_kernel(FpNtParams p)
 {
-    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    __shared__ float ps[kFpNtRedParts][16];
+    const int j = threadIdx.x & 15, q = threadIdx.x >> 4;
+    const int64_t col = (int64_t)blockIdx.x * 16 + j;
     const int m = blockIdx.y;
-    if (col >= p.nc) return;
-    const float *src = p.part + (int64_t)m * p.nc + col;
+    const int per = (p.ranges + kFpNtRedParts - 1) / kFpNtRedParts;
+    const int r0 = min(q * per, p.ranges), r1 = min(r0 + per, p.ranges);
     const int64_t stride = (int64_t)kFpNtRows * p.nc;
+    const float *src = p.part + (int64_t)m * p.nc + min(col, p.nc - 1);
     float s = 0.0f;
-    int r = 0;
-    for (; r + 8 <= p.ranges; r += 8) {
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {
         float v[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[t] = src[(int64_t)(r + t) * stride];
 #pragma unroll
         for (int t = 0; t < 8; ++t) s += v[t];
     }
-    for (; r < p.ranges; ++r) s += src[(int64_t)r * stride];
-    const float g = p.gscale ? *p.gscale : 1.0f;
-    Elt<XT>::store(static_cast<XT *>(p.y), (p.m0 + m) * p.nc + col, s * g);
+    for (; r < r1; ++r) s += src[(int64_t)r * stride];
+    ps[q][j] = s;
+    __syncthreads();
+    if (q == 0 && col < p.nc) {
+        float t = ps[0][j];
+#pragma unroll
+        for (int u = 1; u < kFpNtRedParts; ++u) t += ps[u][j];
+        const float g = p.gscale ? *p.gscale : 1.0f;
+        Elt<XT>::store(static_cast<XT *>(p.y), (p.m0 + m) * p.nc + col, t * g);
+    }
 }
 
 // Many bf16 rows: 128 x 128 tiles of y with bf16 MFMA, K steps of 64 rows i
@@ -1370,7 +1385,7 @@ template <int MODE> struct NtRun {
             else fp_nt_partial_kernel<MODE, float><<<pgrid, 256, 0, stream>>>(p);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
-            const dim3 rgrid((unsigned)((a.nc + 255) / 256), (unsigned)p.mr);
+            const dim3 rgrid((unsigned)((a.nc + 15) / 16), (unsigned)p.mr);
             if (a.x_dt == DT_BF16) fp_nt_reduce_kernel<bf16_bits><<<rgrid, 256, 0, stream>>>(p);
             else fp_nt_reduce_kernel<float><<<rgrid, 256, 0, stream>>>(p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
