@@ -920,10 +920,10 @@ struct FpNtParams {
     int ranges;
 };
 
-template <int MODE, typename XT>
+template <int MODE, typename XT, int MR>
 __global__ void __launch_bounds__(256) fp_nt_partial_kernel(FpNtParams p)
 {
-    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS, MR = kFpNtRows, U = 4;
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS, U = 4;
     __shared__ float red[3][MR][64 * 33];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t chunks = p.nc / 32, chunk = (int64_t)blockIdx.x * 64 + lane;
@@ -994,7 +994,7 @@ __global__ void __launch_bounds__(256) fp_nt_partial_kernel(FpNtParams p)
 #pragma unroll
             for (int j = 0; j < 32; ++j)
                 o[j] = ((acc[m][j] + red[0][m][lane * 33 + j]) + red[1][m][lane * 33 + j]) + red[2][m][lane * 33 + j];
-            uint4 *dst = reinterpret_cast<uint4 *>(p.part + ((int64_t)blockIdx.y * MR + m) * p.nc + chunk * 32);
+            uint4 *dst = reinterpret_cast<uint4 *>(p.part + ((int64_t)blockIdx.y * kFpNtRows + m) * p.nc + chunk * 32);
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 dst[t] = make_uint4(__float_as_uint(o[4 * t]), __float_as_uint(o[4 * t + 1]),
@@ -1381,8 +1381,14 @@ template <int MODE> struct NtRun {
         const dim3 pgrid((unsigned)((a.nc / 32 + 63) / 64), (unsigned)p.ranges);
         for (int64_t m0 = 0; m0 < a.m; m0 += kFpNtRows) {
             p.m0 = m0, p.mr = std::min<int64_t>(kFpNtRows, a.m - m0);
-            if (a.x_dt == DT_BF16) fp_nt_partial_kernel<MODE, bf16_bits><<<pgrid, 256, 0, stream>>>(p);
-            else fp_nt_partial_kernel<MODE, float><<<pgrid, 256, 0, stream>>>(p);
+            // the chunk's row count as a template argument (a row's arithmetic is the same either way)
+            if (a.x_dt == DT_BF16) {
+                if (p.mr == 1) fp_nt_partial_kernel<MODE, bf16_bits, 1><<<pgrid, 256, 0, stream>>>(p);
+                else fp_nt_partial_kernel<MODE, bf16_bits, kFpNtRows><<<pgrid, 256, 0, stream>>>(p);
+            } else {
+                if (p.mr == 1) fp_nt_partial_kernel<MODE, float, 1><<<pgrid, 256, 0, stream>>>(p);
+                else fp_nt_partial_kernel<MODE, float, kFpNtRows><<<pgrid, 256, 0, stream>>>(p);
+            }
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
             const dim3 rgrid((unsigned)((a.nc + 15) / 16), (unsigned)p.mr);
