@@ -345,8 +345,10 @@ nq_status nq_fp_dequantize(const uint32_t *codes, const uint8_t *scales, int64_t
  * null: 1).  With m <= 8 or row_exact = 1 the matrix-vector kernel runs in
  * chunks of up to 8 rows, and every row is bit-equal to its one-row product;
  * otherwise (bf16 x, k a multiple of 64) 128 x 128 bf16-MFMA tiles, whose
- * B operands are bf16(S * E) (exact).  Tolerance as for the affine
- * products. */
+ * B operands are bf16(S * E) (exact while |S * E| fits bf16; beyond -- only
+ * with E8M0 scale codes near 2^127 -- an infinite operand makes its output
+ * column non-finite, where the matrix-vector route stays finite).  Tolerance
+ * as for the affine products. */
 nq_status nq_fp_qmm(const void *x, nq_dtype x_dt, int64_t m, int64_t k, const uint32_t *codes,
                     const uint8_t *scales, const float *global_scale, int64_t n, int32_t mode,
                     int32_t row_exact, void *y, hipStream_t stream);

@@ -342,3 +342,29 @@ def test_notrans_decode_size_and_empty_inner():
     y0 = B.nq_fp_qmm_notrans(x0, c0, s0, mode)
     torch.cuda.synchronize()
     assert y0.shape == (3, 64) and not y0.float().abs().sum().item()
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("route", ["gemv", "tiled"])
+def test_products_extreme_scales_exact(mode, route):
+    # one-hot rows pick w_hat[r, i] exactly, with E8M0 scale codes at the ends
+    # of the range.  The matrix-vector route scales in fp32 after the group
+    # sums and takes every code up to 2^127 (products that overflow bf16 are
+    # +-inf in both); the tiles' B operands are bf16(S * E), so there the
+    # codes stop where |S * E| still fits bf16 (an infinite B element would
+    # make 0 * inf = NaN in the other outputs of its column)
+    _, bits, gs, _ = F.mode_info(mode)
+    k, n = 128, 64
+    words, _ = synthetic.random_fp_matrix(50, (n,), k, bits, gs, (0, 0), finite_bytes=True)
+    if route == "gemv":
+        codes = np.array([0, 1, 2, 3, 60, 127, 200, 250, 252, 253, 254], np.uint8)
+    else:
+        top = 252 if mode == "mxfp4" else 245           # 6 * 2^125, 448 * 2^118 < bf16 max
+        codes = np.array([0, 1, 2, 3, 60, 127, 200, top - 2, top - 1, top], np.uint8)
+    scales = codes[np.arange(n * (k // gs)) % len(codes)].reshape(n, k // gs)
+    x = _one_hot(k, "bf16")
+    exact = F.dequantize(words, scales, mode, k, "bf16").T          # bf16(S * E), [k, n]
+    y = B.nq_fp_qmm(dev(x), dev(words), u8(scales), mode, row_exact=route == "gemv")
+    got = host(y)
+    same = (got == exact) | ((got & 0x7FFF) == 0) & ((exact & 0x7FFF) == 0)   # +-0 alike
+    assert same.all(), (mode, route, np.argwhere(~same)[:4], got[~same][:4], exact[~same][:4])
