@@ -23,9 +23,11 @@
 //   products    the hardware conversions v_cvt_scalef32_pk_{bf16,f32}_{fp4,fp8}
 //               with scale 1 (exact) turn elements into bf16 or fp32 pairs;
 //               the matrix-vector kernel dots them with x per group and
-//               scales each group sum in fp32, the tiled kernel writes
-//               bf16(S * E) tiles to LDS for bf16 MFMA.  A global scale
-//               multiplies the fp32 result.
+//               scales each group sum in fp32, the tiled kernels write
+//               bf16(S * E) tiles to LDS for bf16 MFMA (MX modes: the same
+//               conversions with the power-of-two scale S give bf16(S * E)
+//               in one instruction per pair).  A global scale multiplies the
+//               fp32 result.
 #include <algorithm>
 #include <type_traits>
 
@@ -146,6 +148,26 @@ __device__ __forceinline__ bf16x2_t pair_bf16(const uint32_t *wd, int p)
         case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
         case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
         default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+        }
+    }
+}
+
+// Elements 2p and 2p + 1 times a power-of-two scale S, as bf16 pairs, by the
+// scaled conversions (exact: a power of two times an E2M1 or E4M3 value).
+template <int MODE>
+__device__ __forceinline__ bf16x2_t pair_bf16_scaled(const uint32_t *wd, int p, float S)
+{
+    if constexpr (Fp<MODE>::fp8) {
+        const uint32_t w = wd[p >> 1];
+        return (p & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, S, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, S, false);
+    } else {
+        const uint32_t w = wd[p >> 2];
+        switch (p & 3) {
+        case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 0);
+        case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 1);
+        case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 2);
+        default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 3);
         }
     }
 }
@@ -734,9 +756,13 @@ __global__ void __launch_bounds__(64 * NW) fp_gather_mfma_kernel(FpGemvParams p)
 #pragma unroll
             for (int q = 0; q < GS / 2; ++q) {
                 const int pi = g * (GS / 2) + q;
-                const f32x2_t e = pair_f32<MODE>(wd, pi);
-                const f32x2_t v = {S * e[0], S * e[1]};
-                o[pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                if constexpr (Fp<MODE>::e8m0) {
+                    o[pi] = __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S));
+                } else {
+                    const f32x2_t e = pair_f32<MODE>(wd, pi);
+                    const f32x2_t v = {S * e[0], S * e[1]};
+                    o[pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                }
             }
         }
         uint4 *wdst = reinterpret_cast<uint4 *>(ws + wrl * kFpLdG + 32 * whalf);
@@ -839,9 +865,13 @@ __global__ void __launch_bounds__(256) fp_tiled_kernel(FpTiledParams p)
 #pragma unroll
             for (int q = 0; q < GS / 2; ++q) {
                 const int pi = g * (GS / 2) + q;
-                const f32x2_t e = pair_f32<MODE>(wd, pi);
-                const f32x2_t v = {S * e[0], S * e[1]};
-                o[pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                if constexpr (Fp<MODE>::e8m0) {
+                    o[pi] = __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S));
+                } else {
+                    const f32x2_t e = pair_f32<MODE>(wd, pi);
+                    const f32x2_t v = {S * e[0], S * e[1]};
+                    o[pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                }
             }
         }
         uint4 *wdst = reinterpret_cast<uint4 *>(ws + lrow * kFpLd + 32 * lhalf);
@@ -1099,9 +1129,14 @@ __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
 #pragma unroll
             for (int q = 0; q < GS / 2; ++q) {
                 const int pi = g * (GS / 2) + q;
-                const f32x2_t e = pair_f32<MODE>(wd, pi);
-                const f32x2_t v = {wok ? S * e[0] : 0.0f, wok ? S * e[1] : 0.0f};
-                const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                uint32_t h;
+                if constexpr (Fp<MODE>::e8m0) {
+                    h = wok ? __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S)) : 0u;
+                } else {
+                    const f32x2_t e = pair_f32<MODE>(wd, pi);
+                    const f32x2_t v = {wok ? S * e[0] : 0.0f, wok ? S * e[1] : 0.0f};
+                    h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                }
                 ws[fp_nt_wcol(wcol + 2 * pi) + wrow] = (bf16_bits)(h & 0xffffu);
                 ws[fp_nt_wcol(wcol + 2 * pi + 1) + wrow] = (bf16_bits)(h >> 16);
             }
