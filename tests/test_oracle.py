@@ -93,6 +93,34 @@ def test_hand_derived_ramp(oracle_mod):
     assert np.array_equal(unpack_reference(c[0], 32, 4), want)
 
 
+def _tie_rows():
+    _, rows = read_golden("ties_half_even.txt")
+    return [pytest.param(r, id=r[0]) for r in rows]
+
+
+@pytest.mark.parametrize("row", _tie_rows())
+def test_exact_ties_go_to_the_even_code(oracle_mod, row):
+    """tests/golden/ties_half_even.txt: groups spanning exactly 2^bits - 1
+    units of 2^e, so scale and bias are exact and values j + 0.5 units above
+    the bias are exact ties; the expected codes were worked out by hand with
+    round-half-to-even.  Ties away from zero, floor(t + 0.5) and truncation
+    each fail some row."""
+    _, gs, bits, dtype, e, vals, codes = row
+    gs, bits, e = int(gs), int(bits), int(e)
+    units = np.array([float(v) for v in vals.split()], np.float64)
+    w = f32(np.ldexp(units, e))
+    assert np.array_equal(w.astype(np.float64), np.ldexp(units, e))      # exact in fp32
+    if dtype == "bf16":
+        w = synthetic.to_bf16_bits(w)
+        assert np.array_equal(oracle_mod.bf16_to_f32(w), f32(np.ldexp(units, e)))   # exact in bf16
+    w = w.reshape(1, -1)
+    c, s, b = oracle_mod.quantize(w, gs, bits)
+    assert stored(oracle_mod, s)[0, 0] == np.ldexp(1.0, e)
+    assert stored(oracle_mod, b)[0, 0] == np.ldexp(units.min(), e)
+    want = np.array([int(v) for v in codes.split()], np.uint32)
+    assert np.array_equal(unpack_reference(c[0], w.shape[1], bits), want)
+
+
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("gs", GROUPS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

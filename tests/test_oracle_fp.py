@@ -152,6 +152,44 @@ def test_mx_round_trip_of_representable_blocks(mode):
     assert np.array_equal(F.dequantize_f64(cq, sq, mode, k), w)
 
 
+def _mx_clamp_rows():
+    out = []
+    for line in open(os.path.join(GOLDEN, "mx_scale_clamp.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, mode, vals, scode, ecodes = (t.strip() for t in line.split("|"))
+        out.append(pytest.param(mode, vals, int(scode), [int(c, 16) for c in ecodes.split()], id=name))
+    return out
+
+
+def _parse_pow2_sum(tok):
+    """'c*2^p' -> c * 2^p exactly; 'max' -> the largest finite fp32."""
+    if tok == "max":
+        return float(np.finfo(np.float32).max)
+    c, p = tok.split("*2^")
+    return float(np.ldexp(float(c), int(p)))
+
+
+@pytest.mark.parametrize("mode,vals,scode,ecodes", _mx_clamp_rows())
+def test_mx_scale_code_at_the_ends_of_the_range(mode, vals, scode, ecodes):
+    """tests/golden/mx_scale_clamp.txt, worked out by hand: blocks whose
+    shared exponent X + 127 falls below 0 take scale code 0 (2^-127) and
+    elements w * 2^127; blocks holding the largest finite fp32 take code
+    252 / 246 with saturated elements."""
+    elem, bits, gs, _ = F.mode_info(mode)
+    v = [_parse_pow2_sum(t) for t in vals.split()]
+    w = np.zeros((1, gs), np.float64)
+    w[0, : len(v)] = v
+    w32 = w.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), w)                # exact in fp32
+    cq, sq = F.quantize(w32, mode)
+    assert sq.dtype == np.uint8 and int(sq[0, 0]) == scode
+    b = np.unpackbits(cq[0].astype("<u4").view(np.uint8), bitorder="little")[: gs * bits]
+    got = (b.reshape(gs, bits).astype(np.uint32) << np.arange(bits, dtype=np.uint32)).sum(axis=1)
+    assert list(got[: len(ecodes)]) == ecodes
+    assert not got[len(ecodes):].any()
+
+
 @pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
 def test_mx_shared_exponent_rule(mode):
     # X = floor(log2 amax) - emax: amax / 2^X lies in [2^emax, 2^(emax + 1));
