@@ -35,6 +35,7 @@ METRIC = "qmm weight GB/s at 1 row (decode); TFLOP/s at 2048 rows; 4-bit g64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 ROTATE_BYTES = 600e6
+PREROLL_CYCLES = 2_000_000     # spin before the timed region (clock ticks)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CSRC = os.path.join(ROOT, "group_wise_affine_quantize_amd", "csrc")
 KERNEL_SOURCES = {
@@ -76,8 +77,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "rows"],
-                    help="run one kernel for a profiler and print its timing")
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "multirow_8bit", "splitk",
+                                       "moe_gather"],
+                    help="run one workload for a profiler and print its timing")
     return ap.parse_args()
 
 
@@ -118,6 +120,10 @@ class Timer:
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        # A spin kernel (about 1 ms) keeps the stream busy while the host
+        # submits the timed work behind it, so the event window holds the
+        # launches back to back and no host submission latency.
+        torch.cuda._sleep(PREROLL_CYCLES)
         e0.record()
         if self.eager:
             for i in range(steps):
@@ -137,6 +143,51 @@ def prefill_only(args, B, synthetic, dev, q2, timer, log):
     y4 = torch.empty((2048, 14336), dtype=torch.bfloat16, device="cuda")
     t = timer.run(lambda i: B.nq_qmm(x4, *q2, 64, 4, y=y4), args.prefill_steps, 3, chunk=10)
     log(f"prefill: {args.prefill_steps} launches, {t / args.prefill_steps * 1e6:.1f} us each")
+
+
+def row_only(args, B, synthetic, dev, rotated, timer, log):
+    """--only multirow_8bit | splitk | moe_gather: time that workload's batched
+    (or grouped) product and its row-exact form, for a profiler."""
+    import torch
+    name = args.only
+    wl = synthetic.WORKLOADS[name]
+    d = synthetic.generate(name)
+    q = B.nq_quantize(dev(d["w"]), wl.group_size, wl.bits)
+    xs = dev(d["x"])
+    cps = rotated(q)
+    steps = args.row_steps
+    if name == "moe_gather":
+        ids = dev(d["ids"])
+        rows, l, k = wl.x_shape
+        e, n, _ = wl.w_shape
+        y = torch.empty((rows, l, n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(B.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, wl.group_size, wl.bits,
+                                                         torch.bfloat16, torch.bfloat16),
+                         dtype=torch.uint8, device="cuda")
+        entries = ((B.nq_gather_qmm, "grouped"), (B.nq_gather_qmm_row_exact, "row_exact"))
+        for entry, tag in entries:
+            t = timer.run(lambda i: entry(xs, *cps[i % len(cps)], wl.group_size, wl.bits, ids, y=y,
+                                          workspace=ws), steps, 10)
+            log(f"{name} {tag}: {steps} launches, {t / steps * 1e6:.3f} us each")
+        return
+    m, _ = wl.x_shape
+    n = wl.w_shape[0]
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    for entry, tag in ((B.nq_qmm, "batched"), (B.nq_qmm_row_exact, "row_exact")):
+        t = timer.run(lambda i: entry(xs, *cps[i % len(cps)], wl.group_size, wl.bits, y=y), steps, 10)
+        log(f"{name} {tag}: {steps} launches, {t / steps * 1e6:.3f} us each")
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -211,6 +262,9 @@ def main():
 
     if args.only == "prefill":
         return prefill_only(args, B, synthetic, dev, q2, timer, log)
+    if args.only is not None:
+        del copies2
+        return row_only(args, B, synthetic, dev, rotated, timer, log)
     log("timing decode")
     t_dec = timer.run(decode, args.steps, args.warmup)
     # the graph replays must reproduce the eager result bit for bit
@@ -480,7 +534,7 @@ def main():
         t_cpu = statistics.median(times)
         out["cpu_baseline"] = {
             "value": round(weight_bytes / t_cpu / 1e9, 4), "unit": "GB/s",
-            "cores": O.threads(), "kind": "oracle",
+            "cores": O.threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"the whole decode workload (x [1,4096] . W[14336,4096]^T, fp64 "
                       f"accumulation), median of {len(times)} runs",
         }
@@ -490,7 +544,7 @@ def main():
         t_pre_cpu = time.perf_counter() - t0
         out["prefill"]["cpu_baseline"] = {
             "value": round(2 * 8 * 14336 * 4096 / t_pre_cpu / 1e12, 6), "unit": "TFLOP/s",
-            "cores": O.threads(), "kind": "oracle",
+            "cores": O.threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "8 of the 2048 prefill rows against all of W (1 run)"}
     print(json.dumps(out), flush=True)
 

@@ -145,6 +145,18 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(stream, shape, dtype, device):
+    """A new output or workspace tensor.  With a caller's stream it is
+    allocated under that stream, so the caching allocator ties the memory to
+    the stream the kernels run on and does not hand it to other work while
+    they may still use it."""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _contig(name, t):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -167,12 +179,11 @@ def nq_quantize(w, group_size, bits, codes=None, scales=None, biases=None, strea
     n = w.numel() // k if k else 0
     lead = tuple(w.shape[:-1])
     if codes is None:
-        codes = torch.empty(lead + (words_per_row(k, bits),), dtype=torch.int32, device=w.device)
+        codes = _empty(stream, lead + (words_per_row(k, bits),), torch.int32, w.device)
     if scales is None:
-        scales = torch.empty(lead + (k // group_size if group_size else 0,), dtype=w.dtype,
-                             device=w.device)
+        scales = _empty(stream, lead + (k // group_size if group_size else 0,), w.dtype, w.device)
     if biases is None:
-        biases = torch.empty_like(scales)
+        biases = _empty(stream, scales.shape, scales.dtype, scales.device)
     _check(lib.nq_quantize(_ptr(w), _dt(w), n, k, group_size, bits, _ptr(codes), _ptr(scales),
                            _ptr(biases), _stream(stream)))
     return codes, scales, biases
@@ -188,7 +199,7 @@ def nq_dequantize(codes, scales, biases, group_size, bits, out_dtype=None, out=N
     n = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
     out_dtype = out_dtype or scales.dtype
     if out is None:
-        out = torch.empty(tuple(scales.shape[:-1]) + (k,), dtype=out_dtype, device=scales.device)
+        out = _empty(stream, tuple(scales.shape[:-1]) + (k,), out_dtype, scales.device)
     _check(lib.nq_dequantize(_ptr(codes), _ptr(scales), _ptr(biases), _dt(scales), n, k,
                              group_size, bits, _ptr(out), _dt(out), _stream(stream)))
     return out
@@ -223,7 +234,7 @@ def _qmm_call(entry, x, codes, scales, biases, group_size, bits, y, workspace, s
     if scales.shape[1] * group_size != k or codes.shape != (n, words_per_row(k, bits)):
         raise ValueError("codes/scales shapes do not match x and the quantization")
     if y is None:
-        y = torch.empty((m, n), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (m, n), x.dtype, x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = [_ptr(x), _dt(x), m, k, _ptr(codes), _ptr(scales), _ptr(biases), _dt(scales), n,
             group_size, bits, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)]
@@ -264,7 +275,7 @@ def nq_qmm_batched(x, codes, scales, biases, group_size, bits, y=None, workspace
     if scales.shape[1] * group_size != k or codes.shape != (n, words_per_row(k, bits)):
         raise ValueError("codes/scales shapes do not match x and the quantization")
     if y is None:
-        y = torch.empty((batch, l, n), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (batch, l, n), x.dtype, x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_qmm_batched(_ptr(x), _dt(x), batch, l, k, _ptr(codes), _ptr(scales),
                               _ptr(biases), _dt(scales), n, group_size, bits, _ptr(y),
@@ -289,12 +300,12 @@ def _notrans_call(entry, x, codes, scales, biases, group_size, bits, y, workspac
     if scales.shape[0] != ni or codes.shape != (ni, words_per_row(nc, bits)):
         raise ValueError("codes/scales shapes do not match x and the quantization")
     if y is None:
-        y = torch.empty((m, nc), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (m, nc), x.dtype, x.device)
     if workspace is None:
         need = lib.nq_qmm_notrans_workspace_bytes(m, ni, nc, group_size, bits, _dt(x),
                                                   int(entry.endswith("row_exact")))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = _empty(stream, need, torch.uint8, x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(getattr(lib, entry)(_ptr(x), _dt(x), m, ni, _ptr(codes), _ptr(scales), _ptr(biases),
                                _dt(scales), nc, group_size, bits, _ptr(y), _ptr(workspace),
@@ -332,9 +343,9 @@ def nq_qmm_grad_scales_biases(x, dy, codes, group_size, bits, out_dtype=None, ds
         raise ValueError("x, dy and codes do not match")
     od = out_dtype or x.dtype
     if dscales is None:
-        dscales = torch.empty((n, k // group_size), dtype=od, device=x.device)
+        dscales = _empty(stream, (n, k // group_size), od, x.device)
     if dbiases is None:
-        dbiases = torch.empty((n, k // group_size), dtype=od, device=x.device)
+        dbiases = _empty(stream, (n, k // group_size), od, x.device)
     _check(lib.nq_qmm_grad_scales_biases(_ptr(x), _ptr(dy), _dt(x), m, k, _ptr(codes), n, group_size,
                                          bits, _ptr(dscales), _ptr(dbiases), _dt(dscales),
                                          _stream(stream)))
@@ -364,12 +375,12 @@ def _gather_call(entry, x, codes, scales, biases, group_size, bits, rhs_idx, sor
     if rhs_idx.numel() != rows:
         raise ValueError("rhs_idx must have one id per row")
     if y is None:
-        y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (rows, l, n), x.dtype, x.device)
     if workspace is None:
         need = lib.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, _dt(x),
                                                  _dt(scales), int(bool(sorted_hint)))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = _empty(stream, need, torch.uint8, x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(getattr(lib, entry)(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
                                _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(rhs_idx),
@@ -412,12 +423,12 @@ def nq_gather_qmm_lhs(x, codes, scales, biases, group_size, bits, lhs_idx, rhs_i
     if lhs_idx.numel() != rows:
         raise ValueError("lhs_idx and rhs_idx must have one id per output row")
     if y is None:
-        y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (rows, l, n), x.dtype, x.device)
     if workspace is None:
         need = lib.nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, _dt(x),
                                                  _dt(scales), int(bool(sorted_hint)))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = _empty(stream, need, torch.uint8, x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_gather_qmm_lhs(_ptr(x), _dt(x), x_items, rows, l, k, _ptr(codes), _ptr(scales),
                                  _ptr(biases), _dt(scales), e, n, group_size, bits, _ptr(lhs_idx),
@@ -444,9 +455,9 @@ def nq_fp_quantize(w, mode, codes=None, scales=None, stream=None):
     n = w.numel() // k if k else 0
     lead = tuple(w.shape[:-1])
     if codes is None:
-        codes = torch.empty(lead + (words_per_row(k, bits),), dtype=torch.int32, device=w.device)
+        codes = _empty(stream, lead + (words_per_row(k, bits),), torch.int32, w.device)
     if scales is None:
-        scales = torch.empty(lead + (k // gs,), dtype=torch.uint8, device=w.device)
+        scales = _empty(stream, lead + (k // gs,), torch.uint8, w.device)
     _check(lib.nq_fp_quantize(_ptr(w), _dt(w), n, k, mid, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
@@ -461,8 +472,7 @@ def nq_fp_dequantize(codes, scales, mode, out_dtype=None, out=None, stream=None)
     k = scales.shape[-1] * gs
     n = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
     if out is None:
-        out = torch.empty(tuple(scales.shape[:-1]) + (k,), dtype=out_dtype or torch.bfloat16,
-                          device=scales.device)
+        out = _empty(stream, tuple(scales.shape[:-1]) + (k,), out_dtype or torch.bfloat16, scales.device)
     _check(lib.nq_fp_dequantize(_ptr(codes), _ptr(scales), n, k, mid, _ptr(out), _dt(out),
                                 _stream(stream)))
     return out
@@ -481,7 +491,7 @@ def nq_fp_qmm(x, codes, scales, mode, global_scale=None, row_exact=False, y=None
     if scales.shape[1] * gs != k or codes.shape != (n, words_per_row(k, bits)):
         raise ValueError("codes/scales shapes do not match x and the mode")
     if y is None:
-        y = torch.empty((m, n), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (m, n), x.dtype, x.device)
     _check(lib.nq_fp_qmm(_ptr(x), _dt(x), m, k, _ptr(codes), _ptr(scales), _ptr(global_scale), n, mid,
                          int(bool(row_exact)), _ptr(y), _stream(stream)))
     return y
@@ -510,10 +520,10 @@ def nq_fp_gather_qmm(x, codes, scales, mode, rhs_idx, global_scales=None, row_ex
     if rhs_idx.numel() != rows:
         raise ValueError("rhs_idx must hold one expert per row")
     if y is None:
-        y = torch.empty((rows, l, n), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (rows, l, n), x.dtype, x.device)
     if workspace is None:
         need = lib.nq_fp_gather_qmm_workspace_bytes(rows, l, k, e, n)
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+        workspace = _empty(stream, need, torch.uint8, x.device) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_fp_gather_qmm(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales),
                                 _ptr(global_scales), e, n, mid, _ptr(rhs_idx), int(bool(row_exact)), _ptr(y),
@@ -544,10 +554,10 @@ def nq_fp_qmm_notrans(x, codes, scales, mode, global_scale=None, row_exact=False
     if scales.shape[0] != ni or codes.shape != (ni, words_per_row(nc, bits)):
         raise ValueError("codes/scales shapes do not match x and the mode")
     if y is None:
-        y = torch.empty((m, nc), dtype=x.dtype, device=x.device)
+        y = _empty(stream, (m, nc), x.dtype, x.device)
     if workspace is None:
         need = lib.nq_fp_qmm_notrans_workspace_bytes(m, ni, nc, mid, _dt(x), int(bool(row_exact)))
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+        workspace = _empty(stream, need, torch.uint8, x.device) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.nq_fp_qmm_notrans(_ptr(x), _dt(x), m, ni, _ptr(codes), _ptr(scales), _ptr(global_scale), nc,
                                  mid, int(bool(row_exact)), _ptr(y), _ptr(workspace), ws_bytes,

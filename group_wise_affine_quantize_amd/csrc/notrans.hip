@@ -4,10 +4,10 @@
 // Method: "Quantization" page of the nuvec documentation -- section "Affine"
 // (the quantized_matmul flag: x times the weights as stored instead of their
 // transpose; the weights' groups then run along the output columns) and
-// section "Training through quantized weights" (derivative rules for the
-// activations, and in affine mode for the scales and biases; the one for the
-// activations is dy times the weights as stored, i.e. this file's product
-// with the forward weights, whose rows are the forward outputs).
+// section "Training through quantized weights" (affine products can be
+// differentiated in x and, in affine mode, in the scales and biases; the
+// derivative in x is dy times the weights as stored, i.e. this file's
+// product with the forward weights, whose rows are the forward outputs).
 //
 // Notation: the quantized matrix has ni rows of nc columns, grouped along the
 // columns: codes [ni, nc*bits/32], scales and biases [ni, nc/gs];

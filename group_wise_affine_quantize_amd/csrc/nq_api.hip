@@ -543,8 +543,8 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
     return qmm_common("nq_qmm_with_plan", 0, plan, a, stream);
 }
 
-// Batch items keep their solo bits ("Products on the GPU" section: batch
-// items of quantized products).  The route is the plan of one item; every
+// Batch items keep their solo bits (nuvec API index, section "Determinism":
+// batch items of quantized products).  The route is the plan of one item; every
 // kernel's arithmetic for an output element depends only on its own row of
 // x and its weight row, so running that plan over all items at once gives
 // each item the bits of the call on it alone.  Only the launch is cut where

@@ -169,9 +169,9 @@ nq_status nq_qmm_with_plan(const nq_plan *plan, const void *x, nq_dtype x_dt, in
                            int32_t bits, void *y, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* A product over batch items that keeps each item's solo bits ("Products on
- * the GPU" section: batch items of a quantized product each get the bits of
- * their product alone, the split of K counted per item).  x [batch, l, k]
+/* A product over batch items that keeps each item's solo bits (nuvec API
+ * index, section "Determinism", batch items of quantized products: each item
+ * gets the bits of its product alone, the split of K counted per item).  x [batch, l, k]
  * (x_dt), y [batch, l, n] (x_dt), weights as for nq_qmm; item i of y is
  * bit-equal to nq_qmm(x[i]) with m = l, whatever batch is, because the
  * route is nq_qmm_plan(l, ...) (not of batch * l rows) and no kernel's

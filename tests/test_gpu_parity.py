@@ -443,7 +443,7 @@ def test_gather_lhs(case):
     (2, 20, 96, 512, 4, "f32"),       # fp32 x: matrix-vector route at any size
 ])
 def test_qmm_batched_items_keep_solo_bits(batch, l, n, k, bits, x_dtype):
-    """Batch items of a quantized product ("Products on the GPU" section):
+    """Batch items of a quantized product (nuvec API index, section "Determinism"):
     item i of nq_qmm_batched over [batch, l, k] is bit-equal to nq_qmm on
     x[i] alone, and within the product tolerance of the oracle."""
     gs = 64
@@ -681,3 +681,25 @@ def test_one_hot_and_ones_special_cases():
         bound = 2.0 ** -22 * (np.abs(sc) * top + np.abs(bi))   # two fp32 roundings
         assert np.all(np.abs(y[i] - w_hat[:, col]) <= bound)
     assert np.allclose(y[7], w_hat.sum(axis=1), rtol=1e-5, atol=1e-5)
+
+
+def test_explicit_stream_allocates_on_that_stream():
+    """Calls given a stream other than the current one: the outputs and the
+    gather's workspace come from that stream's memory, the kernels run there,
+    and the results equal those of calls on the current stream, bit for bit."""
+    w, x, c, s, b = quantized_case(77, 384, 1024, 64, 4, "bf16", m=3, x_dtype="bf16")
+    xs, cs, ss, bs = dev(x), *gpu_quantized(c, s, b)
+    wg, xg = synthetic.random_case(78, (4, 256, 512), (40, 1, 512), 0.02, "bf16")
+    cg, sg, bg = O.quantize(wg.reshape(-1, 512), 64, 4)
+    cg, sg, bg = (dev(a.reshape(4, 256, -1)) for a in (cg, sg, bg))
+    ids = dev(np.arange(40, dtype=np.uint32) % 4)
+    xgd = dev(xg)
+    y0 = B.nq_qmm(xs, cs, ss, bs, 64, 4)
+    g0 = B.nq_gather_qmm(xgd, cg, sg, bg, 64, 4, ids)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y1 = B.nq_qmm(xs, cs, ss, bs, 64, 4, stream=side)
+    g1 = B.nq_gather_qmm(xgd, cg, sg, bg, 64, 4, ids, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert bits_equal(y0, y1) and bits_equal(g0, g1)
