@@ -1176,6 +1176,7 @@ hipError_t gemv_dt(const GemvLaunch &a, hipStream_t stream)
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream)
 {
     if (a.ksplit < 1 || a.ksplit > 8) return hipErrorInvalidValue;
+    if (gemv_mfma_family(a.n, a.k, a.gs, a.bits, a.x_dt)) return launch_gemv_mfma(a, stream);
     if (a.x_dt == DT_F32) {
         if (a.sb_dt == DT_F32) return gemv_dt<float, float>(a, stream);
         return gemv_dt<float, bf16_bits>(a, stream);

@@ -88,8 +88,16 @@ nq_status check_launch(const char *op, hipError_t err)
 // never of the row count -- so that a row's arithmetic is the same however
 // many rows share the call.  Enough waves are formed to keep every compute
 // unit's memory pipeline busy: about 2048 waves (8 per CU on 256 CUs).
-int gemv_ksplit(int64_t n, int64_t k)
+int gemv_ksplit(int64_t n, int64_t k, int gs, int bits, int x_dt)
 {
+    if (nqk::gemv_mfma_family(n, k, gs, bits, x_dt)) {
+        // matrix-core waves own 32 weight rows; K units are groups of 128 or
+        // steps of 64
+        const int64_t units = gs >= 128 ? k / gs : k / 64;
+        const int64_t base_waves = (n + 31) / 32;
+        const int64_t want = (2048 + base_waves - 1) / std::max<int64_t>(base_waves, 1);
+        return (int)std::max<int64_t>(1, std::min<int64_t>({want, units, 8}));
+    }
     const int64_t steps = (k + nqk::kStepElems - 1) / nqk::kStepElems;
     if (steps <= 1) return 1;
     const int64_t base_waves = (n + 3) / 4;
@@ -112,7 +120,7 @@ nq_status make_plan(const char *op, int64_t m, int64_t n, int64_t k, int gs, int
         plan->tile_n = big ? 256 : 128;
     } else {
         plan->route = NQ_ROUTE_GEMV;
-        plan->ksplit = gemv_ksplit(n, k);
+        plan->ksplit = gemv_ksplit(n, k, gs, bits, x_dt);
         plan->rows_per_wave = 0;   // chosen per launch chunk; no effect on a row's bits
     }
     return NQ_OK;
@@ -677,7 +685,10 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
             if (overlap(sw, ins[i])) return fail(NQ_ERR_ALIAS, "%s: workspace overlaps %s", op, names[i]);
     }
     uint32_t *ws = static_cast<uint32_t *>(workspace);
-    const int chunk = mfma ? nqk::kGroupChunkMfma : nqk::kGroupChunk;
+    // chunks of 32 vectors for the matrix cores (either route), of 8 for the
+    // VALU matrix-vector kernels
+    const bool gemv_cores = nqk::gemv_mfma_family(n, k, group_size, bits, x_dt);
+    const int chunk = (mfma || gemv_cores) ? nqk::kGroupChunkMfma : nqk::kGroupChunk;
     // the matrix-core route groups small id sets inside its own workgroups
     const bool self_group = mfma && nqk::gather_self_group_fits(v, e);
     if (shared && !self_group) {
@@ -727,7 +738,7 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
     g.e = e;
     g.gs = group_size;
     g.bits = bits;
-    g.ksplit = gemv_ksplit(n, k);   // the plan nq_qmm_row_exact takes
+    g.ksplit = gemv_ksplit(n, k, group_size, bits, x_dt);   // the plan nq_qmm_row_exact takes
     g.rows_per_wave = 0;
     g.lhs = lhs_idx;
     g.x_items = x_items;
@@ -739,7 +750,8 @@ nq_status gather_impl(const char *op, int row_exact, const void *x, nq_dtype x_d
         g.chunks = ws + ((v + 1 + 3) & ~(int64_t)3);
         g.max_chunks = nqk::gather_group_max_chunks(v, e, chunk);
         g.items = 1;
-        g.rows_per_item = nqk::kGroupChunk;   // chunks of up to 8 vectors
+        g.rows_per_item = chunk;   // chunks of up to `chunk` vectors
+        g.max_rows = chunk;
     }
     return check_launch(op, nqk::launch_gemv(g, stream));
 }

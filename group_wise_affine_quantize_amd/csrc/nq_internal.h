@@ -46,12 +46,20 @@ struct GemvLaunch {
     int ksplit, rows_per_wave;
     const uint32_t *perm = nullptr, *chunks = nullptr, *nchunks = nullptr;
     int64_t max_chunks = 0;
+    int max_rows = 8;   // largest vector count of a chunk of the table
     // gather with left indices: vector r * l + j reads x row lhs[r] * l + j
     // (lhs[r] >= x_items gives a zero row)
     const uint32_t *lhs = nullptr;
     int64_t x_items = 0, lhs_l = 1;
 };
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
+
+// The matrix-core arithmetic of the matrix-vector family: bf16 activations,
+// 4-bit codes, k a multiple of 64 up to 4096, n below the streaming one-row
+// shapes.  A function of the sizes and dtypes only, so a row's arithmetic
+// never depends on how many rows share its call.
+bool gemv_mfma_family(int64_t n, int64_t k, int gs, int bits, int x_dt);
+hipError_t launch_gemv_mfma(const GemvLaunch &a, hipStream_t stream);
 
 // Vectors per chunk of the grouped matrix-vector gather (that family's
 // largest row count per launch chunk) and of the grouped matrix-core gather.

@@ -703,3 +703,66 @@ def test_explicit_stream_allocates_on_that_stream():
     side.synchronize()
     torch.cuda.synchronize()
     assert bits_equal(y0, y1) and bits_equal(g0, g1)
+
+
+# ------------------------------------------------------------------ matrix-core matrix-vector family
+# 4-bit codes with bf16 activations, k a multiple of 64 up to 4096 and n below
+# the streaming one-row shapes: the matrix-vector family's matrix-core
+# arithmetic (every route at these shapes, whatever the row count).
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m", [1, 3, 8, 21])
+def test_gemv_cores_parity(gs, w_dtype, m):
+    """Values within the product tolerance of the oracle; every row bit-equal
+    to its one-row product."""
+    n, k, bits = 77, 1408, 4          # n not a multiple of the 32-row blocks
+    w, x, c, s, b = quantized_case(gs + m, n, k, gs, bits, w_dtype, m, "bf16", 0.02)
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y = B.nq_qmm_row_exact(xs, *q, gs, bits) if m > 8 else B.nq_qmm(xs, *q, gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), tolerance(y.dtype), "cores")
+    for i in range(m):
+        assert bits_equal(B.nq_qmm(xs[i:i + 1].contiguous(), *q, gs, bits)[0], y[i]), i
+
+
+@pytest.mark.parametrize("ksplit", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("gs", [32, 128])
+def test_gemv_cores_forced_splits(ksplit, gs):
+    """Any K split (slices of whole groups added in slice order): values
+    within tolerance, and rows bit-equal to one-row calls under the same plan."""
+    n, k, m, bits = 45, 2048 + 128, 5, 4
+    w, x, c, s, b = quantized_case(ksplit + gs, n, k, gs, bits, "bf16", m, "bf16", 0.02)
+    plan = B.Plan()
+    plan.route, plan.ksplit, plan.rows_per_wave = B.NQ_ROUTE_GEMV, ksplit, 0
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y = B.nq_qmm_with_plan(plan, xs, *q, gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), tolerance(y.dtype), "cores split")
+    for i in range(m):
+        assert bits_equal(B.nq_qmm_with_plan(plan, xs[i:i + 1].contiguous(), *q, gs, bits)[0], y[i]), i
+
+
+def test_gemv_cores_batched_and_gathered_rows_keep_bits():
+    """Batch items, per-row gather and the grouped row-exact gather at a
+    matrix-core shape give every row the bits of its plain product."""
+    e, n, k, gs, bits = 3, 70, 768, 64, 4
+    w, _ = synthetic.random_case(90, (e, n, k), (1, k), 0.02, "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    cs, ss, bs = dev(c), dev(s), dev(b)
+    _, xb = synthetic.random_case(91, (1, 1), (4, 3, k), 1.0, "f32", "bf16")
+    xbd = dev(xb)
+    yb = B.nq_qmm_batched(xbd, cs[1], ss[1], bs[1], gs, bits)
+    assert_rows_close(values(host(yb)).reshape(12, n), O.qmm_f64(xb.reshape(12, k), c[1], s[1], b[1], gs, bits),
+                      tolerance(yb.dtype), "batched")
+    for i in range(4):
+        assert bits_equal(B.nq_qmm(xbd[i].contiguous(), cs[1], ss[1], bs[1], gs, bits), yb[i]), i
+    for rows in (6, 40):   # per-row route, then the grouped row-exact route
+        _, xg = synthetic.random_case(92 + rows, (1, 1), (rows, 1, k), 1.0, "f32", "bf16")
+        ids = np.random.default_rng(rows).integers(0, e, size=rows, dtype=np.uint32)
+        xgd = dev(xg)
+        yg = B.nq_gather_qmm_row_exact(xgd, cs, ss, bs, gs, bits, dev(ids))
+        assert_rows_close(values(host(yg)), O.gather_qmm_f64(xg, c, s, b, gs, bits, ids),
+                          tolerance(yg.dtype), "gather")
+        for r in range(rows):
+            yr = B.nq_qmm(xgd[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+            assert bits_equal(yr, yg[r]), (rows, r)
