@@ -43,7 +43,9 @@ class Plan(ctypes.Structure):
 
 
 def library_path():
-    return os.path.join(HERE, _LIB_NAME)
+    """libnq.so next to this file, or the build NQ_LIBRARY names (for
+    instance the host-sanitizer build)."""
+    return os.environ.get("NQ_LIBRARY") or os.path.join(HERE, _LIB_NAME)
 
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t

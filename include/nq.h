@@ -75,7 +75,15 @@ typedef enum {
     NQ_ERR_PLAN = 9       /* an explicit plan that does not fit the shapes */
 } nq_status;
 
+/* Dtype arguments are validated (NQ_ERR_DTYPE for any other value), so the
+ * type holds every int32 value: compiled as C++ its underlying type is fixed
+ * to int32_t (in C an enum of these constants is int-sized anyway), and
+ * reading an unknown value is defined behaviour on both sides. */
+#ifdef __cplusplus
+typedef enum : int32_t { NQ_F32 = 0, NQ_BF16 = 1 } nq_dtype;
+#else
 typedef enum { NQ_F32 = 0, NQ_BF16 = 1 } nq_dtype;
+#endif
 
 /* Rows of a product that keep the bits of their one-row product in every
  * mode (nuvec API index, constant ROW_INDEPENDENT_ROWS). */

@@ -14,15 +14,26 @@ FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-
          "-Wall", "-Wextra", "-std=c11"]
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", *FLAGS, "-o", tmp, SRC, "-lm"]
+# AddressSanitizer / UndefinedBehaviorSanitizer variant (gcc), for running
+# the oracle's pins against:  LD_PRELOAD=$(gcc -print-file-name=libasan.so)
+# ASAN_OPTIONS=detect_leaks=0 NQ_ORACLE_LIB=oracle/liboracle_san.so pytest ...
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose=False, sanitize=False):
+    lib = SAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    flags = [f for f in FLAGS if not (sanitize and f == "-O2")] + (SAN_FLAGS if sanitize else [])
+    cmd = ["gcc", *flags, "-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))
