@@ -65,6 +65,8 @@ _SIGNATURES = {
                                       _I32],
     "nq_gather_qmm": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P,
                       _I32, _P, _P, _SZ, _P],
+    "nq_gather_qmm_noalloc": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P,
+                              _I32, _P, _P],
     "nq_gather_qmm_row_exact": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32,
                                 _I32, _P, _I32, _P, _P, _SZ, _P],
     "nq_gather_qmm_lhs": [_P, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _I32, _I64, _I64, _I32, _I32,
@@ -398,6 +400,29 @@ def nq_gather_qmm(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hi
     A workspace is allocated when the call needs one and none is given."""
     return _gather_call("nq_gather_qmm", x, codes, scales, biases, group_size, bits, rhs_idx,
                         sorted_hint, y, workspace, stream)
+
+
+def nq_gather_qmm_noalloc(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint=False, y=None,
+                          stream=None):
+    """nq_gather_qmm with the grouping tables in the library's static device
+    array: no workspace argument, and nothing allocated by the library (y is
+    allocated here only when not given)."""
+    lib = load_library()
+    for name, t in (("x", x), ("codes", codes), ("scales", scales), ("biases", biases),
+                    ("rhs_idx", rhs_idx)):
+        _contig(name, t)
+    if rhs_idx.element_size() != 4:
+        raise ValueError("rhs_idx must hold 32-bit ids")
+    rows, l, k = x.shape
+    e, n = scales.shape[0], scales.shape[1]
+    if rhs_idx.numel() != rows:
+        raise ValueError("rhs_idx must have one id per row")
+    if y is None:
+        y = _empty(stream, (rows, l, n), x.dtype, x.device)
+    _check(lib.nq_gather_qmm_noalloc(_ptr(x), _dt(x), rows, l, k, _ptr(codes), _ptr(scales), _ptr(biases),
+                                     _dt(scales), e, n, group_size, bits, _ptr(rhs_idx), int(bool(sorted_hint)),
+                                     _ptr(y), _stream(stream)))
+    return y
 
 
 def nq_gather_qmm_row_exact(x, codes, scales, biases, group_size, bits, rhs_idx, sorted_hint=False,

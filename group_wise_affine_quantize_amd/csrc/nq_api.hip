@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "nq.h"
@@ -777,6 +778,66 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
     (void)sorted_hint;
     return gather_impl("nq_gather_qmm", 0, x, x_dt, rows, l, k, codes, scales, biases, sb_dt, e, n,
                        group_size, bits, nullptr, rows, rhs_idx, y, workspace, workspace_bytes, stream);
+}
+
+// ---- the gather for callers that cannot allocate
+
+// The grouping tables of nq_gather_qmm_noalloc: one array per GPU, in the
+// library's own device memory.  Host code never passes the array's name to
+// a kernel or a copy (on the host it is only a stand-in for the device
+// address); the address of each GPU's copy is taken once, with that GPU
+// current, and kept.
+static __device__ __align__(256) uint8_t scratch[NQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kScratchDevices];   // device address of `scratch`, per GPU
+
+// The current GPU's copy of `scratch` (its address taken on first use).
+nq_status scratch_of_current_device(const char *op, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return fail(NQ_ERR_LAUNCH, "%s: no usable current device (%d)", op, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !ptr)
+            return fail(NQ_ERR_LAUNCH, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                        op, dev, hipGetErrorString(err));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NQ_OK;
+}
+
+}  // namespace
+
+nq_status nq_gather_qmm_noalloc(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                                const uint32_t *codes, const void *scales, const void *biases,
+                                nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                                const uint32_t *rhs_idx, int32_t sorted_hint, void *y, hipStream_t stream)
+{
+    const char *op = "nq_gather_qmm_noalloc";
+    g_last_error.clear();
+    const size_t need = nq_gather_qmm_workspace_bytes(rows, l, k, e, n, group_size, bits, x_dt, sb_dt,
+                                                      sorted_hint);
+    if (need > NQ_NOALLOC_SCRATCH_BYTES)
+        return fail(NQ_ERR_WORKSPACE,
+                    "%s: the grouping tables of %lld x %lld vectors and %lld experts need %zu bytes, above "
+                    "the %u-byte static scratch",
+                    op, (long long)rows, (long long)l, (long long)e, need, (unsigned)NQ_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need) {
+        // the grouping pass rewrites every table entry a later kernel reads,
+        // so nothing in the array has to start at zero
+        if (nq_status st = scratch_of_current_device(op, &ws)) return st;
+    }
+    return gather_impl(op, 0, x, x_dt, rows, l, k, codes, scales, biases, sb_dt, e, n, group_size, bits,
+                       nullptr, rows, rhs_idx, y, ws, need ? (size_t)NQ_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 nq_status nq_gather_qmm_row_exact(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,

@@ -272,6 +272,24 @@ nq_status nq_gather_qmm(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, i
                         const uint32_t *rhs_idx, int32_t sorted_hint, void *y, void *workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: nq_gather_qmm with its
+ * workspace taken from a static array of NQ_NOALLOC_SCRATCH_BYTES (1 MiB) in
+ * the library's own device memory, one per GPU, held until the process
+ * ends.  Same arguments (minus the workspace), routes, results and errors
+ * as nq_gather_qmm, and bit-identical outputs; NQ_ERR_WORKSPACE if the
+ * grouping tables would need more than the array holds (a workspace size
+ * above 1 MiB: about 160,000 vectors).  It calls no hipMalloc, hipFree or
+ * other allocating routine; the array's address is looked up once per GPU
+ * (hipGetSymbolAddress).  Every call on one GPU uses the same array and
+ * leaves its tables in it: calls that overlap in time on one GPU (on other
+ * streams or threads) race, and the caller must order them. */
+#define NQ_NOALLOC_SCRATCH_BYTES (1u << 20)
+nq_status nq_gather_qmm_noalloc(const void *x, nq_dtype x_dt, int64_t rows, int64_t l, int64_t k,
+                                const uint32_t *codes, const void *scales, const void *biases,
+                                nq_dtype sb_dt, int64_t e, int64_t n, int32_t group_size, int32_t bits,
+                                const uint32_t *rhs_idx, int32_t sorted_hint, void *y, hipStream_t stream);
+
 /* As nq_gather_qmm in row-exact mode ("Products on the GPU" section; nuvec
  * API index, with_row_exact): every row of y is bit-equal to
  * nq_qmm_row_exact of x[r] with expert rhs_idx[r]'s weights, whatever the
