@@ -1,6 +1,7 @@
 // Matrix-vector family of quantized products on gfx950 matrix cores: few
 // activation rows (a launch chunk of up to 32) times the quantized weights,
-// for bf16 activations and 4- or 8-bit codes.
+// for bf16 activations and 4- or 8-bit codes (the routing takes it for
+// 4-bit codes only; see gemv_mfma_family).
 //
 // Method: "Quantization" page of the nuvec documentation -- section "Affine"
 // (w ~ scale * code + bias per group; the product is x times the transposed
