@@ -335,8 +335,8 @@ struct FpGemvParams {
 
 __device__ __forceinline__ float wave_sum(float v, int lane)
 {
-    v += xor_lane<32>(v, lane);
-    v += xor_lane<16>(v, lane);
+    v = swap_sum<32>(v, v);
+    v = swap_sum<16>(v, v);
     v += xor_lane<8>(v, lane);
     v += xor_lane<4>(v, lane);
     v += xor_lane<2>(v, lane);
@@ -559,13 +559,19 @@ __device__ __forceinline__ float wave_sum_many(float (&v)[V], int lane)
         float h[V / 2];
 #pragma unroll
         for (int i = 0; i < V / 2; ++i) {
-            const float send = pick(upper, v[i], v[i + V / 2]);
-            const float keep = pick(upper, v[i + V / 2], v[i]);
-            h[i] = keep + xor_lane<OFF>(send, lane);
+            if constexpr (OFF >= 16) {
+                h[i] = swap_sum<OFF>(v[i], v[i + V / 2]);
+            } else {
+                const float send = pick(upper, v[i], v[i + V / 2]);
+                const float keep = pick(upper, v[i + V / 2], v[i]);
+                h[i] = keep + xor_lane<OFF>(send, lane);
+            }
         }
         return wave_sum_many<V / 2, OFF / 2>(h, lane);
     } else {
-        float one[1] = {v[0] + xor_lane<OFF>(v[0], lane)};
+        float one[1];
+        if constexpr (OFF >= 16) one[0] = swap_sum<OFF>(v[0], v[0]);
+        else one[0] = v[0] + xor_lane<OFF>(v[0], lane);
         return wave_sum_many<1, OFF / 2>(one, lane);
     }
 }

@@ -140,13 +140,19 @@ __device__ __forceinline__ float wave_reduce_transposed(float (&v)[V], int lane)
         float h[V / 2];
 #pragma unroll
         for (int i = 0; i < V / 2; ++i) {
-            const float send = pick(upper, v[i], v[i + V / 2]);
-            const float keep = pick(upper, v[i + V / 2], v[i]);
-            h[i] = keep + xor_lane<OFF>(send, lane);
+            if constexpr (OFF >= 16) {
+                h[i] = swap_sum<OFF>(v[i], v[i + V / 2]);
+            } else {
+                const float send = pick(upper, v[i], v[i + V / 2]);
+                const float keep = pick(upper, v[i + V / 2], v[i]);
+                h[i] = keep + xor_lane<OFF>(send, lane);
+            }
         }
         return wave_reduce_transposed<V / 2, OFF / 2>(h, lane);
     } else {
-        float r = v[0] + xor_lane<OFF>(v[0], lane);
+        float r;
+        if constexpr (OFF >= 16) r = swap_sum<OFF>(v[0], v[0]);
+        else r = v[0] + xor_lane<OFF>(v[0], lane);
         float one[1] = {r};
         return wave_reduce_transposed<1, OFF / 2>(one, lane);
     }

@@ -88,8 +88,12 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t *w, int j)
     return q & ((1u << BITS) - 1u);
 }
 
-// v from lane (lane ^ OFF) of the wave: DPP quad permutes for 1 and 2,
-// ds_swizzle (xor mode, within 32 lanes) for 4, 8 and 16, ds_bpermute for 32.
+// v from lane (lane ^ OFF) of the wave, without the LDS pipe: DPP quad
+// permutes for 1 and 2, DPP row rotations for 4 and 8 (a rotation by 8
+// inside a 16-lane row is the xor; for 4 the lanes pick a rotation by 4 or
+// by 12), gfx950's v_permlane16_swap / v_permlane32_swap for 16 and 32.
+// A swap of a register with itself leaves, in the first result, the lower
+// row (half) of each pair twice and, in the second, the upper one twice.
 template <int OFF>
 __device__ __forceinline__ float xor_lane(float v, int lane)
 {
@@ -97,10 +101,34 @@ __device__ __forceinline__ float xor_lane(float v, int lane)
     int r;
     if constexpr (OFF == 1) r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);   // [1,0,3,2]
     else if constexpr (OFF == 2) r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
-    else if constexpr (OFF == 4 || OFF == 8 || OFF == 16)
-        r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (OFF << 10));
-    else r = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, iv);
+    else if constexpr (OFF == 4) {
+        const int a = __builtin_amdgcn_update_dpp(0, iv, 0x124, 0xF, 0xF, false);   // row_ror:4
+        const int b = __builtin_amdgcn_update_dpp(0, iv, 0x12C, 0xF, 0xF, false);   // row_ror:12
+        r = (lane & 4) ? a : b;
+    } else if constexpr (OFF == 8) {
+        r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);             // row_ror:8
+    } else if constexpr (OFF == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+        r = (lane & 16) ? (int)s[0] : (int)s[1];
+    } else {
+        static_assert(OFF == 32, "lane exchange distance");
+        const auto s = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
+        r = (lane & 32) ? (int)s[0] : (int)s[1];
+    }
     return __int_as_float(r);
+}
+
+// One step (distance OFF = 16 or 32) of a transposed lane reduction: lanes
+// without bit OFF keep a and add it from lane ^ OFF, lanes with it keep b and
+// add it from lane ^ OFF -- one swap of the two registers.  The sum of each
+// lane's pair is the same as keep + partner (addition commutes).
+template <int OFF>
+__device__ __forceinline__ float swap_sum(float a, float b)
+{
+    static_assert(OFF == 16 || OFF == 32, "swap distance");
+    const auto s = OFF == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_int(a), __float_as_int(b), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_int(a), __float_as_int(b), false, false);
+    return __int_as_float((int)s[0]) + __int_as_float((int)s[1]);
 }
 
 __device__ __forceinline__ float pick(bool c, float a, float b)
