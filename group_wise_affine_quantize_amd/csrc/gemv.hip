@@ -1183,6 +1183,10 @@ hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream)
 {
     if (a.ksplit < 1 || a.ksplit > 8) return hipErrorInvalidValue;
     if (gemv_mfma_family(a.n, a.k, a.gs, a.bits, a.x_dt)) return launch_gemv_mfma(a, stream);
+    // the 8-bit matrix-core family takes the plan's own split; an explicit
+    // plan with another split runs the VALU kernels
+    if (gemv_band_family(a.n, a.k, a.gs, a.bits, a.x_dt) && a.ksplit == kBandKsplit && a.rows_per_wave == 0)
+        return launch_gemv_band(a, stream);
     if (a.x_dt == DT_F32) {
         if (a.sb_dt == DT_F32) return gemv_dt<float, float>(a, stream);
         return gemv_dt<float, bf16_bits>(a, stream);

@@ -44,6 +44,8 @@ namespace nqk {
 
 typedef __bf16 mf_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float mf_f32x16_t __attribute__((ext_vector_type(16)));
+typedef float mf_f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <typename ST>
 struct MfmaGemvParams {
@@ -372,6 +374,246 @@ __global__ void __launch_bounds__(512) gemv_mfma_kernel(MfmaGemvParams<ST> p)
     store(tot);
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit codes: one band of 16 weight rows per workgroup, staged whole in LDS.
+//
+// Per element (activation row m, weight row n), group g and K quarter w:
+//     G = sum_{k in g} x[m, k] * q[n, k]     (v_mfma_f32_16x16x32_bf16, fp32)
+//     X = sum_{k in g} x[m, k]               (the same instruction against ones)
+//     acc_w = fma(s[n, g], G, acc_w);  acc_w = fma(b[n, g], X, acc_w)
+// in increasing g inside quarter w (of the four equal K quarters), and
+// y = ((acc_0 + acc_1) + acc_2) + acc_3.  The codes enter the matrix cores
+// as their exact bf16 values.  Inside a group, MFMA j of lane group h takes
+// k = 32 j + 8 h .. + 8 of the quarter: every instruction's 32 k lie in one
+// group.  Nothing depends on the other rows of the launch chunk (up to 8
+// activation rows; MFMA rows 8..15 are computed and not stored), so every
+// row keeps the bits of its one-row product on every route.
+//
+// Work decomposition: workgroup (band, launch chunk); its 4 waves take the K
+// quarters.  Each wave issues all of its loads at once, as direct-to-LDS
+// loads of whole 16-byte chunks: the codes of its 16 rows (every
+// instruction 1 KB of consecutive chunks, a row's quarter in 256-byte
+// stages), the chunk's activations of its quarter and the quarter's scales
+// and biases.  Chunk q of row r is written to slot q ^ (r mod 16) of its
+// stage, so the B-operand reads (16 rows of one chunk column) and the
+// A-operand reads spread over all banks.  Stage t is computed after a
+// counted wait for its own loads; later stages stay in flight.
+constexpr int kBandRows = 16;        // weight rows per workgroup (MFMA columns)
+constexpr int kBandVectors = 8;      // activation rows per launch chunk
+constexpr int kBandStageK = 256;     // K per stage
+constexpr int kBandMaxK = 4096;
+
+template <typename ST, int GPQ>
+constexpr int band_sb_loads() { return (kBandRows * GPQ * (int)sizeof(ST) + 255) / 256; }
+
+template <typename ST, int GS, int NST, bool SBLDS>
+__global__ void __launch_bounds__(256) gemv_band_kernel(MfmaGemvParams<ST> p)
+{
+    constexpr int KQ = NST * kBandStageK;            // K per wave (quarter)
+    constexpr int RBS = kBandStageK;                 // code bytes per row and stage (8-bit)
+    constexpr int CPS = RBS / 16;                    // 16-byte chunks per row and stage
+    constexpr int NIC = kBandRows * RBS / 1024;      // code loads per stage
+    constexpr int XCS = kBandStageK * 2 / 16;        // activation chunks per row and stage
+    constexpr int NIX = kBandVectors * XCS / 64;     // activation loads per stage
+    constexpr int GPQ = KQ / GS;                     // groups per quarter
+    constexpr int SBW = (int)sizeof(ST) / 2;         // scale words (16-bit) per group
+    constexpr int NSB = band_sb_loads<ST, GPQ>();    // scale (and bias) loads
+    constexpr int L = NIC + NIX;
+    static_assert(CPS >= kBandRows, "the swizzle stays inside a stage");
+    static_assert((NST - 1) * L < 64, "vmcnt");
+    static_assert(GPQ * (int)sizeof(ST) >= 4, "scale runs of whole dwords");
+    __shared__ __attribute__((aligned(16))) uint8_t c_lds[4][kBandRows * KQ];
+    __shared__ __attribute__((aligned(16))) uint8_t x_lds[4][kBandVectors * KQ * 2];
+    __shared__ __attribute__((aligned(16))) uint8_t s_lds[4][NSB * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t b_lds[4][NSB * 256];
+    __shared__ mf_f32x4_t part[3][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * kBandRows;
+    const int64_t k0 = (int64_t)wave * KQ;
+    const int c = lane & 15, h = lane >> 4;
+
+    // ---- launch chunk (as in the kernel above)
+    bool live = true;
+    int64_t slab = 0;
+    int mrows;
+    uint32_t first = 0;
+    const bf16_bits *xb = p.x;
+    bf16_bits *yb = p.y;
+    if (p.chunks) {
+        if (blockIdx.y >= *p.nchunks) return;   // uniform over the workgroup
+        const uint4 ch = p.chunks[blockIdx.y];
+        if ((int64_t)ch.x >= p.e) live = false;
+        else slab = ch.x;
+        first = ch.y;
+        mrows = (int)ch.z;
+    } else {
+        const int64_t item = p.item0 + blockIdx.y / p.chunks_per_item;
+        const int64_t r0 = (int64_t)(blockIdx.y % p.chunks_per_item) * kBandVectors;
+        mrows = (int)min((int64_t)kBandVectors, p.rows_per_item - r0);
+        int64_t xi = item;
+        if (p.lhs) {
+            xi = p.lhs[item];
+            if (xi >= p.x_items) live = false, xi = 0;   // a zero row; x is never read
+        }
+        xb = p.x + (xi * p.rows_per_item + r0) * p.k;
+        yb = p.y + (item * p.rows_per_item + r0) * p.n;
+        if (p.idx) {
+            const uint32_t ex = p.idx[item];
+            if ((int64_t)ex >= p.e) live = false;
+            else slab = ex;
+        }
+    }
+    auto x_row = [&](int r) -> const bf16_bits * {   // r < mrows
+        if (p.chunks) {
+            int64_t v = p.perm[first + r];
+            if (p.lhs) {
+                const int64_t xi = p.lhs[v / p.lhs_l];
+                v = (xi < p.x_items ? xi : 0) * p.lhs_l + v % p.lhs_l;
+            }
+            return p.x + v * p.k;
+        }
+        return xb + (int64_t)r * p.k;
+    };
+
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        // scales and biases of the quarter (4-byte aligned rows): lane t of
+        // load i -> row t / DPR, dword t % DPR
+        if constexpr (SBLDS) {
+            constexpr int DPR = GPQ * (int)sizeof(ST) / 4;
+#pragma unroll
+            for (int i = 0; i < NSB; ++i) {
+                const int t = i * 64 + lane;
+                const int r = min(t / DPR, kBandRows - 1), d = t % DPR;
+                const int64_t row = slab * p.n + min(n0 + r, p.n - 1);
+                const int64_t off = row * p.groups_per_row + k0 / GS + d * (4 / (int)sizeof(ST));
+                __builtin_amdgcn_global_load_lds((const void *)(p.scales + off), (lds_void_t *)&s_lds[wave][i * 256], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(p.biases + off), (lds_void_t *)&b_lds[wave][i * 256], 4, 0, 0);
+            }
+        }
+        // activation rows of this lane's loads (rows past the chunk read row 0)
+        const bf16_bits *xsrc[NIX];
+#pragma unroll
+        for (int i = 0; i < NIX; ++i) {
+            const int r = (i * 64 + lane) / XCS;
+            xsrc[i] = x_row(r < mrows ? r : 0) + k0;
+        }
+        const uint8_t *csrc = reinterpret_cast<const uint8_t *>(p.codes) + k0;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+#pragma unroll
+            for (int i = 0; i < NIC; ++i) {
+                const int t = i * 64 + lane;
+                const int r = t / CPS, sl = t % CPS;
+                const int q = sl ^ (r & (kBandRows - 1));   // the chunk that goes to slot sl
+                const int64_t row = slab * p.n + min(n0 + r, p.n - 1);
+                __builtin_amdgcn_global_load_lds((const void *)(csrc + row * p.words_per_row * 4 + (int64_t)(st * CPS + q) * 16),
+                                                 (lds_void_t *)&c_lds[wave][st * kBandRows * RBS + i * 1024], 16, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NIX; ++i) {
+                const int t = i * 64 + lane;
+                const int r = t / XCS, sl = t % XCS;
+                const int q = sl ^ (r & (kBandRows - 1));
+                __builtin_amdgcn_global_load_lds((const void *)(xsrc[i] + (int64_t)(st * XCS + q) * 8),
+                                                 (lds_void_t *)&x_lds[wave][st * kBandVectors * XCS * 16 + i * 1024], 16, 0, 0);
+            }
+        }
+#else
+        (void)x_row;
+#endif
+        mf_f32x4_t dq = {}, dx = {};
+        const uint32_t onew = 0x3f803f80u;
+        const mf_bf16x8_t ones = __builtin_bit_cast(mf_bf16x8_t, make_uint4(onew, onew, onew, onew));
+        const int xr = c & (kBandVectors - 1);   // MFMA rows 8..15 repeat rows 0..7 (not stored)
+        const uint16_t *ss = reinterpret_cast<const uint16_t *>(&s_lds[wave][0]);
+        const uint16_t *bs = reinterpret_cast<const uint16_t *>(&b_lds[wave][0]);
+        static_for_mf<0, NST>([&](auto stt) {
+            constexpr int ST_ = decltype(stt)::value;
+            constexpr int after = (NST - 1 - ST_) * L;   // loads issued after this stage's
+            __builtin_amdgcn_s_waitcnt((after & 15) | ((after >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+            asm volatile("" ::: "memory");
+            const uint8_t *cs = &c_lds[wave][ST_ * kBandRows * RBS];
+            const uint8_t *xs = &x_lds[wave][ST_ * kBandVectors * XCS * 16];
+            constexpr int NJ = kBandStageK / 32;
+            uint2 braw[NJ];
+            uint4 araw[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {   // all of the stage's operands first
+                const int byte = 32 * j + 8 * h;
+                braw[j] = *reinterpret_cast<const uint2 *>(cs + c * RBS + 16 * ((byte >> 4) ^ c) + (byte & 15));
+                araw[j] = *reinterpret_cast<const uint4 *>(xs + xr * XCS * 16 + 16 * ((4 * j + h) ^ xr));
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int kk = ST_ * kBandStageK + 32 * j;   // inside the quarter
+                const uint2 w = braw[j];
+                const float f0 = (float)(w.x & 0xffu), f1 = (float)((w.x >> 8) & 0xffu);
+                const float f2 = (float)((w.x >> 16) & 0xffu), f3 = (float)(w.x >> 24);
+                const float f4 = (float)(w.y & 0xffu), f5 = (float)((w.y >> 8) & 0xffu);
+                const float f6 = (float)((w.y >> 16) & 0xffu), f7 = (float)(w.y >> 24);
+                uint4 b;
+                b.x = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+                b.y = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+                b.z = __builtin_amdgcn_perm(__float_as_uint(f5), __float_as_uint(f4), 0x07060302u);
+                b.w = __builtin_amdgcn_perm(__float_as_uint(f7), __float_as_uint(f6), 0x07060302u);
+                const mf_bf16x8_t av = __builtin_bit_cast(mf_bf16x8_t, araw[j]);
+                const mf_bf16x8_t bv = __builtin_bit_cast(mf_bf16x8_t, b);
+                const bool fresh = (kk % GS) == 0;
+                const mf_f32x4_t z = {};
+                dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, fresh ? z : dq, 0, 0, 0);
+                dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, fresh ? z : dx, 0, 0, 0);
+                if ((kk + 32) % GS == 0) {
+                    const int gi = kk / GS;
+                    uint32_t sr, br;
+                    if constexpr (!SBLDS) {   // read in place: the same values
+                        const int64_t at = (slab * p.n + min(n0 + c, p.n - 1)) * p.groups_per_row + (k0 + kk) / GS;
+                        sr = sizeof(ST) == 2 ? (uint32_t)reinterpret_cast<const uint16_t *>(p.scales)[at] << 16
+                                             : reinterpret_cast<const uint32_t *>(p.scales)[at];
+                        br = sizeof(ST) == 2 ? (uint32_t)reinterpret_cast<const uint16_t *>(p.biases)[at] << 16
+                                             : reinterpret_cast<const uint32_t *>(p.biases)[at];
+                    } else if constexpr (SBW == 1) {
+                        sr = (uint32_t)ss[c * GPQ + gi] << 16;
+                        br = (uint32_t)bs[c * GPQ + gi] << 16;
+                    } else {
+                        sr = reinterpret_cast<const uint32_t *>(ss)[c * GPQ + gi];
+                        br = reinterpret_cast<const uint32_t *>(bs)[c * GPQ + gi];
+                    }
+                    const float sc = __uint_as_float(sr), bi = __uint_as_float(br);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        acc[v] = fmaf(sc, dq[v], acc[v]);
+                        acc[v] = fmaf(bi, dx[v], acc[v]);
+                    }
+                }
+            }
+        });
+    }
+    // the quarters added in quarter order
+    if (wave > 0) part[wave - 1][lane] = mf_f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w2 = 0; w2 < 3; ++w2) {
+        const mf_f32x4_t o = part[w2][lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += o[v];
+    }
+    // lane (c, h) holds rows 4 h + v of column c
+    const bool col_ok = n0 + c < p.n;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * h + v;
+        if (col_ok && m < mrows) {
+            bf16_bits *yr = p.chunks ? p.y + (int64_t)p.perm[first + m] * p.n : yb + (int64_t)m * p.n;
+            Elt<bf16_bits>::store(yr, n0 + c, acc[v]);
+        }
+    }
+}
+
 namespace {
 
 constexpr int kMfMaxGridY = 65535;
@@ -444,6 +686,102 @@ hipError_t gemv_mfma_rows(const GemvLaunch &a, hipStream_t stream)
 }
 
 }  // namespace
+
+namespace {
+
+template <typename ST, int GS, int NST, bool SBLDS>
+hipError_t gemv_band_run(const GemvLaunch &a, hipStream_t stream)
+{
+    MfmaGemvParams<ST> p{};
+    p.x = static_cast<const bf16_bits *>(a.x);
+    p.y = static_cast<bf16_bits *>(a.y);
+    p.codes = a.codes;
+    p.scales = static_cast<const ST *>(a.scales);
+    p.biases = static_cast<const ST *>(a.biases);
+    p.idx = a.idx;
+    p.chunks = reinterpret_cast<const uint4 *>(a.chunks);
+    p.perm = a.perm;
+    p.nchunks = a.nchunks;
+    p.lhs = a.lhs;
+    p.x_items = a.x_items;
+    p.lhs_l = a.lhs_l;
+    p.rows_per_item = a.rows_per_item;
+    p.k = a.k;
+    p.n = a.n;
+    p.e = a.e;
+    p.words_per_row = a.k / 4;
+    p.groups_per_row = a.k / a.gs;
+    p.gs = a.gs;
+    p.ksplit = 4;
+    p.chunks_per_item = (int)((a.rows_per_item + kBandVectors - 1) / kBandVectors);
+    const unsigned gx = (unsigned)((a.n + kBandRows - 1) / kBandRows);
+    if (a.chunks) {
+        if (a.max_chunks > kMfMaxGridY) return hipErrorInvalidValue;
+        p.item0 = 0;
+        gemv_band_kernel<ST, GS, NST, SBLDS><<<dim3(gx, (unsigned)a.max_chunks), dim3(256), 0, stream>>>(p);
+        return hipGetLastError();
+    }
+    const int64_t items_per_launch = std::max<int64_t>(1, kMfMaxGridY / p.chunks_per_item);
+    for (int64_t i0 = 0; i0 < a.items; i0 += items_per_launch) {
+        const int64_t cnt = std::min(items_per_launch, a.items - i0);
+        p.item0 = i0;
+        gemv_band_kernel<ST, GS, NST, SBLDS><<<dim3(gx, (unsigned)(cnt * p.chunks_per_item)), dim3(256), 0, stream>>>(p);
+        if (hipError_t err = hipGetLastError()) return err;
+    }
+    return hipSuccess;
+}
+
+template <typename ST, int GS, bool SBLDS>
+hipError_t gemv_band_stages(const GemvLaunch &a, hipStream_t stream)
+{
+    switch (a.k / (4 * kBandStageK)) {
+    case 1: return gemv_band_run<ST, GS, 1, SBLDS>(a, stream);
+    case 2: return gemv_band_run<ST, GS, 2, SBLDS>(a, stream);
+    case 3: return gemv_band_run<ST, GS, 3, SBLDS>(a, stream);
+    default: return gemv_band_run<ST, GS, 4, SBLDS>(a, stream);
+    }
+}
+
+// Scales and biases go to LDS as dwords when both start on a 4-byte
+// boundary (the rest of each row's run is then aligned too); otherwise the
+// kernel reads them in place.  The values, and so the results, are the same.
+template <typename ST, int GS>
+hipError_t gemv_band_sb(const GemvLaunch &a, hipStream_t stream)
+{
+    if ((((uintptr_t)a.scales | (uintptr_t)a.biases) & 3) == 0) return gemv_band_stages<ST, GS, true>(a, stream);
+    return gemv_band_stages<ST, GS, false>(a, stream);
+}
+
+template <typename ST>
+hipError_t gemv_band_gs(const GemvLaunch &a, hipStream_t stream)
+{
+    switch (a.gs) {
+    case 32: return gemv_band_sb<ST, 32>(a, stream);
+    case 64: return gemv_band_sb<ST, 64>(a, stream);
+    default: return gemv_band_sb<ST, 128>(a, stream);
+    }
+}
+
+}  // namespace
+
+bool gemv_band_family(int64_t n, int64_t k, int gs, int bits, int x_dt)
+{
+    // Measured choice, by shape only: 8-bit codes with bf16 activations, K
+    // in whole quarters of 256-wide stages up to 4096, below the streaming
+    // one-row shapes (x [8, 4096] x [4096, 4096] 8-bit g128: 7.1 us against
+    // 11.9 us for the matrix-vector VALU kernel).
+    if (x_dt != DT_BF16 || bits != 8 || k < 4 * kBandStageK || k % (4 * kBandStageK) != 0 || k > kBandMaxK)
+        return false;
+    if (gs != 32 && gs != 64 && gs != 128) return false;
+    return n < 8 * 1024;
+}
+
+hipError_t launch_gemv_band(const GemvLaunch &a, hipStream_t stream)
+{
+    if (!gemv_band_family(a.n, a.k, a.gs, a.bits, a.x_dt)) return hipErrorInvalidValue;
+    if (a.sb_dt == DT_F32) return gemv_band_gs<float>(a, stream);
+    return gemv_band_gs<bf16_bits>(a, stream);
+}
 
 bool gemv_mfma_family(int64_t n, int64_t k, int gs, int bits, int x_dt)
 {

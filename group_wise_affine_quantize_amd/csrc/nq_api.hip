@@ -91,6 +91,7 @@ nq_status check_launch(const char *op, hipError_t err)
 // unit's memory pipeline busy: about 2048 waves (8 per CU on 256 CUs).
 int gemv_ksplit(int64_t n, int64_t k, int gs, int bits, int x_dt)
 {
+    if (nqk::gemv_band_family(n, k, gs, bits, x_dt)) return nqk::kBandKsplit;   // four K quarters
     if (nqk::gemv_mfma_family(n, k, gs, bits, x_dt)) {
         // matrix-core waves own 32 weight rows; K units are groups of 128 or
         // steps of 64

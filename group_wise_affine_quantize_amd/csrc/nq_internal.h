@@ -61,6 +61,13 @@ hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 bool gemv_mfma_family(int64_t n, int64_t k, int gs, int bits, int x_dt);
 hipError_t launch_gemv_mfma(const GemvLaunch &a, hipStream_t stream);
 
+// The matrix-core arithmetic of the 8-bit matrix-vector family: bf16
+// activations, k a multiple of 1024 up to 4096, n below the streaming
+// one-row shapes; K in four fixed quarters (the plan's ksplit is 4).
+bool gemv_band_family(int64_t n, int64_t k, int gs, int bits, int x_dt);
+constexpr int kBandKsplit = 4;
+hipError_t launch_gemv_band(const GemvLaunch &a, hipStream_t stream);
+
 // Vectors per chunk of the grouped matrix-vector gather (that family's
 // largest row count per launch chunk) and of the grouped matrix-core gather.
 constexpr int kGroupChunk = 8;

@@ -104,6 +104,10 @@ def test_plan_routes(lib):
     # long inner dimension with a small output splits K
     assert plan(lib, 4, 1024, 14336).ksplit > 1
     assert plan(lib, 1, 14336, 4096).ksplit == 1
+    # 8-bit codes with k in whole 1024-wide quarters up to 4096 below the
+    # streaming shapes: the matrix-core family's four K quarters, for any m
+    for m in (1, 8, 21):
+        assert plan(lib, m, 4096, 4096, gs=128, bits=8, row_exact=1).ksplit == 4
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced

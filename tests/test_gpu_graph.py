@@ -121,3 +121,50 @@ def test_graph_replays_match_eager():
         for k, v in outs.items():
             assert bits_equal(v, eager[k]), (rep, k)
         assert scratch.shape == (3, 512)
+
+
+def test_graph_replays_match_eager_band():
+    """The 8-bit matrix-core matrix-vector kernel (plain, row-exact and the
+    grouped gather behind the grouping pass) under graph replay."""
+    gs, bits = 128, 8
+    w, x = synthetic.random_case(21, (4096, 2048), (11, 2048), 0.02, "bf16")
+    c, s, b = (dev(a) for a in O.quantize(w, gs, bits))
+    xs = dev(x)
+    we, xe = synthetic.random_case(22, (3, 96, 1024), (40, 1, 1024), 0.02, "bf16")
+    ce, se, be = (dev(a) for a in O.quantize(we, gs, bits))
+    xes = dev(xe)
+    ide = dev(np.random.default_rng(23).integers(0, 3, size=40, dtype=np.uint32))
+    ws = torch.empty(B.nq_gather_qmm_workspace_bytes(40, 1, 1024, 3, 96, gs, bits, torch.bfloat16,
+                                                     torch.bfloat16), dtype=torch.uint8, device="cuda")
+    outs = {
+        "few": torch.empty((8, 4096), dtype=torch.bfloat16, device="cuda"),
+        "exact": torch.empty((11, 4096), dtype=torch.bfloat16, device="cuda"),
+        "gather": torch.empty((40, 1, 96), dtype=torch.bfloat16, device="cuda"),
+    }
+
+    def launch():
+        B.nq_qmm(xs[:8], c, s, b, gs, bits, y=outs["few"])
+        B.nq_qmm_row_exact(xs, c, s, b, gs, bits, y=outs["exact"])
+        B.nq_gather_qmm_row_exact(xes, ce, se, be, gs, bits, ide, y=outs["gather"], workspace=ws)
+
+    launch()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    for rep in range(4):
+        for v in outs.values():
+            v.fill_(0)
+        scratch = B.nq_qmm(xs[:3], c, s, b, gs, bits)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert bits_equal(v, eager[k]), (rep, k)
+        assert scratch.shape == (3, 4096)

@@ -766,3 +766,100 @@ def test_gemv_cores_batched_and_gathered_rows_keep_bits():
         for r in range(rows):
             yr = B.nq_qmm(xgd[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
             assert bits_equal(yr, yg[r]), (rows, r)
+
+
+# ------------------------------------------------------------------ 8-bit matrix-core matrix-vector family
+# 8-bit codes with bf16 activations, k a multiple of 1024 up to 4096 and n
+# below the streaming one-row shapes: a band of 16 weight rows per workgroup
+# on 16x16x32 matrix cores, K in four quarters (every route at these shapes).
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m,k", [(1, 1024), (3, 3072), (8, 2048), (21, 4096)])
+def test_gemv_band_parity(gs, w_dtype, m, k):
+    """Values within the product tolerance of the oracle; every row bit-equal
+    to its one-row product."""
+    n, bits = 131, 8                 # n not a multiple of the 16-row bands
+    w, x, c, s, b = quantized_case(gs + m + k, n, k, gs, bits, w_dtype, m, "bf16", 0.02)
+    plan = B.nq_qmm_plan(m, n, k, gs, bits, torch.bfloat16,
+                         torch.float32 if w_dtype == "f32" else torch.bfloat16, row_exact=True)
+    assert plan.route == B.NQ_ROUTE_GEMV and plan.ksplit == 4
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    y = B.nq_qmm_row_exact(xs, *q, gs, bits) if m > 8 else B.nq_qmm(xs, *q, gs, bits)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), tolerance(y.dtype), "band")
+    for i in range(m):
+        assert bits_equal(B.nq_qmm(xs[i:i + 1].contiguous(), *q, gs, bits)[0], y[i]), i
+
+
+def test_gemv_band_unaligned_scales_keep_bits():
+    """Scales and biases that start on a 2-byte (not 4-byte) boundary are read
+    in place instead of through LDS: the same values, the same bits."""
+    n, k, gs, bits, m = 70, 2048, 64, 8, 5
+    w, x, c, s, b = quantized_case(5, n, k, gs, bits, "bf16", m, "bf16", 0.02)
+    xs, cs, ss, bs = dev(x), *gpu_quantized(c, s, b)
+    y = B.nq_qmm(xs, cs, ss, bs, gs, bits)
+
+    def shifted(t):   # the same values at a data pointer 2 bytes past a 4-byte boundary
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 4 == 2
+        return v
+    y2 = B.nq_qmm(xs, cs, shifted(ss), shifted(bs), gs, bits)
+    assert bits_equal(y, y2)
+    assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), tolerance(y.dtype), "band")
+
+
+def test_gemv_band_other_split_runs_the_vector_kernels():
+    """An explicit plan with a K split other than the family's four quarters
+    runs the VALU kernels: values within tolerance."""
+    n, k, gs, bits, m = 96, 2048, 128, 8, 4
+    w, x, c, s, b = quantized_case(6, n, k, gs, bits, "bf16", m, "bf16", 0.02)
+    xs, q = dev(x), gpu_quantized(c, s, b)
+    for ksplit in (1, 2):
+        plan = B.Plan()
+        plan.route, plan.ksplit, plan.rows_per_wave = B.NQ_ROUTE_GEMV, ksplit, 0
+        y = B.nq_qmm_with_plan(plan, xs, *q, gs, bits)
+        assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), tolerance(y.dtype), "split")
+
+
+def test_gemv_band_batched_and_gathered_rows_keep_bits():
+    """Batch items, per-row gather, the grouped row-exact gather (with an id
+    past the last expert: zero rows) and left indices at an 8-bit band shape
+    give every row the bits of its plain product."""
+    e, n, k, gs, bits = 3, 70, 2048, 64, 8
+    w, _ = synthetic.random_case(95, (e, n, k), (1, k), 0.02, "bf16")
+    c, s, b = O.quantize(w, gs, bits)
+    cs, ss, bs = dev(c), dev(s), dev(b)
+    _, xb = synthetic.random_case(96, (1, 1), (4, 3, k), 1.0, "f32", "bf16")
+    xbd = dev(xb)
+    yb = B.nq_qmm_batched(xbd, cs[1], ss[1], bs[1], gs, bits)
+    assert_rows_close(values(host(yb)).reshape(12, n), O.qmm_f64(xb.reshape(12, k), c[1], s[1], b[1], gs, bits),
+                      tolerance(yb.dtype), "batched")
+    for i in range(4):
+        assert bits_equal(B.nq_qmm(xbd[i].contiguous(), cs[1], ss[1], bs[1], gs, bits), yb[i]), i
+    for rows in (6, 40):   # per-row route, then the grouped row-exact route
+        _, xg = synthetic.random_case(97 + rows, (1, 1), (rows, 1, k), 1.0, "f32", "bf16")
+        ids = np.random.default_rng(rows).integers(0, e, size=rows, dtype=np.uint32)
+        ids[rows // 2] = e + 2   # past the last expert: a zero row
+        xgd = dev(xg)
+        yg = B.nq_gather_qmm_row_exact(xgd, cs, ss, bs, gs, bits, dev(ids))
+        assert_rows_close(values(host(yg)), O.gather_qmm_f64(xg, c, s, b, gs, bits, ids),
+                          tolerance(yg.dtype), "gather")
+        for r in range(rows):
+            if ids[r] >= e:
+                assert not torch.any(yg[r].float() != 0)
+                continue
+            yr = B.nq_qmm(xgd[r].contiguous(), cs[ids[r]], ss[ids[r]], bs[ids[r]], gs, bits)
+            assert bits_equal(yr, yg[r]), (rows, r)
+    # left indices: output row r reads x item lhs[r]
+    _, xl = synthetic.random_case(99, (1, 1), (7, 1, k), 1.0, "f32", "bf16")
+    xld = dev(xl)
+    rng = np.random.default_rng(9)
+    lhs = rng.integers(0, 7, size=24, dtype=np.uint32)
+    rhs = rng.integers(0, e, size=24, dtype=np.uint32)
+    yl = B.nq_gather_qmm_lhs(xld, cs, ss, bs, gs, bits, dev(lhs), dev(rhs), row_exact=True)
+    for r in range(24):
+        yr = B.nq_qmm(xld[lhs[r]].contiguous(), cs[rhs[r]], ss[rhs[r]], bs[rhs[r]], gs, bits)
+        assert bits_equal(yr, yl[r]), r
