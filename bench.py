@@ -41,6 +41,9 @@ CSRC = os.path.join(ROOT, "group_wise_affine_quantize_amd", "csrc")
 KERNEL_SOURCES = {
     "decode_gemv": ["gemv.hip", "nq_device.h", "nq_internal.h"],
     "prefill": ["tiled.hip", "nq_device.h", "nq_internal.h"],
+    "multirow_8bit": ["gemv_mfma.hip", "gemv.hip", "nq_device.h", "nq_internal.h"],
+    "splitk": ["gemv.hip", "nq_device.h", "nq_internal.h"],
+    "moe_gather": ["tiled.hip", "gemv.hip", "nq_device.h", "nq_internal.h"],
 }
 
 
@@ -52,17 +55,28 @@ def source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def profile_record(kind):
+    """The committed rocprofv3 figures of a workload's kernel (HBM bytes per
+    launch from the counter passes, average duration from the kernel trace),
+    if they were taken on the current kernel source; else {}."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kind)
     except (OSError, ValueError):
-        return None
+        return {}
     if not rec or rec.get("source_hash") != source_hash(kind):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return {}
+    return rec
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch (None when the counters predate the source)."""
+    return profile_record(kind).get("hbm_bytes_per_launch")
+
+
+def trace_avg_us(kind):
+    """The kernel trace's average duration in us (None when stale)."""
+    return profile_record(kind).get("trace_avg_us")
 
 
 def parse_args():
@@ -287,7 +301,8 @@ def main():
     out["roofline"] = {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                        "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                        "traffic": traffic, "kernel": "gemv_stream_kernel<bf16,2,14>",
-                       "launch_us": round(dec_launch_s * 1e6, 3)}
+                       "launch_us": round(dec_launch_s * 1e6, 3),
+                       "trace_avg_us": trace_avg_us("decode_gemv")}
     del copies2
 
     # ---------------------------------------------------------------- prefill
@@ -312,7 +327,8 @@ def main():
                    "flops_per_step": flops, "plan": plan4},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill"), "kernel": "tiled256_kernel<4,bf16>"},
+                     "traffic": measured_traffic("prefill"), "kernel": "tiled256_kernel<4,bf16>",
+                     "launch_us": round(pre_launch_s * 1e6, 3), "trace_avg_us": trace_avg_us("prefill")},
     }
 
     # ---------------------------------------------------------------- other rows
@@ -358,7 +374,8 @@ def main():
                 put(f"{name}_{tag}", t, steps, wb, "GB/s",
                     {"workload": f"x bf16 [{m},{k}] . W[{n},{k}]^T {wl.bits}-bit g{wl.group_size}",
                      "plan": B.nq_qmm_plan(m, n, k, wl.group_size, wl.bits, torch.bfloat16,
-                                           torch.bfloat16, tag == "row_exact").as_dict()})
+                                           torch.bfloat16, tag == "row_exact").as_dict(),
+                     "traffic": measured_traffic(name), "trace_avg_us": trace_avg_us(name)})
             del cps
 
         # the decode shape at the other code widths (3 and 6 straddle words)
@@ -410,10 +427,13 @@ def main():
                            (B.nq_gather_qmm_row_exact, "moe_gather_row_exact")):
             t = timer.run(lambda i: entry(xs, *cps[i % len(cps)], 64, 4, ids, y=yg, workspace=wsg),
                           steps, 10)
-            put(tag, t, steps, nbytes(*q), "GB/s",
-                {"workload": "x bf16 [512,1,2048], 32 experts W[1408,2048] 4-bit g64, "
-                             "unsorted ids (grouped by expert on the device)",
-                 "tflops": round(2 * 512 * 1408 * 2048 / (t / steps) / 1e12, 3)})
+            extra = {"workload": "x bf16 [512,1,2048], 32 experts W[1408,2048] 4-bit g64, "
+                                 "unsorted ids (grouped by expert on the device)",
+                     "tflops": round(2 * 512 * 1408 * 2048 / (t / steps) / 1e12, 3)}
+            if tag == "moe_gather":
+                extra.update({"traffic": measured_traffic("moe_gather"),
+                              "trace_avg_us": trace_avg_us("moe_gather")})
+            put(tag, t, steps, nbytes(*q), "GB/s", extra)
         del cps
 
         wl = synthetic.WORKLOADS["affine_f32_256x512"]
