@@ -1,7 +1,9 @@
 // Matrix-vector family of quantized products on gfx950 matrix cores: few
-// activation rows (a launch chunk of up to 32) times the quantized weights,
-// for bf16 activations and 4- or 8-bit codes (the routing takes it for
-// 4-bit codes only; see gemv_mfma_family).
+// activation rows times the quantized weights, for bf16 activations.  Two
+// kernels: gemv_mfma_kernel (launch chunks of up to 32 rows, 32 weight rows
+// per wave; the routing takes it for 4-bit codes, see gemv_mfma_family) and
+// gemv_band_kernel (8-bit codes; bands of 16 weight rows staged whole in
+// LDS, see gemv_band_family).
 //
 // Method: "Quantization" page of the nuvec documentation -- section "Affine"
 // (w ~ scale * code + bias per group; the product is x times the transposed
