@@ -138,6 +138,13 @@ nq_status check_plan(const char *op, const nq_plan *plan, int x_dt, int sb_dt, i
         if (plan->rows_per_wave != 0 && plan->rows_per_wave != 2 && plan->rows_per_wave != 4)
             return fail(NQ_ERR_PLAN, "%s: rows_per_wave=%d is not supported (0, 2 or 4)", op,
                         plan->rows_per_wave);
+        // the VALU kernels take 2 rows per wave for launch chunks of one or
+        // two activation rows and 4 for more (the matrix-core forms ignore it)
+        const int fit = std::min<int64_t>(m, 8) <= 2 ? 2 : 4;
+        if (plan->rows_per_wave != 0 && plan->rows_per_wave != fit &&
+            !nqk::gemv_mfma_family(n, k, gs, bits, x_dt))
+            return fail(NQ_ERR_PLAN, "%s: rows_per_wave=%d does not fit m=%lld (%d)", op,
+                        plan->rows_per_wave, (long long)m, fit);
         return NQ_OK;
     }
     if (plan->route == NQ_ROUTE_TILED) {

@@ -125,8 +125,10 @@ typedef enum { NQ_ROUTE_GEMV = 1, NQ_ROUTE_TILED = 2 } nq_route;
 typedef struct {
     int32_t route;          /* nq_route */
     int32_t ksplit;         /* GEMV: K slices per output row, 1..8 (1 = no split) */
-    int32_t rows_per_wave;  /* GEMV: weight rows per 64-lane wavefront: 2 or 4, 0 = chosen
-                               per launch chunk (it never changes a row's bits) */
+    int32_t rows_per_wave;  /* GEMV: weight rows per 64-lane wavefront: 0 = chosen per
+                               launch chunk (it never changes a row's bits), else the
+                               value that chunk takes -- 2 for m <= 2, 4 for more --
+                               or NQ_ERR_PLAN */
     int32_t tile_m;         /* TILED: rows of x per workgroup tile */
     int32_t tile_n;         /* TILED: weight rows per workgroup tile */
     int32_t reserved[3];    /* zero */

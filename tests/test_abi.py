@@ -205,6 +205,11 @@ def test_plan_errors(lib):
     st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, BF16, 4, 128, FAKE2, FAKE2 + 0x100000,
                               FAKE2 + 0x200000, BF16, 64, 64, 4, FAKE2 + 0x300000, 0, 0, None)
     assert st == NQ_ERR_PLAN
+    # 4 rows take 4 weight rows per wave in the VALU kernels (8-bit codes, k = 128)
+    p.route, p.ksplit, p.rows_per_wave = B.NQ_ROUTE_GEMV, 2, 2
+    st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, BF16, 4, 128, FAKE2, FAKE2 + 0x100000,
+                              FAKE2 + 0x200000, BF16, 64, 64, 8, FAKE2 + 0x300000, 0, 0, None)
+    assert st == NQ_ERR_PLAN and b"does not fit" in lib.nq_last_error()
     p.route, p.tile_m, p.tile_n = B.NQ_ROUTE_TILED, 128, 128
     st = lib.nq_qmm_with_plan(ctypes.byref(p), FAKE, F32, 4, 128, FAKE2, FAKE2 + 0x100000,
                               FAKE2 + 0x200000, BF16, 64, 64, 4, FAKE2 + 0x300000, 0, 0, None)
