@@ -64,24 +64,66 @@ __global__ void __launch_bounds__(256)
 quantize_kernel(const WT *__restrict__ w, int64_t chunks, int64_t k, int gs,
                 uint32_t *__restrict__ codes, WT *__restrict__ scales, WT *__restrict__ biases)
 {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // A wave's 64 chunks are one contiguous run of w, moved into LDS by
+    // direct-to-LDS loads that each cover 1 KB of the run (16 bytes every 64
+    // or 128 per instruction if each lane loaded its own chunk).  Instruction
+    // i, lane l takes the run's 16-byte piece 64 i + kPPC (l % kCPI) + l / kCPI
+    // into LDS slot 64 i + l, so that piece q of chunk c sits in slot
+    // 64 (c / kCPI) + kCPI q + c % kCPI: a lane's q-th read and its 15
+    // neighbours' touch 16 consecutive slots (bf16; two such runs for f32).
+    constexpr int kPPC = kLaneChunk * (int)sizeof(WT) / 16;   // pieces per chunk: 4 (bf16), 8 (f32)
+    constexpr int kCPI = 64 / kPPC;                           // chunks per load instruction
+    constexpr int kEPP = 16 / (int)sizeof(WT);                // elements per piece
+    __shared__ uint4 stage[4][64 * kPPC];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * blockDim.x + wave * 64;   // the wave's first chunk
+    const int64_t c = c0 + lane;
     const bool valid = c < chunks;
     const int lanes_per_group = gs / kLaneChunk;   // 1, 2 or 4, adjacent lanes
     const float top = (float)((1u << BITS) - 1u);
 
+    if (c0 >= chunks) return;   // the whole wave is past the end (no barriers here)
     float v[kLaneChunk];
-    if (valid) {
-        load32_f32<WT>(w + c * kLaneChunk, v);
-    } else {
+    {
+        // pieces past the end of w re-read its last piece (the lanes they
+        // reach are past the end too, and their groups hold no valid lane)
+        const int64_t last_piece = min((chunks - c0) * kPPC, (int64_t)64 * kPPC) - 1;
+        const WT *run = w + c0 * kLaneChunk;
 #pragma unroll
-        for (int j = 0; j < kLaneChunk; ++j) v[j] = 0.0f;
+        for (int i = 0; i < kPPC; ++i) {
+            const int64_t piece = min((int64_t)(64 * i + kPPC * (lane % kCPI) + lane / kCPI), last_piece);
+            __builtin_amdgcn_global_load_lds((const void *)(run + piece * kEPP),
+                                             (__attribute__((address_space(3))) void *)(stage[wave] + 64 * i),
+                                             16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xf70);   // vmcnt(0): this wave's pieces are in LDS
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < kPPC; ++q) {
+            const uint4 d = stage[wave][64 * (lane / kCPI) + kCPI * q + lane % kCPI];
+            const uint32_t u[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(WT) == 2) {
+                    v[kEPP * q + 2 * j] = __uint_as_float(u[j] << 16);
+                    v[kEPP * q + 2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+                } else {
+                    v[kEPP * q + j] = __uint_as_float(u[j]);
+                }
+            }
+        }
     }
+    // Three-input hardware min and max (weights are finite by contract; the
+    // sign of a zero extreme is dropped below, so ties between -0 and +0 do
+    // not matter).
     float mn = v[0], mx = v[0];
 #pragma unroll
-    for (int j = 1; j < kLaneChunk; ++j) {
-        mn = v[j] < mn ? v[j] : mn;
-        mx = v[j] > mx ? v[j] : mx;
+    for (int j = 1; j + 1 < kLaneChunk; j += 2) {
+        asm("v_min3_f32 %0, %1, %2, %3" : "=v"(mn) : "v"(mn), "v"(v[j]), "v"(v[j + 1]));
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(v[j]), "v"(v[j + 1]));
     }
+    asm("v_min_f32 %0, %1, %2" : "=v"(mn) : "v"(mn), "v"(v[kLaneChunk - 1]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(mx), "v"(v[kLaneChunk - 1]));
     // A group's lanes are all valid or all invalid (k is a multiple of gs).
     for (int off = 1; off < lanes_per_group; off <<= 1) {
         const float omn = __shfl_xor(mn, off);
@@ -99,27 +141,61 @@ quantize_kernel(const WT *__restrict__ w, int64_t chunks, int64_t k, int gs,
     const float s = Elt<WT>::stored(scale);
     const float b = Elt<WT>::stored(mn);
 
-    const int64_t chunks_per_row = k / kLaneChunk;
-    const int64_t row = c / chunks_per_row;
-    const int64_t cir = c - row * chunks_per_row;
-    if (cir % lanes_per_group == 0) {
-        const int64_t gi = row * (k / gs) + cir / lanes_per_group;
+    // A row is k / gs whole groups of lanes_per_group chunks, so chunk c
+    // belongs to group c / lanes_per_group (row-major over [n, k / gs]).
+    if ((c & (lanes_per_group - 1)) == 0) {
+        const int64_t gi = c >> (lanes_per_group == 4 ? 2 : lanes_per_group - 1);
         Elt<WT>::store(scales, gi, scale);
         Elt<WT>::store(biases, gi, mn);
     }
 
+    // Code = clamp(rint(t), 0, top) with t = (v - b) / s rounded once (IEEE
+    // division; 0 when s is 0).  No division runs per element: with r within
+    // 1 ulp of 1 / s (v_rcp_f32), t0 = (v - b) * r is within
+    // 4.0000003 u |t0| of t (u = 2^-24).  Where t0 is more than
+    // 2^-21 (1 + |t0|) from the nearest half-integer, t lies strictly inside
+    // the same unit interval as t0, so rint(t) = rint(t0).  Elements nearer
+    // a half-integer (a few in 10^4 for spread values), and every element
+    // of a group whose scale is 0 or outside [2^-120, 2^120] (where r or t0
+    // could leave the normal range), take the division itself.
+    // The margin test's value is a non-negative float or NaN, so comparing
+    // its bits as unsigned integers orders it as a float with NaN above all:
+    // one running maximum per lane says whether any element failed.
+    // Up to 7 bits the fast codes need no clamp: 0 <= v - b <= max - min, so
+    // 0 <= t0 <= top (1 + 2^-9 + 4 u) (the stored scale is at most 2^-9 below
+    // (max - min) / top), which rounds to at most top.
+    const bool s_ok = s >= 0x1p-120f && s <= 0x1p120f;
+    const float r = __builtin_amdgcn_rcpf(s_ok ? s : 1.0f);
+    constexpr float kMargin = 0.5f - 0x1p-20f;
+    constexpr bool kClampFast = BITS == 8;
+    auto margin = [](float t0, float m) { return fmaf(fabsf(t0), 0x1p-21f, fabsf(t0 - m)); };
+    auto clamp = [&](float t) {
+        float o;   // [0, top] in one instruction (the codes are finite)
+        asm("v_med3_f32 %0, %1, 0, %2" : "=v"(o) : "v"(t), "v"(top));
+        return o;
+    };
+    float tq[kLaneChunk];
+    uint32_t worst = s_ok ? 0u : 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < kLaneChunk; ++j) {
+        const float t0 = (v[j] - b) * r;
+        tq[j] = rintf(t0);
+        worst = max(worst, __float_as_uint(margin(t0, tq[j])));
+    }
+    if (worst >= __float_as_uint(kMargin)) {
+#pragma unroll
+        for (int j = 0; j < kLaneChunk; ++j) {
+            const float d = v[j] - b;
+            const float t0 = d * r;
+            if (!(s_ok && margin(t0, rintf(t0)) < kMargin)) tq[j] = s != 0.0f ? clamp(rintf(d / s)) : 0.0f;
+        }
+    }
     uint32_t wd[BITS];
 #pragma unroll
     for (int i = 0; i < BITS; ++i) wd[i] = 0u;
 #pragma unroll
     for (int j = 0; j < kLaneChunk; ++j) {
-        uint32_t q = 0u;
-        if (s != 0.0f) {
-            float t = (v[j] - b) / s;
-            t = rintf(t);
-            t = fminf(fmaxf(t, 0.0f), top);
-            q = (uint32_t)t;
-        }
+        const uint32_t q = (uint32_t)(kClampFast ? clamp(tq[j]) : tq[j]);
         const int bit = j * BITS;
         wd[bit >> 5] |= q << (bit & 31);
         if ((bit & 31) + BITS > 32) wd[(bit >> 5) + 1] |= q >> (32 - (bit & 31));

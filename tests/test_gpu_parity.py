@@ -69,6 +69,52 @@ def test_quantize_bit_exact(bits, gs, w_dtype):
     assert np.array_equal(host(b).view(np.uint8), b_ref.view(np.uint8))
 
 
+def near_half_level_rows(seed, n, k, gs, bits, w_dtype):
+    """Rows whose groups span [mn, mn + top * S] exactly (first two elements)
+    and whose other elements sit within a few ulps of the half levels
+    mn + (j + 1/2) s of the stored scale s, where the code's rounding is
+    decided by the last bits of (w - b) / s; S spans 2^-30 .. 2^30."""
+    rng = np.random.default_rng(seed)
+    top = np.float32((1 << bits) - 1)
+    bf16 = w_dtype == "bf16"
+    rnd = (lambda a: values(synthetic.to_bf16_bits(np.asarray(a, np.float32))).astype(np.float32)
+           .reshape(np.shape(a))) if bf16 else (lambda a: np.asarray(a, np.float32))
+    ulp_scale = np.float32(2.0 ** 16 if bf16 else 1.0)   # a bf16 ulp is 2^16 float32 ulps
+    w = np.zeros((n, k), np.float32)
+    for r in range(n):
+        for g in range(k // gs):
+            mag = np.float32(2.0 ** rng.integers(-30, 31))
+            mn = rnd(np.float32(rng.uniform(-1, 1)) * mag * top)
+            mx = rnd(mn + np.float32(rng.uniform(0.5, 2.0)) * mag * top)
+            s = rnd(np.float32(np.float32(mx - mn) / top))   # the stored scale
+            lev = rng.integers(0, int(top), gs - 2).astype(np.float32) + np.float32(0.5)
+            t = rnd(mn + lev * s)
+            # move each value by -4 .. +4 ulps of its own storage format
+            steps = rng.integers(-4, 5, gs - 2).astype(np.float32)
+            t = rnd(t + steps * np.spacing(t) * ulp_scale)
+            grp = np.concatenate([[mn, mx], np.clip(t, mn, mx)]).astype(np.float32)
+            w[r, g * gs:(g + 1) * gs] = grp
+    return synthetic.to_bf16_bits(w) if bf16 else w
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_quantize_near_half_levels(bits, gs, w_dtype):
+    """Codes decided within a few ulps of a rounding boundary: the kernel
+    multiplies by the reciprocal scale where that provably gives the same
+    code as the division and divides elsewhere; every code must still be
+    the oracle's (one correctly rounded division per element)."""
+    n, k = 24, 4 * gs
+    w = near_half_level_rows(bits * 100 + gs, n, k, gs, bits, w_dtype)
+    c_ref, s_ref, b_ref = O.quantize(w, gs, bits)
+    c, s, b = B.nq_quantize(dev(w), gs, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c), c_ref)
+    assert np.array_equal(host(s).view(np.uint8), s_ref.view(np.uint8))
+    assert np.array_equal(host(b).view(np.uint8), b_ref.view(np.uint8))
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("sb_dtype", ["f32", "bf16"])
