@@ -33,6 +33,7 @@
 
 #include "nq_device.h"
 #include "nq_internal.h"
+#include "nq_tiles.h"
 
 namespace nqk {
 
@@ -833,7 +834,10 @@ __global__ void __launch_bounds__(256) fp_tiled_kernel(FpTiledParams p)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kFpTM, n0 = (int64_t)blockIdx.x * kFpTN;
+    int tm, tn;
+    if (!xcd_panel_tile(blockIdx.x, (int)((p.m + kFpTM - 1) / kFpTM), (int)((p.n + kFpTN - 1) / kFpTN), tm, tn))
+        return;
+    const int64_t m0 = (int64_t)tm * kFpTM, n0 = (int64_t)tn * kFpTN;
     const int lrow = tid >> 1, lhalf = tid & 1;
     const int64_t xm = m0 + lrow, wr = n0 + lrow;
     const int64_t xmc = min(xm, p.m - 1), wrc = min(wr, p.n - 1);
@@ -1094,7 +1098,9 @@ __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
     __shared__ __attribute__((aligned(16))) bf16_bits ws[128 * 72 + 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+    int tm, tn;
+    if (!xcd_panel_tile(blockIdx.x, (int)((p.mr + 127) / 128), (int)((p.nc + 127) / 128), tm, tn)) return;
+    const int64_t m0 = (int64_t)tm * 128, c0 = (int64_t)tn * 128;
     const int lrow = tid >> 1, lhalf = tid & 1;
     const int64_t xm = m0 + lrow, xmc = min(xm, p.mr - 1);
     const int wrow = tid >> 2, wcol = 32 * (tid & 3);
@@ -1356,8 +1362,10 @@ template <int MODE> struct QmmRun {
             p.x = static_cast<const bf16_bits *>(a.x), p.y = static_cast<bf16_bits *>(a.y);
             p.codes = a.codes, p.scales = a.scales, p.gscale = a.gscale;
             p.m = a.vpi, p.n = a.n, p.k = a.k;
-            const dim3 grid((unsigned)((a.n + kFpTN - 1) / kFpTN), (unsigned)((a.vpi + kFpTM - 1) / kFpTM));
-            fp_tiled_kernel<MODE><<<grid, 256, 0, stream>>>(p);
+            const int64_t tiles = ((a.n + kFpTN - 1) / kFpTN) * ((a.vpi + kFpTM - 1) / kFpTM);
+            const unsigned blocks = xcd_panel_blocks(tiles);
+            if (blocks == 0) return hipErrorInvalidValue;
+            fp_tiled_kernel<MODE><<<dim3(blocks), 256, 0, stream>>>(p);
             return hipGetLastError();
         }
         const int64_t v = a.chunks ? kGroupChunk : a.vpi;
@@ -1412,8 +1420,10 @@ template <int MODE> struct NtRun {
         p.ni = a.ni, p.nc = a.nc;
         if (a.tiled) {
             p.mr = a.m;
-            const dim3 grid((unsigned)((a.nc + 127) / 128), (unsigned)((a.m + 127) / 128));
-            fp_tiled_nt_kernel<MODE><<<grid, 256, 0, stream>>>(p);
+            const int64_t tiles = ((a.nc + 127) / 128) * ((a.m + 127) / 128);
+            const unsigned blocks = xcd_panel_blocks(tiles);
+            if (blocks == 0) return hipErrorInvalidValue;
+            fp_tiled_nt_kernel<MODE><<<dim3(blocks), 256, 0, stream>>>(p);
             return hipGetLastError();
         }
         p.part = static_cast<float *>(a.workspace);

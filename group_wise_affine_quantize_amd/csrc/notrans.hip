@@ -16,6 +16,7 @@
 
 #include "nq_device.h"
 #include "nq_internal.h"
+#include "nq_tiles.h"
 
 namespace nqk {
 
@@ -260,8 +261,11 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kNtTM;
-    const int64_t c0 = (int64_t)blockIdx.x * kNtTN;
+    int tm, tn;
+    if (!xcd_panel_tile(blockIdx.x, (int)((p.m + kNtTM - 1) / kNtTM), (int)((p.nc + kNtTN - 1) / kNtTN), tm, tn))
+        return;
+    const int64_t m0 = (int64_t)tm * kNtTM;
+    const int64_t c0 = (int64_t)tn * kNtTN;
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -506,8 +510,10 @@ hipError_t tiled_nt_run(const NtLaunch &a, hipStream_t stream)
     p.groups_per_row = a.nc / a.gs;
     p.lg_gs = lg_of(a.gs);
     if (a.ni % kNtBK != 0) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((a.nc + kNtTN - 1) / kNtTN), (unsigned)((a.m + kNtTM - 1) / kNtTM));
-    tiled_nt_kernel<BITS, ST><<<grid, dim3(256), 0, stream>>>(p);
+    const int64_t tiles = ((a.nc + kNtTN - 1) / kNtTN) * ((a.m + kNtTM - 1) / kNtTM);
+    const unsigned blocks = xcd_panel_blocks(tiles);
+    if (blocks == 0) return hipErrorInvalidValue;
+    tiled_nt_kernel<BITS, ST><<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -1,0 +1,36 @@
+// Workgroup-to-tile mapping for the 128 x 128 tile kernels (the products
+// with the weights as stored and the floating-point tiled product).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace nqk {
+
+// Tile of workgroup b in a grid of tiles_m x tiles_n output tiles, for
+// kernels launched with 8 * ceil(tiles_m * tiles_n / 8) workgroups.
+// Workgroups are dealt to the 8 XCDs round-robin (b on XCD b % 8), and XCD x
+// takes the x-th eighth of a tile list that runs through panels of 4 tile
+// rows, column by column inside a panel: the tiles one XCD holds at once
+// then share 4 row tiles of the activations and a band of weight columns in
+// that XCD's L2, instead of every XCD reading every activation row.  False
+// for the workgroups past the last tile.
+__device__ __forceinline__ bool xcd_panel_tile(int b, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n, per_xcd = (total + 7) / 8;
+    const int t = (b % 8) * per_xcd + b / 8;
+    if (t >= total) return false;
+    const int per_panel = 4 * tiles_n, p0 = t / per_panel * 4, in_panel = t % per_panel;
+    const int h = min(4, tiles_m - p0);
+    tm = p0 + in_panel % h;
+    tn = in_panel / h;
+    return true;
+}
+
+// Workgroups to launch for `tiles` tiles (a multiple of 8), or 0 when the
+// tile count does not fit the 32-bit index arithmetic.
+inline unsigned xcd_panel_blocks(int64_t tiles)
+{
+    return tiles >= ((int64_t)1 << 31) - 8 ? 0u : (unsigned)((tiles + 7) / 8 * 8);
+}
+
+}  // namespace nqk

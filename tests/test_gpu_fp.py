@@ -100,6 +100,7 @@ def test_products_pick_every_element_exactly(mode, route):
     (8, 128, 2048 + 96, "bf16", False),
     (40, 200, 320, "bf16", False),      # tiles, ragged m and n
     (130, 260, 448, "bf16", False),     # several tiles
+    (700, 650, 256, "bf16", False),     # 6 x 6 tiles: a partial panel of tile rows, 36 tiles
     (40, 200, 96, "bf16", False),       # k not a multiple of 64: matrix-vector chunks
     (13, 150, 320, "bf16", True),
     (20, 64, 256, "f32", False),
@@ -307,6 +308,7 @@ def test_gather_matrix_core_moe_shape():
     (5, 448, 256, "bf16", True),
     (40, 320, 224, "bf16", False),                # tiles, ragged nc
     (130, 448, 96, "bf16", False),                # several row tiles, nc < one tile
+    (700, 192, 640, "bf16", False),               # 6 x 5 tiles: a partial panel, 30 tiles
 ])
 def test_notrans_matches_oracle(mode, m, ni, nc, dtype, row_exact):
     words, scales = codes_case(30 + m, (ni,), nc, mode)

@@ -240,6 +240,36 @@ def test_tiled256_parity(bits, gs, w_dtype, m, n, k):
     assert_rows_close(values(host(y)), O.qmm_f64(x, c, s, b, gs, bits), 1e-2, "tiled256")
 
 
+@pytest.mark.parametrize("m,n,k,gs,bits,w_dtype", [
+    (1892, 14180, 512, 64, 4, "bf16"),   # 8 x 56 tiles of 256 x 256, ragged m and n
+    (2048, 12200, 256, 128, 8, "f32"),   # 8 x 48 tiles, ragged n
+])
+def test_tiled256_column_slices_keep_bits(m, n, k, gs, bits, w_dtype):
+    """An output's bits do not depend on where its tile sits or how many
+    tiles the launch has: each 2048-column slice of y equals, bit for bit,
+    the product with that slice of the weight rows alone.  Whole rows and
+    scattered outputs are checked against the oracle."""
+    w, x, c, s, b = quantized_case(m + n + bits, n, k, gs, bits, w_dtype, m, "bf16", 0.02)
+    xs = dev(x)
+    cg, sg, bg = gpu_quantized(c, s, b)
+    sb_dtype = torch.bfloat16 if w_dtype == "bf16" else torch.float32
+    assert B.nq_qmm_plan(m, n, k, gs, bits, torch.bfloat16, sb_dtype).tile_m == 256
+    y = B.nq_qmm(xs, cg, sg, bg, gs, bits)
+    for n0 in range(0, n, 2048):
+        n1 = min(n, n0 + 2048)
+        ys = B.nq_qmm(xs, cg[n0:n1].contiguous(), sg[n0:n1].contiguous(), bg[n0:n1].contiguous(), gs, bits)
+        assert bits_equal(y[:, n0:n1].contiguous(), ys), n0
+    yv = values(host(y))
+    rows = np.array([0, 1, 127, 128, 255, 256, 1023, 1535, 1536, m - 1])
+    y_ref = O.qmm_f64(x[rows], c, s, b, gs, bits)
+    assert_rows_close(yv[rows], y_ref, 1e-2, "tiled256 rows")
+    rng = np.random.default_rng(11)
+    ms = np.concatenate([rng.integers(0, m, 6000), [0, m - 1, 1535, 1536]])
+    ns = np.concatenate([rng.integers(0, n, 6000), [0, n - 1, 8191, 8192]])
+    ref = O.qmm_sample_f64(x, c, s, b, gs, bits, ms, ns)
+    assert np.max(np.abs(yv[ms, ns] - ref)) <= 1e-2 * np.max(np.abs(y_ref))
+
+
 def test_tiled_is_chosen_for_many_rows():
     for m, n, k, tile in [(200, 192, 1024, 128), (300, 600, 1024, 256)]:
         gs, bits = 64, 4
@@ -567,6 +597,7 @@ def test_other_widths_gather(bits, rows):
     (30, 192, 320, 64, 6, "bf16", "bf16"),     # tiles, three K steps, ragged m and nc
     (200, 512, 384, 64, 4, "bf16", "bf16"),    # 128-row tiles
     (150, 320, 4160, 64, 5, "bf16", "bf16"),   # tiles, odd width, ragged m and nc
+    (700, 256, 640, 64, 4, "bf16", "bf16"),    # 6 x 5 tiles: a partial panel of tile rows, 30 tiles
 ])
 def test_qmm_notrans(m, ni, nc, gs, bits, x_dtype, w_dtype):
     """x times the weights as stored against the oracle; row-exact rows (and
