@@ -229,9 +229,9 @@ qmm_nt_reduce_kernel(const float *part, XT *y, int64_t m0, int mrows, int64_t nc
 // rows i of 128 columns c) is dequantized from the rows as stored and written
 // to LDS transposed, [c][i], so that the B operands read 8 consecutive i of
 // one column.  Each thread dequantizes 32 columns of one row (a run of
-// codes that starts on a word) into round_bf16(fmaf(s, q, b)).  The next K step's
-// loads are issued before this step's MFMAs, so they are in flight while the
-// matrix cores run.
+// codes that starts on a word) into round_bf16(fmaf(s, q, b)).  The tiles are
+// double buffered in LDS and a step's global loads are issued two steps
+// ahead, so they are in flight while the matrix cores run.
 
 template <typename ST>
 struct NtTiledParams {
@@ -256,8 +256,10 @@ constexpr int kNtWsElems = kNtTN * kNtLd + 64;
 template <int BITS, typename ST>
 __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
 {
-    __shared__ __attribute__((aligned(16))) bf16_bits xs[kNtTM * kNtLd];
-    __shared__ __attribute__((aligned(16))) bf16_bits ws[kNtWsElems];
+    // two LDS buffers for the x and weight tiles: step j is staged into
+    // buffer j % 2 while the MFMAs of step j - 1 read the other one
+    __shared__ __attribute__((aligned(16))) bf16_bits xs[2][kNtTM * kNtLd];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[2][kNtWsElems];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -280,67 +282,111 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
     const int64_t g = (wv_ok ? cb : 0) >> p.lg_gs;
     constexpr int NW = BITS;   // 32 codes from a word boundary (32 columns x bits)
 
+    // One K step's global data for this thread: 32 activations, a run of 32
+    // codes and the raw storage bits of its scale and bias (converted only
+    // when used, so that no conversion waits on the load early).
     struct Ld {
         uint4 x[4];
         uint32_t raw[NW];
-        float s, b;
+        uint32_t s, b;
     };
-    const int64_t xmc = min(xm, p.m - 1);   // rows past m read row m - 1 (not stored)
-    const int64_t cbc = wv_ok ? cb : 0;     // columns past nc read column 0 (dropped)
-    auto load = [&](int64_t i0, Ld &l) {
+    // Rows past m read row m - 1 and columns past nc read column 0: their
+    // products land only in outputs past m or nc, which are never stored.
+    const int64_t xmc = min(xm, p.m - 1);
+    const int64_t cbc = wv_ok ? cb : 0;
+    auto raw_of = [](const ST *a, int64_t i) -> uint32_t {
+        if constexpr (sizeof(ST) == 2) return (uint32_t)a[i];
+        else return __float_as_uint(a[i]);
+    };
+    auto f32_of = [](uint32_t v) -> float { return sizeof(ST) == 2 ? __uint_as_float(v << 16) : __uint_as_float(v); };
+    auto load = [&](int step, Ld &l) {
+        const int64_t i0 = (int64_t)step * kNtBK;
         const uint4 *src = reinterpret_cast<const uint4 *>(p.x + xmc * p.ni + i0 + 32 * lhalf);
 #pragma unroll
         for (int u = 0; u < 4; ++u) l.x[u] = src[u];
         const int64_t i = i0 + wrow;
-        l.s = Elt<ST>::load(p.scales, i * p.groups_per_row + g);
-        l.b = Elt<ST>::load(p.biases, i * p.groups_per_row + g);
+        l.s = raw_of(p.scales, i * p.groups_per_row + g);
+        l.b = raw_of(p.biases, i * p.groups_per_row + g);
         load_run<BITS>(p.codes + i * p.words_per_row + ((cbc * BITS) >> 5), l.raw);
     };
     typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
     typedef float f32x2_v __attribute__((ext_vector_type(2)));
-    Ld cur, nxt;
-    if (p.ni > 0) load(0, cur);
-    for (int64_t i0 = 0; i0 < p.ni; i0 += kNtBK) {       // ni is a multiple of 64
+    // dequantize a step's weights, round_bf16(fmaf(s, q, b)), and write them
+    // with its activations into LDS buffer B (the weights transposed)
+    auto stage = [&](const Ld &l, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        const float sc = f32_of(l.s), bi = f32_of(l.b);
         uint32_t outw[16];
-        {
-            float qf[kLaneChunk];
-            codes_f32<BITS>(cur.raw, qf);
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16 for finite values
-                const f32x2_v f = {wv_ok ? fmaf(cur.s, qf[2 * u], cur.b) : 0.0f,
-                                   wv_ok ? fmaf(cur.s, qf[2 * u + 1], cur.b) : 0.0f};
-                outw[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
-            }
-        }
-        __syncthreads();   // the previous step's MFMA reads are done
-        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * kNtLd + 32 * lhalf);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xd[u] = xm < p.m ? cur.x[u] : make_uint4(0u, 0u, 0u, 0u);
+        float qf[kLaneChunk];
+        codes_f32<BITS>(l.raw, qf);
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            ws[nt_wcol(wcol + 2 * u) + wrow] = (bf16_bits)(outw[u] & 0xffffu);
-            ws[nt_wcol(wcol + 2 * u + 1) + wrow] = (bf16_bits)(outw[u] >> 16);
+            // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16 for finite values
+            const f32x2_v f = {fmaf(sc, qf[2 * u], bi), fmaf(sc, qf[2 * u + 1], bi)};
+            outw[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
         }
-        if (i0 + kNtBK < p.ni) load(i0 + kNtBK, nxt);   // in flight during this step's MFMAs
-        __syncthreads();
+        uint4 *xd = reinterpret_cast<uint4 *>(xs[B] + lrow * kNtLd + 32 * lhalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xd[u] = make_uint4(l.x[u].x, l.x[u].y, l.x[u].z, l.x[u].w);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            ws[B][nt_wcol(wcol + 2 * u) + wrow] = (bf16_bits)(outw[u] & 0xffffu);
+            ws[B][nt_wcol(wcol + 2 * u + 1) + wrow] = (bf16_bits)(outw[u] >> 16);
+        }
+    };
+    auto mfmas = [&](auto bufc) {
+        constexpr int B = decltype(bufc)::value;
 #pragma unroll
         for (int ks = 0; ks < kNtBK / 16; ++ks) {
             const int kk = ks * 16 + 8 * (lane >> 5);
             bf16x8_t a[2], bo[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t *>(xs + (wm * 64 + i * 32 + (lane & 31)) * kNtLd + kk);
+                a[i] = *reinterpret_cast<const bf16x8_t *>(xs[B] + (wm * 64 + i * 32 + (lane & 31)) * kNtLd + kk);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bo[j] = *reinterpret_cast<const bf16x8_t *>(ws + nt_wcol(wn * 64 + j * 32 + (lane & 31)) + kk);
+                bo[j] = *reinterpret_cast<const bf16x8_t *>(ws[B] + nt_wcol(wn * 64 + j * 32 + (lane & 31)) + kk);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bo[j], acc[i][j], 0, 0, 0);
         }
-        cur = nxt;
+    };
+
+    // Step j's global data sits in ld[j % 2]; it is loaded two steps before
+    // its MFMAs and staged one step before them.  One barrier per step, which
+    // waits for LDS accesses only: the loads of the next two steps stay in
+    // flight across it.  At step j the MFMAs read buffer j % 2 (staged before
+    // the previous barrier), then step j + 1 is staged into the other buffer,
+    // whose last reader, step j - 1, every wave finished before that barrier.
+    // Inside the loop every load and stage is unconditional, with step
+    // indices past the last clamped to it (re-reading the last step, staged
+    // into a buffer nothing reads any more), so the same loads are in flight
+    // at every step and the compiler's waits count only the step it uses.
+    const int steps = (int)(p.ni / kNtBK);   // ni is a multiple of 64
+    const int last = steps - 1;
+    Ld ld[2];
+    auto step = [&](int j, auto parc) {
+        constexpr int B = decltype(parc)::value;
+        mfmas(parc);
+        stage(ld[B ^ 1], std::integral_constant<int, B ^ 1>{});
+        load(min(j + 3, last), ld[B ^ 1]);
+        lds_barrier();
+    };
+    if (steps > 0) {
+        load(0, ld[0]);
+        load(min(1, last), ld[1]);
+        stage(ld[0], std::integral_constant<int, 0>{});
+        load(min(2, last), ld[0]);
+        lds_barrier();
+        int j = 0;
+        for (; j + 1 < steps; j += 2) {
+            step(j, std::integral_constant<int, 0>{});
+            step(j + 1, std::integral_constant<int, 1>{});
+        }
+        if (j < steps) mfmas(std::integral_constant<int, 0>{});   // an odd last step, staged in buffer 0
+        __builtin_amdgcn_s_waitcnt(0);   // the clamped prefetches
     }
     // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
 #pragma unroll

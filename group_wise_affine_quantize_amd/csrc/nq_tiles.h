@@ -26,6 +26,24 @@ __device__ __forceinline__ bool xcd_panel_tile(int b, int tiles_m, int tiles_n, 
     return true;
 }
 
+// Workgroup barrier that waits only for this wave's LDS accesses (and
+// scalar loads), leaving its global loads in flight: __syncthreads() would
+// also wait for every outstanding global load.  s_waitcnt fields on gfx9:
+// vmcnt in bits 3:0 and 15:14 (all ones: no wait), expcnt in bits 6:4 (7: no
+// wait), lgkmcnt in bits 11:8 (0).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier, and the
+// scheduling barriers any other instruction: arithmetic on data of a later
+// step stays after it, so that its wait for that data does too.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroups to launch for `tiles` tiles (a multiple of 8), or 0 when the
 // tile count does not fit the 32-bit index arithmetic.
 inline unsigned xcd_panel_blocks(int64_t tiles)
