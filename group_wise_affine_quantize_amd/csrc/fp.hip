@@ -1094,19 +1094,20 @@ template <int MODE>
 __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
 {
     constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
-    __shared__ __attribute__((aligned(16))) bf16_bits xs[128 * 72];
-    __shared__ __attribute__((aligned(16))) bf16_bits ws[128 * 72 + 64];
+    __shared__ __attribute__((aligned(16))) bf16_bits xs[2][128 * 72];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[2][128 * 72 + 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
     if (!xcd_panel_tile(blockIdx.x, (int)((p.mr + 127) / 128), (int)((p.nc + 127) / 128), tm, tn)) return;
     const int64_t m0 = (int64_t)tm * 128, c0 = (int64_t)tn * 128;
     const int lrow = tid >> 1, lhalf = tid & 1;
-    const int64_t xm = m0 + lrow, xmc = min(xm, p.mr - 1);
+    // rows past mr read row mr - 1 and columns past nc column 0: their
+    // products land only in outputs that are not stored
+    const int64_t xmc = min(m0 + lrow, p.mr - 1);
     const int wrow = tid >> 2, wcol = 32 * (tid & 3);
     const int64_t cb = c0 + wcol;
-    const bool wok = cb < p.nc;
-    const int64_t cbc = wok ? cb : 0;
+    const int64_t cbc = cb < p.nc ? cb : 0;
     const int64_t wpr = p.nc * BITS / 32, gpr = p.nc / GS;
     const bf16_bits *x = static_cast<const bf16_bits *>(p.x);
     const int nsteps = (int)(p.ni / 64);
@@ -1127,10 +1128,11 @@ __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
 #pragma unroll
         for (int g = 0; g < NG; ++g) l.s[g] = p.scales[i * gpr + cbc / GS + g];
     };
-    auto store = [&](const Ld &l) {
-        uint4 *xd = reinterpret_cast<uint4 *>(xs + lrow * 72 + 32 * lhalf);
+    auto store = [&](const Ld &l, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        uint4 *xd = reinterpret_cast<uint4 *>(xs[B] + lrow * 72 + 32 * lhalf);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) xd[u] = xm < p.mr ? l.x[u] : make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < 4; ++u) xd[u] = make_uint4(l.x[u].x, l.x[u].y, l.x[u].z, l.x[u].w);
         uint32_t wd[BITS];
 #pragma unroll
         for (int u = 0; u < BITS / 4; ++u)
@@ -1143,14 +1145,14 @@ __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
                 const int pi = g * (GS / 2) + q;
                 uint32_t h;
                 if constexpr (Fp<MODE>::e8m0) {
-                    h = wok ? __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S)) : 0u;
+                    h = __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S));
                 } else {
                     const f32x2_t e = pair_f32<MODE>(wd, pi);
-                    const f32x2_t v = {wok ? S * e[0] : 0.0f, wok ? S * e[1] : 0.0f};
+                    const f32x2_t v = {S * e[0], S * e[1]};
                     h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
                 }
-                ws[fp_nt_wcol(wcol + 2 * pi) + wrow] = (bf16_bits)(h & 0xffffu);
-                ws[fp_nt_wcol(wcol + 2 * pi + 1) + wrow] = (bf16_bits)(h >> 16);
+                ws[B][fp_nt_wcol(wcol + 2 * pi) + wrow] = (bf16_bits)(h & 0xffffu);
+                ws[B][fp_nt_wcol(wcol + 2 * pi + 1) + wrow] = (bf16_bits)(h >> 16);
             }
         }
     };
@@ -1159,31 +1161,26 @@ __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-    Ld cur, nxt;
-    if (nsteps > 0) load(0, cur);
-    for (int step = 0; step < nsteps; ++step) {
-        store(cur);
-        __syncthreads();
-        if (step + 1 < nsteps) load(step + 1, nxt);
+    auto mfmas = [&](auto bufc) {
+        constexpr int B = decltype(bufc)::value;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kk = ks * 16 + 8 * (lane >> 5);
             bf16x8_t a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t *>(xs + (wm * 64 + i * 32 + (lane & 31)) * 72 + kk);
+                a[i] = *reinterpret_cast<const bf16x8_t *>(xs[B] + (wm * 64 + i * 32 + (lane & 31)) * 72 + kk);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const bf16x8_t *>(ws + fp_nt_wcol(wn * 64 + j * 32 + (lane & 31)) + kk);
+                b[j] = *reinterpret_cast<const bf16x8_t *>(ws[B] + fp_nt_wcol(wn * 64 + j * 32 + (lane & 31)) + kk);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        __syncthreads();
-        cur = nxt;
-    }
+    };
+    tile_pipeline<Ld>(nsteps, load, store, mfmas);
     const float gsc = p.gscale ? *p.gscale : 1.0f;
     bf16_bits *y = static_cast<bf16_bits *>(p.y);
 #pragma unroll

@@ -354,40 +354,7 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
         }
     };
 
-    // Step j's global data sits in ld[j % 2]; it is loaded two steps before
-    // its MFMAs and staged one step before them.  One barrier per step, which
-    // waits for LDS accesses only: the loads of the next two steps stay in
-    // flight across it.  At step j the MFMAs read buffer j % 2 (staged before
-    // the previous barrier), then step j + 1 is staged into the other buffer,
-    // whose last reader, step j - 1, every wave finished before that barrier.
-    // Inside the loop every load and stage is unconditional, with step
-    // indices past the last clamped to it (re-reading the last step, staged
-    // into a buffer nothing reads any more), so the same loads are in flight
-    // at every step and the compiler's waits count only the step it uses.
-    const int steps = (int)(p.ni / kNtBK);   // ni is a multiple of 64
-    const int last = steps - 1;
-    Ld ld[2];
-    auto step = [&](int j, auto parc) {
-        constexpr int B = decltype(parc)::value;
-        mfmas(parc);
-        stage(ld[B ^ 1], std::integral_constant<int, B ^ 1>{});
-        load(min(j + 3, last), ld[B ^ 1]);
-        lds_barrier();
-    };
-    if (steps > 0) {
-        load(0, ld[0]);
-        load(min(1, last), ld[1]);
-        stage(ld[0], std::integral_constant<int, 0>{});
-        load(min(2, last), ld[0]);
-        lds_barrier();
-        int j = 0;
-        for (; j + 1 < steps; j += 2) {
-            step(j, std::integral_constant<int, 0>{});
-            step(j + 1, std::integral_constant<int, 1>{});
-        }
-        if (j < steps) mfmas(std::integral_constant<int, 0>{});   // an odd last step, staged in buffer 0
-        __builtin_amdgcn_s_waitcnt(0);   // the clamped prefetches
-    }
+    tile_pipeline<Ld>((int)(p.ni / kNtBK), load, stage, mfmas);   // ni is a multiple of 64
     // D layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4
 #pragma unroll
     for (int i = 0; i < 2; ++i)

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace nqk {
 
 // Tile of workgroup b in a grid of tiles_m x tiles_n output tiles, for
@@ -42,6 +44,48 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// The K loop of the 128 x 128 tile kernels, for `steps` K steps.  The
+// kernel supplies load(j, ld) (issue step j's global loads into registers),
+// stage(ld, buffer) (convert them and write the x and weight tiles into LDS
+// buffer 0 or 1, a std::integral_constant) and mfmas(buffer) (the step's
+// matrix-core work on that buffer).  Step j's data sits in ld[j % 2]: it is
+// loaded two steps before its MFMAs and staged one step before them, into
+// buffer j % 2.  At step j the MFMAs read buffer j % 2, staged before the
+// previous barrier; then step j + 1 is staged into the other buffer, whose
+// last reader, step j - 1, every wave finished before that barrier.  One
+// barrier per step, waiting for LDS accesses only, so the loads of the next
+// two steps stay in flight across it.  Inside the loop every load and stage
+// is unconditional, with step indices past the last clamped to it (the last
+// step read again, staged into a buffer nothing reads any more): the same
+// loads are then in flight at every step, and the compiler's waits count
+// only the step being staged.
+template <typename Ld, typename LoadF, typename StageF, typename MfmaF>
+__device__ __forceinline__ void tile_pipeline(int steps, LoadF &&load, StageF &&stage, MfmaF &&mfmas)
+{
+    if (steps <= 0) return;
+    const int last = steps - 1;
+    Ld ld[2];
+    auto step = [&](int j, auto parc) {
+        constexpr int B = decltype(parc)::value;
+        mfmas(parc);
+        stage(ld[B ^ 1], std::integral_constant<int, B ^ 1>{});
+        load(min(j + 3, last), ld[B ^ 1]);
+        lds_barrier();
+    };
+    load(0, ld[0]);
+    load(min(1, last), ld[1]);
+    stage(ld[0], std::integral_constant<int, 0>{});
+    load(min(2, last), ld[0]);
+    lds_barrier();
+    int j = 0;
+    for (; j + 1 < steps; j += 2) {
+        step(j, std::integral_constant<int, 0>{});
+        step(j + 1, std::integral_constant<int, 1>{});
+    }
+    if (j < steps) mfmas(std::integral_constant<int, 0>{});   // an odd last step, staged in buffer 0
+    __builtin_amdgcn_s_waitcnt(0);                            // the clamped prefetches
 }
 
 // Workgroups to launch for `tiles` tiles (a multiple of 8), or 0 when the
