@@ -309,6 +309,8 @@ def test_gather_matrix_core_moe_shape():
     (40, 320, 224, "bf16", False),                # tiles, ragged nc
     (130, 448, 96, "bf16", False),                # several row tiles, nc < one tile
     (700, 192, 640, "bf16", False),               # 6 x 5 tiles: a partial panel, 30 tiles
+    (40, 64, 224, "bf16", False),                 # tiles, one K step
+    (130, 128, 96, "bf16", False),                # tiles, two K steps
 ])
 def test_notrans_matches_oracle(mode, m, ni, nc, dtype, row_exact):
     words, scales = codes_case(30 + m, (ni,), nc, mode)

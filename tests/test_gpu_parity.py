@@ -598,6 +598,8 @@ def test_other_widths_gather(bits, rows):
     (200, 512, 384, 64, 4, "bf16", "bf16"),    # 128-row tiles
     (150, 320, 4160, 64, 5, "bf16", "bf16"),   # tiles, odd width, ragged m and nc
     (700, 256, 640, 64, 4, "bf16", "bf16"),    # 6 x 5 tiles: a partial panel of tile rows, 30 tiles
+    (20, 64, 256, 64, 4, "bf16", "bf16"),      # tiles, one K step
+    (40, 128, 320, 64, 8, "bf16", "f32"),      # tiles, two K steps
 ])
 def test_qmm_notrans(m, ni, nc, gs, bits, x_dtype, w_dtype):
     """x times the weights as stored against the oracle; row-exact rows (and
