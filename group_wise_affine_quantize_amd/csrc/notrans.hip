@@ -245,13 +245,16 @@ struct NtTiledParams {
 };
 
 constexpr int kNtTM = 128, kNtTN = 128, kNtBK = 64, kNtLd = kNtBK + 8;
-// Column c of the transposed weight tile starts at c * kNtLd + 16 * ((c / 32) % 4)
-// elements: with the plain stride, the 2-byte writes of a wave (16 rows x 4
-// groups of 32 columns) all fall in the same few LDS banks; the shift spreads
-// the groups over distinct banks, and the 16 columns one B-operand read
-// touches share a shift, so the reads stay conflict-free.
-__device__ __forceinline__ int nt_wcol(int c) { return c * kNtLd + 16 * ((c >> 5) & 3); }
-constexpr int kNtWsElems = kNtTN * kNtLd + 64;
+// Column c of the transposed weight tile starts at c * kNtLd + 16 * ((c / 16) % 8)
+// elements.  With the plain stride the writes of a wave all fall in the same
+// few LDS banks: a column start is 36 c dwords, i.e. the same bank for every
+// 16 columns.  The shift, 8 dwords per 16 columns, spreads them: the 4-byte
+// writes of a wave (8 row pairs x 8 groups of 16 columns) land in 64
+// distinct banks, the 2-byte writes (16 rows x 4 groups of 32 columns) in 32
+// distinct dwords; and the 16 columns one B-operand read phase touches share
+// a shift, so the reads stay conflict-free.
+__device__ __forceinline__ int nt_wcol(int c) { return c * kNtLd + 16 * ((c >> 4) & 7); }
+constexpr int kNtWsElems = kNtTN * kNtLd + 128;
 
 template <int BITS, typename ST>
 __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
@@ -276,19 +279,30 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
 
     const int lrow = tid >> 1, lhalf = tid & 1;          // x loader: one row, 32 elements
     const int64_t xm = m0 + lrow;
-    const int wrow = tid >> 2, wcol = 32 * (tid & 3);    // weight loader: one row, 32 columns
+    // Weight loader.  Widths 2, 4 and 8 (PAIR): thread t takes rows
+    // 2 (t / 8) and 2 (t / 8) + 1 of the step and the 16 columns from
+    // 16 (t % 8), and writes the two rows' values of a column into LDS as one
+    // 4-byte word.  Other widths: row t / 4, the 32 columns from 32 (t % 4),
+    // 2-byte writes.  Either way a thread's columns lie inside one group and
+    // its codes start on a word boundary.
+    constexpr bool PAIR = BITS == 2 || BITS == 4 || BITS == 8;
+    constexpr int NR = PAIR ? 2 : 1;                      // rows per thread
+    constexpr int NCOL = PAIR ? 16 : 32;                  // columns per thread
+    constexpr int NW = NCOL * BITS / 32;                  // code words per row
+    const int wrow = PAIR ? 2 * (tid >> 3) : tid >> 2;
+    const int wcol = PAIR ? 16 * (tid & 7) : 32 * (tid & 3);
     const int64_t cb = c0 + wcol;
-    const bool wv_ok = cb < p.nc;                         // nc % 32 == 0: then cb + 32 <= nc
+    const bool wv_ok = cb < p.nc;                         // nc % 32 == 0: then cb + NCOL <= nc
     const int64_t g = (wv_ok ? cb : 0) >> p.lg_gs;
-    constexpr int NW = BITS;   // 32 codes from a word boundary (32 columns x bits)
 
-    // One K step's global data for this thread: 32 activations, a run of 32
-    // codes and the raw storage bits of its scale and bias (converted only
-    // when used, so that no conversion waits on the load early).
+    // One K step's global data for this thread: 32 activations, the codes of
+    // its rows and the raw storage bits of their scales and biases
+    // (converted only when used, so that no conversion waits on the load
+    // early).
     struct Ld {
         uint4 x[4];
-        uint32_t raw[NW];
-        uint32_t s, b;
+        uint32_t raw[NR][NW];
+        uint32_t s[NR], b[NR];
     };
     // Rows past m read row m - 1 and columns past nc read column 0: their
     // products land only in outputs past m or nc, which are never stored.
@@ -304,10 +318,24 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
         const uint4 *src = reinterpret_cast<const uint4 *>(p.x + xmc * p.ni + i0 + 32 * lhalf);
 #pragma unroll
         for (int u = 0; u < 4; ++u) l.x[u] = src[u];
-        const int64_t i = i0 + wrow;
-        l.s = raw_of(p.scales, i * p.groups_per_row + g);
-        l.b = raw_of(p.biases, i * p.groups_per_row + g);
-        load_run<BITS>(p.codes + i * p.words_per_row + ((cbc * BITS) >> 5), l.raw);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int64_t i = i0 + wrow + r;
+            l.s[r] = raw_of(p.scales, i * p.groups_per_row + g);
+            l.b[r] = raw_of(p.biases, i * p.groups_per_row + g);
+            const uint32_t *src = p.codes + i * p.words_per_row + ((cbc * BITS) >> 5);
+            if constexpr (NW == 4) {
+                const uint4 d = *reinterpret_cast<const uint4 *>(src);
+                l.raw[r][0] = d.x, l.raw[r][1] = d.y, l.raw[r][2] = d.z, l.raw[r][3] = d.w;
+            } else if constexpr (NW == 2) {
+                const uint2 d = *reinterpret_cast<const uint2 *>(src);
+                l.raw[r][0] = d.x, l.raw[r][1] = d.y;
+            } else if constexpr (NW == 1) {
+                l.raw[r][0] = *src;
+            } else {
+                load_run<BITS>(src, l.raw[r]);
+            }
+        }
     };
     typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
     typedef float f32x2_v __attribute__((ext_vector_type(2)));
@@ -315,23 +343,36 @@ __global__ void __launch_bounds__(256) tiled_nt_kernel(NtTiledParams<ST> p)
     // with its activations into LDS buffer B (the weights transposed)
     auto stage = [&](const Ld &l, auto bufc) {
         constexpr int B = decltype(bufc)::value;
-        const float sc = f32_of(l.s), bi = f32_of(l.b);
-        uint32_t outw[16];
-        float qf[kLaneChunk];
-        codes_f32<BITS>(l.raw, qf);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16 for finite values
-            const f32x2_v f = {fmaf(sc, qf[2 * u], bi), fmaf(sc, qf[2 * u + 1], bi)};
-            outw[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
-        }
         uint4 *xd = reinterpret_cast<uint4 *>(xs[B] + lrow * kNtLd + 32 * lhalf);
 #pragma unroll
         for (int u = 0; u < 4; ++u) xd[u] = make_uint4(l.x[u].x, l.x[u].y, l.x[u].z, l.x[u].w);
+        // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16 for finite values
+        if constexpr (PAIR) {
+            float q0[kLaneChunk], q1[kLaneChunk];
+            uint32_t w0[BITS] = {}, w1[BITS] = {};   // the first NW words hold the 16 codes
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            ws[B][nt_wcol(wcol + 2 * u) + wrow] = (bf16_bits)(outw[u] & 0xffffu);
-            ws[B][nt_wcol(wcol + 2 * u + 1) + wrow] = (bf16_bits)(outw[u] >> 16);
+            for (int j = 0; j < NW; ++j) w0[j] = l.raw[0][j], w1[j] = l.raw[1][j];
+            codes_f32<BITS>(w0, q0);
+            codes_f32<BITS>(w1, q1);
+            const float s0 = f32_of(l.s[0]), b0 = f32_of(l.b[0]);
+            const float s1 = f32_of(l.s[1]), b1 = f32_of(l.b[1]);
+#pragma unroll
+            for (int u = 0; u < NCOL; ++u) {
+                const f32x2_v f = {fmaf(s0, q0[u], b0), fmaf(s1, q1[u], b1)};
+                *reinterpret_cast<uint32_t *>(&ws[B][nt_wcol(wcol + u) + wrow]) =
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+            }
+        } else {
+            const float sc = f32_of(l.s[0]), bi = f32_of(l.b[0]);
+            float qf[kLaneChunk];
+            codes_f32<BITS>(l.raw[0], qf);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const f32x2_v f = {fmaf(sc, qf[2 * u], bi), fmaf(sc, qf[2 * u + 1], bi)};
+                const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+                ws[B][nt_wcol(wcol + 2 * u) + wrow] = (bf16_bits)(pk & 0xffffu);
+                ws[B][nt_wcol(wcol + 2 * u + 1) + wrow] = (bf16_bits)(pk >> 16);
+            }
         }
     };
     auto mfmas = [&](auto bufc) {
