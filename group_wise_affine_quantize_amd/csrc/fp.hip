@@ -1082,20 +1082,21 @@ __global__ void __launch_bounds__(256) fp_nt_reduce_kernel(FpNtParams p)
 }
 
 // Many bf16 rows: 128 x 128 tiles of y with bf16 MFMA, K steps of 64 rows i
-// of w_hat; thread t stages 32 elements of x row t / 2 and the 32 columns
-// 32 (t % 4) .. + 31 of w_hat row t / 4 (one lane chunk), converted to
-// bf16(S * E) and written down LDS columns, so that a B operand reads 8
-// consecutive i of one column.  Column c starts at c * 72 + 16 ((c / 32) % 4)
-// elements, which keeps the 2-byte writes of 16 rows x 4 column groups on
-// distinct banks.  ni is a multiple of 64.
-__device__ __forceinline__ int fp_nt_wcol(int c) { return c * 72 + 16 * ((c >> 5) & 3); }
+// of w_hat; thread t stages 32 elements of x row t / 2 and the 16 columns
+// 16 (t % 8) .. + 15 of w_hat rows 2 (t / 8) and 2 (t / 8) + 1, converted to
+// bf16(S * E) and written down LDS columns, two rows per 4-byte write, so
+// that a B operand reads 8 consecutive i of one column.  Column c starts at
+// c * 72 + 16 ((c / 16) % 8) elements, which puts the 64 writes of a wave
+// instruction (8 row pairs x 8 column groups) on distinct banks and keeps a
+// B-operand read phase (16 columns) on one shift.  ni is a multiple of 64.
+__device__ __forceinline__ int fp_nt_wcol(int c) { return c * 72 + 16 * ((c >> 4) & 7); }
 
 template <int MODE>
 __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
 {
-    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs, NG = 32 / GS;
+    constexpr int BITS = Fp<MODE>::bits, GS = Fp<MODE>::gs;
     __shared__ __attribute__((aligned(16))) bf16_bits xs[2][128 * 72];
-    __shared__ __attribute__((aligned(16))) bf16_bits ws[2][128 * 72 + 64];
+    __shared__ __attribute__((aligned(16))) bf16_bits ws[2][128 * 72 + 128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
@@ -1105,55 +1106,71 @@ __global__ void __launch_bounds__(256) fp_tiled_nt_kernel(FpNtParams p)
     // rows past mr read row mr - 1 and columns past nc column 0: their
     // products land only in outputs that are not stored
     const int64_t xmc = min(m0 + lrow, p.mr - 1);
-    const int wrow = tid >> 2, wcol = 32 * (tid & 3);
+    // weights: thread t takes rows 2 (t / 8) and 2 (t / 8) + 1 of the step
+    // and the 16 columns from 16 (t % 8), inside one scale group (GS is 16
+    // or 32), and writes the two rows' values of a column as one 4-byte word
+    const int wrow = 2 * (tid >> 3), wcol = 16 * (tid & 7);
     const int64_t cb = c0 + wcol;
     const int64_t cbc = cb < p.nc ? cb : 0;
     const int64_t wpr = p.nc * BITS / 32, gpr = p.nc / GS;
     const bf16_bits *x = static_cast<const bf16_bits *>(p.x);
     const int nsteps = (int)(p.ni / 64);
+    constexpr int NW = 16 * BITS / 32;   // code words of a row's 16 columns
     struct Ld {
         uint4 x[4];
-        uint4 c[BITS / 4];
-        uint32_t s[NG];
+        uint32_t c[2][NW];
+        uint32_t s[2];
     };
     auto load = [&](int step, Ld &l) {
         const int64_t i0 = (int64_t)step * 64;
         const uint4 *xsrc = reinterpret_cast<const uint4 *>(x + xmc * p.ni + i0 + 32 * lhalf);
 #pragma unroll
         for (int u = 0; u < 4; ++u) l.x[u] = xsrc[u];
-        const int64_t i = i0 + wrow;
-        const uint4 *csrc = reinterpret_cast<const uint4 *>(p.codes + i * wpr + cbc * BITS / 32);
 #pragma unroll
-        for (int u = 0; u < BITS / 4; ++u) l.c[u] = csrc[u];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) l.s[g] = p.scales[i * gpr + cbc / GS + g];
+        for (int r = 0; r < 2; ++r) {
+            const int64_t i = i0 + wrow + r;
+            const uint32_t *csrc = p.codes + i * wpr + cbc * BITS / 32;
+            if constexpr (NW == 4) {
+                const uint4 d = *reinterpret_cast<const uint4 *>(csrc);
+                l.c[r][0] = d.x, l.c[r][1] = d.y, l.c[r][2] = d.z, l.c[r][3] = d.w;
+            } else {
+                const uint2 d = *reinterpret_cast<const uint2 *>(csrc);
+                l.c[r][0] = d.x, l.c[r][1] = d.y;
+            }
+            l.s[r] = p.scales[i * gpr + cbc / GS];
+        }
     };
     auto store = [&](const Ld &l, auto bufc) {
         constexpr int B = decltype(bufc)::value;
         uint4 *xd = reinterpret_cast<uint4 *>(xs[B] + lrow * 72 + 32 * lhalf);
 #pragma unroll
         for (int u = 0; u < 4; ++u) xd[u] = make_uint4(l.x[u].x, l.x[u].y, l.x[u].z, l.x[u].w);
-        uint32_t wd[BITS];
+        // bf16 pairs of adjacent columns of each row, regrouped by one
+        // v_perm_b32 per word into the two rows of one column
+        uint32_t h[2][8];
 #pragma unroll
-        for (int u = 0; u < BITS / 4; ++u)
-            wd[4 * u] = l.c[u].x, wd[4 * u + 1] = l.c[u].y, wd[4 * u + 2] = l.c[u].z, wd[4 * u + 3] = l.c[u].w;
+        for (int r = 0; r < 2; ++r) {
+            uint32_t wd[BITS] = {};   // the first NW words hold the 16 codes
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const float S = scale_value<MODE>(l.s[g]);
+            for (int j = 0; j < NW; ++j) wd[j] = l.c[r][j];
+            const float S = scale_value<MODE>(l.s[r]);
 #pragma unroll
-            for (int q = 0; q < GS / 2; ++q) {
-                const int pi = g * (GS / 2) + q;
-                uint32_t h;
+            for (int pi = 0; pi < 8; ++pi) {
                 if constexpr (Fp<MODE>::e8m0) {
-                    h = __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S));
+                    h[r][pi] = __builtin_bit_cast(uint32_t, pair_bf16_scaled<MODE>(wd, pi, S));
                 } else {
                     const f32x2_t e = pair_f32<MODE>(wd, pi);
                     const f32x2_t v = {S * e[0], S * e[1]};
-                    h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+                    h[r][pi] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
                 }
-                ws[B][fp_nt_wcol(wcol + 2 * pi) + wrow] = (bf16_bits)(h & 0xffffu);
-                ws[B][fp_nt_wcol(wcol + 2 * pi + 1) + wrow] = (bf16_bits)(h >> 16);
             }
+        }
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) {
+            *reinterpret_cast<uint32_t *>(&ws[B][fp_nt_wcol(wcol + 2 * pi) + wrow]) =
+                __builtin_amdgcn_perm(h[1][pi], h[0][pi], 0x05040100u);
+            *reinterpret_cast<uint32_t *>(&ws[B][fp_nt_wcol(wcol + 2 * pi + 1) + wrow]) =
+                __builtin_amdgcn_perm(h[1][pi], h[0][pi], 0x07060302u);
         }
     };
     f32x16_t acc[2][2];
