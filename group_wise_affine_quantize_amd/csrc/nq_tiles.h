@@ -1,5 +1,7 @@
-// Workgroup-to-tile mapping for the 128 x 128 tile kernels (the products
-// with the weights as stored and the floating-point tiled product).
+// Shared pieces of the 128 x 128 tile kernels (the products with the
+// weights as stored and the floating-point tiled product): the
+// workgroup-to-tile mapping, a barrier that leaves global loads in flight,
+// and the double-buffered K loop of the weights-as-stored kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
