@@ -71,12 +71,17 @@ __device__ __forceinline__ float e2m1_value(uint32_t c)
 
 // E4M3 (OCP): sign bit 7, exponent bits 6:3 (bias 7), mantissa bits 2:0;
 // exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN.
+// Both magnitudes are formed and selected, and the sign is or-ed in, so
+// that the conversion is straight-line code (no branch around the NaN or
+// subnormal cases inside the kernels' loops).
 __device__ __forceinline__ float e4m3_value(uint32_t c)
 {
-    if ((c & 0x7fu) == 0x7fu) return __uint_as_float(kQuietNan);
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    return (c & 0x80u) ? -mag : mag;
+    const float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    const float subnormal = (float)m * 0x1p-9f;
+    const float mag = e ? normal : subnormal;
+    const float v = __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+    return (c & 0x7fu) == 0x7fu ? __uint_as_float(kQuietNan) : v;
 }
 
 // E8M0: 2^(s - 127); s = 0 is the fp32 subnormal 2^-127; s = 255 is NaN.
