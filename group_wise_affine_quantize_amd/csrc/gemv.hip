@@ -912,16 +912,10 @@ gather_group_small_kernel(const uint32_t *ids, const uint32_t *lhs, int64_t x_it
         }
     };
 
-    for (int b = t; b < nb; b += kGroupThreads) hist[b] = 0;
-    __syncthreads();
-    for (int64_t v0 = 0; v0 < v_total; v0 += kGroupThreads) {
-        const uint32_t b = bucket(v0 + t);
-        match(b, [&](uint32_t lb, uint64_t m, int leader) {
-            if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
-        });
-    }
-    __syncthreads();
-    if (w == 0) {
+    // the bucket sizes in hist -> start[b] (first position), coff[b] (first
+    // chunk), coff[nb] and *nchunks (the chunk count)
+    auto scan = [&] {
+        if (w != 0) return;
         // exclusive scans of the bucket sizes and chunk counts; lane i holds
         // buckets 4 i .. 4 i + 3
         uint32_t h[4], cn[4], sh = 0, sc = 0;
@@ -950,20 +944,66 @@ gather_group_small_kernel(const uint32_t *ids, const uint32_t *lhs, int64_t x_it
             coff[nb] = ic;
             *nchunks = ic;
         }
+    };
+    // chunk table: entry j belongs to the last bucket whose first chunk is <= j
+    auto write_table = [&] {
+        const uint32_t total = coff[nb];
+        for (uint32_t j = t; j < total; j += kGroupThreads) {
+            int lo = 0, hi = nb;   // coff[lo] <= j < coff[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (coff[mid] <= j) lo = mid;
+                else hi = mid;
+            }
+            const uint32_t i = j - coff[lo];
+            table[j] = make_uint4((uint32_t)lo, start[lo] + i * chunk, min(chunk, hist[lo] - i * chunk), 0u);
+        }
+    };
+
+    if (v_total <= kGroupThreads) {   // uniform
+        // One round: a single pass over the ids gives each wave's count per
+        // bucket and each vector's rank among the earlier lanes of its wave
+        // with the same bucket; the bucket sizes are the waves' counts
+        // summed, and a vector goes to start[b] + (the earlier waves' count
+        // in b) + its rank -- the positions of the general path below.
+        for (int i = t; i < kGroupWaves * kGroupSmallBuckets; i += kGroupThreads) (&wc[0][0])[i] = 0;
+        __syncthreads();
+        const uint32_t b = bucket(t);
+        uint32_t rank = 0;
+        match(b, [&](uint32_t lb, uint64_t m, int leader) {
+            if (b == lb) rank = (uint32_t)__popcll(m & lanes_below);
+            if (lane == leader) wc[w][lb] = (uint32_t)__popcll(m);
+        });
+        __syncthreads();
+        for (int bb = t; bb < nb; bb += kGroupThreads) {
+            uint32_t run = 0;
+            for (int w2 = 0; w2 < kGroupWaves; ++w2) {
+                const uint32_t cnt = wc[w2][bb];
+                wc[w2][bb] = run;
+                run += cnt;
+            }
+            hist[bb] = run;
+        }
+        __syncthreads();
+        scan();
+        __syncthreads();
+        write_table();
+        if (b != 0xffffffffu) perm[start[b] + wc[w][b] + rank] = (uint32_t)t;
+        return;
+    }
+
+    for (int b = t; b < nb; b += kGroupThreads) hist[b] = 0;
+    __syncthreads();
+    for (int64_t v0 = 0; v0 < v_total; v0 += kGroupThreads) {
+        const uint32_t b = bucket(v0 + t);
+        match(b, [&](uint32_t lb, uint64_t m, int leader) {
+            if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+        });
     }
     __syncthreads();
-    // chunk table: entry j belongs to the last bucket whose first chunk is <= j
-    const uint32_t total = coff[nb];
-    for (uint32_t j = t; j < total; j += kGroupThreads) {
-        int lo = 0, hi = nb;   // coff[lo] <= j < coff[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (coff[mid] <= j) lo = mid;
-            else hi = mid;
-        }
-        const uint32_t i = j - coff[lo];
-        table[j] = make_uint4((uint32_t)lo, start[lo] + i * chunk, min(chunk, hist[lo] - i * chunk), 0u);
-    }
+    scan();
+    __syncthreads();
+    write_table();
     __syncthreads();
     // stable placement, kGroupThreads vectors a round
     for (int64_t v0 = 0; v0 < v_total; v0 += kGroupThreads) {

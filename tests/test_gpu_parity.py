@@ -376,6 +376,39 @@ def test_gather_grouped(case):
     assert bits_equal(yd, B.nq_gather_qmm(xs, cs, ss, bs, gs, bits, dev(ids)))
 
 
+@pytest.mark.parametrize("rows", [300, 1024, 1500])
+def test_gather_grouping_tables(rows):
+    """The device grouping pass that the row-exact gather runs leaves in the
+    workspace a stable counting sort of the vectors by expert (ids past e in
+    one last bucket) and a table of chunks; both are checked against the
+    sort written out plainly, for one round of ids (up to 1024 vectors, a
+    single pass over them) and for several rounds."""
+    e, n, k, gs, bits = 8, 64, 256, 64, 4
+    rng = np.random.default_rng(rows)
+    ids = rng.integers(0, e + 3, rows).astype(np.uint32)   # some ids past e
+    w, x, c, sc, b = quantized_case(rows, e * n, k, gs, bits, "bf16", rows, "bf16", 0.02)
+    cg, sg, bg = (dev(a.reshape((e, n) + a.shape[1:])) for a in (c, sc, b))
+    xs = dev(x).reshape(rows, 1, k)
+    ws = torch.zeros(B.nq_gather_qmm_workspace_bytes(rows, 1, k, e, n, gs, bits, torch.bfloat16,
+                                                      torch.bfloat16) // 4, dtype=torch.int32, device="cuda")
+    B.nq_gather_qmm_row_exact(xs, cg, sg, bg, gs, bits, dev(ids), workspace=ws)
+    torch.cuda.synchronize()
+    t = ws.cpu().numpy().view(np.uint32)
+    bucket = np.minimum(ids, e)
+    assert np.array_equal(t[:rows], np.argsort(bucket, kind="stable"))
+    nchunks = int(t[rows])
+    t0 = (rows + 1 + 3) & ~3
+    table = t[t0:t0 + 4 * nchunks].reshape(nchunks, 4)
+    size = int(table[:, 2].max())
+    expect, first = [], 0
+    for bk in range(e + 1):
+        cnt = int(np.sum(bucket == bk))
+        for f in range(0, cnt, size):
+            expect.append((bk, first + f, min(size, cnt - f)))
+        first += cnt
+    assert [tuple(int(v) for v in r[:3]) for r in table] == expect
+
+
 @pytest.mark.parametrize("case", ["many_vectors", "many_experts"])
 def test_gather_large_id_sets(case):
     """Id sets past what a matrix-core workgroup groups by itself (more than
